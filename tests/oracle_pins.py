@@ -1,0 +1,312 @@
+"""Checks that pin the fp64 oracle to facts other than itself.
+
+Each ``pin_*`` takes the oracle module and raises AssertionError on a violation,
+so the same checks run against the real oracle (test_oracle_pins.py) and against
+deliberately broken copies of it (test_oracle_mutants.py).
+
+Sources: MoDA deck (arXiv 2603.15619), slides "One denominator allocates probability
+across both memories" (the joint equation), "Shared online-softmax states preserve
+the joint operator" (running-state merge), "Local packing avoids scanning irrelevant
+depth entries" (Fig. 4 utilizations) and "Backup: grouped indexing preserves the
+correct token map" (expanded-row map and its G = 4 example).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def rand_case(seed, B=2, T=9, Hq=2, Hkv=1, d=8, S=3, Scap=None):
+    rng = np.random.default_rng(seed)
+    Scap = S if Scap is None else Scap
+    q = rng.standard_normal((B, T, Hq, d))
+    k = rng.standard_normal((B, T, Hkv, d))
+    v = rng.standard_normal((B, T, Hkv, d))
+    kd = rng.standard_normal((B, T, Scap, Hkv, d))
+    vd = rng.standard_normal((B, T, Scap, Hkv, d))
+    return q, k, v, kd, vd
+
+
+def _sdpa(q, k, v, causal, scale, attn_mask=None):
+    """torch's scaled_dot_product_attention in float64 on [B,T,H,d] tensors."""
+    G = q.shape[2] // k.shape[2]
+    qt = torch.from_numpy(np.ascontiguousarray(q.transpose(0, 2, 1, 3)))
+    kt = torch.from_numpy(np.ascontiguousarray(np.repeat(k, G, axis=2).transpose(0, 2, 1, 3)))
+    vt = torch.from_numpy(np.ascontiguousarray(np.repeat(v, G, axis=2).transpose(0, 2, 1, 3)))
+    m = None if attn_mask is None else torch.from_numpy(attn_mask)
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, is_causal=causal and m is None, scale=scale)
+    return o.numpy().transpose(0, 2, 1, 3)
+
+
+# p1 -----------------------------------------------------------------------------
+def pin_empty_depth_is_sdpa(orc):
+    """An empty depth set leaves ordinary (causal) softmax attention: compare with
+    torch's SDPA, an independent library routine, MHA and grouped heads."""
+    for seed, (Hq, Hkv), causal in [(1, (2, 2), True), (2, (4, 2), True), (3, (4, 1), False), (4, (3, 3), False)]:
+        q, k, v, kd, vd = rand_case(seed, B=2, T=11, Hq=Hq, Hkv=Hkv, d=8, S=2)
+        scale = 0.37
+        o, _ = orc.joint_attention(q, k, v, kd, vd, 0, causal, scale)
+        ref = _sdpa(q, k, v, causal, scale)
+        assert np.max(np.abs(o - ref)) < 1e-12, np.max(np.abs(o - ref))
+
+
+# p2 -----------------------------------------------------------------------------
+def pin_equal_logits_plain_mean(orc):
+    """q = 0 makes every logit 0: the output is the plain mean of the visible values
+    (t+1 sequence values and S depth values) and lse = ln(t+1+S)."""
+    B, T, H, d, S = 2, 7, 2, 5, 3
+    q, k, v, kd, vd = rand_case(5, B, T, H, H, d, S, Scap=S + 2)
+    q[:] = 0
+    for causal in (True, False):
+        o, lse = orc.joint_attention(q, k, v, kd, vd, S, causal, 0.5)
+        for b in range(B):
+            for h in range(H):
+                for t in range(T):
+                    J = t + 1 if causal else T
+                    mean = (v[b, :J, h].sum(0) + vd[b, t, :S, h].sum(0)) / (J + S)
+                    assert np.max(np.abs(o[b, t, h] - mean)) < 1e-13
+                    assert abs(lse[b, h, t] - math.log(J + S)) < 1e-13
+
+
+# p3 -----------------------------------------------------------------------------
+def pin_convex_and_affine(orc):
+    """Weights are non-negative and sum to one: each output coordinate lies in the
+    range of the visible values, o(v + c) = o + c and o(alpha v) = alpha o."""
+    q, k, v, kd, vd = rand_case(6, B=1, T=10, Hq=2, Hkv=2, d=6, S=4)
+    o, _ = orc.joint_attention(q, k, v, kd, vd, 4, True, 1.3)
+    for t in range(10):
+        for h in range(2):
+            vals = np.concatenate([v[0, : t + 1, h], vd[0, t, :4, h]], axis=0)
+            assert np.all(o[0, t, h] >= vals.min(0) - 1e-12) and np.all(o[0, t, h] <= vals.max(0) + 1e-12)
+    c = np.linspace(-2, 3, 6)
+    o2, _ = orc.joint_attention(q, k, v + c, kd, vd + c, 4, True, 1.3)
+    assert np.max(np.abs(o2 - (o + c))) < 1e-12
+    o3, _ = orc.joint_attention(q, k, 2.5 * v, kd, 2.5 * vd, 4, True, 1.3)
+    assert np.max(np.abs(o3 - 2.5 * o)) < 1e-12
+
+
+# p4 -----------------------------------------------------------------------------
+def pin_lse_merge(orc):
+    """Merging the sequence-only and depth-only running states (m, acc, o) the way
+    the shared online-softmax update does gives the joint result:
+    o = sigma(lse_s - lse_d) o_s + sigma(lse_d - lse_s) o_d, lse = logaddexp."""
+    for seed, Hq, Hkv in [(7, 2, 2), (8, 4, 2)]:
+        q, k, v, kd, vd = rand_case(seed, B=2, T=9, Hq=Hq, Hkv=Hkv, d=8, S=3)
+        o, lse = orc.joint_attention(q, k, v, kd, vd, 3, True, 0.4)
+        os_, ls = orc.sequence_only(q, k, v, True, 0.4)
+        od, ld = orc.depth_only(q, k, v, kd, vd, 3, 0.4)
+        lm = np.logaddexp(ls, ld)
+        ws = np.exp(ls - lm).transpose(0, 2, 1)[..., None]
+        wd = np.exp(ld - lm).transpose(0, 2, 1)[..., None]
+        assert np.max(np.abs(lse - lm)) < 1e-12
+        assert np.max(np.abs(o - (ws * os_ + wd * od))) < 1e-12
+
+
+# p5 -----------------------------------------------------------------------------
+def pin_separate_softmax_differs(orc):
+    """Separate softmaxes followed by addition is a different operator."""
+    q, k, v, kd, vd = rand_case(9, B=1, T=16, Hq=2, Hkv=2, d=8, S=4)
+    o, _ = orc.joint_attention(q, k, v, kd, vd, 4, True)
+    sep = orc.separate_then_add(q, k, v, kd, vd, 4, True)
+    assert np.max(np.abs(o - sep)) > 1e-2
+
+
+# p6 -----------------------------------------------------------------------------
+def pin_locality_and_causality(orc):
+    """Row t sees keys j <= t and only its own depth slots: changing later keys or
+    other tokens' depth slots leaves row t bit-identical."""
+    q, k, v, kd, vd = rand_case(10, B=1, T=8, Hq=2, Hkv=2, d=4, S=2)
+    o, lse = orc.joint_attention(q, k, v, kd, vd, 2, True, 0.7)
+    t = 4
+    k2, v2, kd2, vd2 = k.copy(), v.copy(), kd.copy(), vd.copy()
+    k2[:, t + 1 :] += 5.0
+    v2[:, t + 1 :] -= 3.0
+    kd2[:, np.arange(8) != t] *= -2.0
+    vd2[:, np.arange(8) != t] += 1.0
+    o2, lse2 = orc.joint_attention(q, k2, v2, kd2, vd2, 2, True, 0.7)
+    assert np.array_equal(o[:, t], o2[:, t]) and np.array_equal(lse[:, :, t], lse2[:, :, t])
+    assert not np.allclose(o[:, t + 1], o2[:, t + 1])
+    # and slots beyond n_depth are never read
+    kd3, vd3 = kd.copy(), vd.copy()
+    q2, k3, v3, kd4, vd4 = rand_case(10, B=1, T=8, Hq=2, Hkv=2, d=4, S=2, Scap=4)
+    o4, _ = orc.joint_attention(q2, k3, v3, kd4, vd4, 2, True, 0.7)
+    kd4[:, :, 2:] = 1e3
+    vd4[:, :, 2:] = -1e3
+    o5, _ = orc.joint_attention(q2, k3, v3, kd4, vd4, 2, True, 0.7)
+    assert np.array_equal(o4, o5)
+    del kd3, vd3
+
+
+# p7 -----------------------------------------------------------------------------
+def pin_slot_permutation(orc):
+    """The depth slots form a set: a joint permutation of the slot axis of
+    (k_depth, v_depth) leaves the output unchanged."""
+    q, k, v, kd, vd = rand_case(11, B=1, T=6, Hq=2, Hkv=1, d=5, S=5)
+    o, lse = orc.joint_attention(q, k, v, kd, vd, 5, True)
+    p = np.array([3, 0, 4, 1, 2])
+    o2, lse2 = orc.joint_attention(q, k, v, kd[:, :, p], vd[:, :, p], 5, True)
+    assert np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(lse - lse2)) < 1e-12
+
+
+# p8 -----------------------------------------------------------------------------
+def pin_gqa_is_repeated_mha(orc):
+    """Query head h reads KV head h // G: identical to MHA with every sequence and
+    depth KV head repeated G times in place."""
+    q, k, v, kd, vd = rand_case(12, B=2, T=7, Hq=6, Hkv=2, d=4, S=3)
+    o, lse = orc.joint_attention(q, k, v, kd, vd, 3, True)
+    G = 3
+    o2, lse2 = orc.joint_attention(
+        q, np.repeat(k, G, 2), np.repeat(v, G, 2), np.repeat(kd, G, 3), np.repeat(vd, G, 3), 3, True
+    )
+    assert np.max(np.abs(o - o2)) < 1e-13 and np.max(np.abs(lse - lse2)) < 1e-13
+
+
+# p9 -----------------------------------------------------------------------------
+def pin_varlen_is_independent(orc):
+    """Packed sequences (cu_seqlens) behave as independent runs."""
+    rng = np.random.default_rng(13)
+    lens = [5, 1, 9, 3]
+    N, Hq, Hkv, d, S = sum(lens), 4, 2, 6, 3
+    q = rng.standard_normal((N, Hq, d))
+    k = rng.standard_normal((N, Hkv, d))
+    v = rng.standard_normal((N, Hkv, d))
+    kd = rng.standard_normal((N, S, Hkv, d))
+    vd = rng.standard_normal((N, S, Hkv, d))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    o, lse = orc.joint_attention(q, k, v, kd, vd, S, True, cu_seqlens=cu)
+    for s in range(len(lens)):
+        a, b = cu[s], cu[s + 1]
+        o1, l1 = orc.joint_attention(q[None, a:b], k[None, a:b], v[None, a:b], kd[None, a:b], vd[None, a:b], S, True)
+        assert np.max(np.abs(o[a:b] - o1[0])) < 1e-13
+        assert np.max(np.abs(lse[:, a:b] - l1[0])) < 1e-13
+
+
+# p10 ----------------------------------------------------------------------------
+def pin_depth_copies_of_current_kv(orc):
+    """If every depth slot of token t holds (k_t, v_t), the joint softmax equals
+    causal attention with ln(1 + S) added to the diagonal logit: checked against
+    SDPA with that additive mask."""
+    q, k, v, _, _ = rand_case(14, B=1, T=9, Hq=2, Hkv=2, d=6, S=1)
+    S = 3
+    kd = np.repeat(k[:, :, None], S, axis=2)
+    vd = np.repeat(v[:, :, None], S, axis=2)
+    o, _ = orc.joint_attention(q, k, v, kd, vd, S, True, 0.6)
+    T = 9
+    mask = np.full((T, T), -np.inf)
+    mask[np.tril_indices(T)] = 0.0
+    mask[np.diag_indices(T)] = math.log(1 + S)
+    ref = _sdpa(q, k, v, False, 0.6, attn_mask=mask)
+    assert np.max(np.abs(o - ref)) < 1e-12
+
+
+# p11 ----------------------------------------------------------------------------
+def pin_hand_example(orc):
+    with open(os.path.join(GOLDEN, "hand_example.json")) as f:
+        g = json.load(f)
+    one = lambda x: np.array(x, dtype=np.float64).reshape(1, 1, 1, 1)  # noqa: E731
+    kd = np.array(math.log(3.0)).reshape(1, 1, 1, 1, 1)
+    vd = np.array(g["v_depth"]).reshape(1, 1, 1, 1, 1)
+    o, lse = orc.joint_attention(one(g["q"]), one(g["k"]), one(g["v"]), kd, vd, 1, True, g["scale"])
+    assert abs(o.item() - g["out"]) < 1e-15
+    assert abs(lse.item() - math.log(4.0)) < 1e-15
+
+
+# p12 ----------------------------------------------------------------------------
+def pin_brute_force(orc):
+    """Pure-Python fsum brute force agrees with the vectorised oracle."""
+    rng = np.random.default_rng(15)
+    for it in range(6):
+        T = int(rng.integers(1, 8))
+        G = int(rng.integers(1, 3))
+        Hkv = int(rng.integers(1, 3))
+        d = int(rng.integers(1, 7))
+        S = int(rng.integers(0, 4))
+        causal = bool(it % 2 == 0)
+        q, k, v, kd, vd = rand_case(100 + it, B=1, T=T, Hq=G * Hkv, Hkv=Hkv, d=d, S=S, Scap=S + 1)
+        o, lse = orc.joint_attention(q, k, v, kd, vd, S, causal, 0.8)
+        o2, lse2 = orc.scalar_ref(q, k, v, kd, vd, S, causal, 0.8)
+        assert np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(lse - lse2)) < 1e-12
+
+
+# p13 ----------------------------------------------------------------------------
+def pin_large_logits(orc):
+    """Huge logit spread stays finite and tends to the value of the arg-max key."""
+    q, k, v, kd, vd = rand_case(16, B=1, T=6, Hq=1, Hkv=1, d=4, S=2)
+    o, lse = orc.joint_attention(1e4 * q, k, v, kd, vd, 2, True, 1.0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    for t in range(6):
+        logits = np.concatenate([k[0, : t + 1, 0] @ q[0, t, 0], kd[0, t, :2, 0] @ q[0, t, 0]])
+        vals = np.concatenate([v[0, : t + 1, 0], vd[0, t, :2, 0]])
+        srt = np.sort(logits)
+        if len(srt) > 1 and srt[-1] - srt[-2] < 1e-3:
+            continue
+        assert np.max(np.abs(o[0, t, 0] - vals[np.argmax(logits)])) < 1e-9
+
+
+# p14 ----------------------------------------------------------------------------
+def pin_index_map_example(orc):
+    """G = 4: expanded rows 8-15 see depth entries of positions 2 and 3 only, and the
+    sequence keys up to their own position."""
+    with open(os.path.join(GOLDEN, "index_map_g4.json")) as f:
+        g = json.load(f)
+    G, L, T = g["G"], 3, 6
+    seen = set()
+    for i_q in g["rows"]:
+        pos = {j_d // L for j_d in range(T * L) if orc.depth_visible(i_q, j_d, G, L)}
+        assert len(pos) == 1
+        seen |= pos
+        (p,) = pos
+        assert [i_k for i_k in range(T) if orc.sequence_visible(i_q, i_k, G)] == list(range(p + 1))
+    assert sorted(seen) == g["positions"]
+
+
+def pin_expanded_rows_equal(orc):
+    """The expanded-row formulation with the two visibility predicates computes the
+    same operator as the per-head form."""
+    for seed, Hq, Hkv, S in [(17, 4, 1, 2), (18, 4, 2, 3), (19, 2, 2, 1)]:
+        q, k, v, kd, vd = rand_case(seed, B=1, T=5, Hq=Hq, Hkv=Hkv, d=4, S=S)
+        o, _ = orc.joint_attention(q, k, v, kd, vd, S, True, 0.9)
+        o2 = orc.expanded_rows_attention(q, k, v, kd, vd, S, 0.9)
+        assert np.max(np.abs(o - o2)) < 1e-12
+
+
+# p15 ----------------------------------------------------------------------------
+def pin_utilization(orc):
+    """Brute-force counts of usable depth entries reproduce the printed sweep values
+    (3.12% at G = 2, 50% at G = 32, C = L = 64) and the 1/T, 1/C, G/C forms."""
+    with open(os.path.join(GOLDEN, "depth_utilization.json")) as f:
+        g = json.load(f)
+    C, L = g["C"], 8  # utilization does not depend on L; a small L keeps the count fast
+    for G, pct in g["printed_percent"].items():
+        u = orc.depth_utilization("group", T=0, C=C, G=int(G), L=L)
+        assert math.floor(100 * u * 100) / 100 == pct or round(100 * u, g["printed_decimals"]) == pct, (G, u)
+    assert abs(orc.depth_utilization("chunk", T=0, C=16, G=1, L=3) - 1 / 16) < 1e-15
+    assert abs(orc.depth_utilization("contiguous", T=12, C=4, G=1, L=2) - 1 / 12) < 1e-15
+    assert abs(orc.depth_utilization("group", T=0, C=16, G=4, L=2) - 4 / 16) < 1e-15
+
+
+ALL_PINS = [
+    pin_empty_depth_is_sdpa,
+    pin_equal_logits_plain_mean,
+    pin_convex_and_affine,
+    pin_lse_merge,
+    pin_separate_softmax_differs,
+    pin_locality_and_causality,
+    pin_slot_permutation,
+    pin_gqa_is_repeated_mha,
+    pin_varlen_is_independent,
+    pin_depth_copies_of_current_kv,
+    pin_hand_example,
+    pin_brute_force,
+    pin_large_logits,
+    pin_index_map_example,
+    pin_expanded_rows_equal,
+    pin_utilization,
+]
