@@ -1,0 +1,324 @@
+"""Benchmark of the MoDA joint sequence/depth attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+One step = one launch of the fused forward (sequence + depth, all rows, all heads)
+over one batch of seeded synthetic inputs already resident in HBM. Consecutive
+steps cycle through enough independent input batches that the 256 MB Infinity
+Cache cannot hold them, so every step streams its operands from HBM. The timed
+steps are replayed as a HIP graph (one graph launch per pass over the batches) so
+that host launch overhead does not enter the per-step time.
+
+Prints one JSON line. ``value`` = (sequence + depth FLOPs) per step / step time.
+``roofline`` rates the fused kernel against the bound that limits it at this
+workload (HBM bytes or bf16 MFMA FLOPs, whichever takes longer at peak).
+``cpu_baseline`` times the fp64 oracle on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+for _p in (ROOT, os.path.join(ROOT, "tests")):
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
+
+METRIC = "fused seq+depth attention fwd TFLOP/s; % MFMA peak and depth-KV HBM GB/s"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector
+CACHE_DEFEAT_BYTES = 768 << 20  # > 256 MB Infinity Cache + 8 x 4 MB L2
+KERNEL_SOURCES = ["moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_attn.hip", "moda_internal.h"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "joint_sequence_depth_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_name(w) -> str:
+    if not w.bf16:
+        return f"moda_fwd_f32_kernel<{w.head_dim}>"
+    G = w.group
+    gb = 8 if G % 8 == 0 else 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+    return f"moda_fwd_bf16_kernel<{w.head_dim}, {gb}, false>"
+
+
+def roofline(w, sec_per_launch: float) -> dict:
+    flops = w.seq_flops() + w.depth_flops()
+    nbytes = w.total_bytes()
+    peak_f = PEAK_BF16_TFLOPS if w.bf16 else PEAK_F32_TFLOPS
+    t_mfma = flops / (peak_f * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        achieved = nbytes / sec_per_launch / 1e9
+        return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": traffic_from_profile(w, nbytes)}
+    achieved = flops / sec_per_launch / 1e12
+    return {"bound": "mfma", "achieved": achieved, "peak": peak_f, "unit": "TFLOP/s", "frac": achieved / peak_f,
+            "traffic": traffic_from_profile(w, nbytes)}
+
+
+def traffic_from_profile(w, algorithmic_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The fp64 oracle as it stands, on (segment, KV-head group) units of the same
+    workload, as many as fit in about ``budget_s`` seconds."""
+    import numpy as np
+
+    import oracle
+    from workloads import configs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        cores = len(os.sched_getaffinity(0))
+    G, d = w.group, w.head_dim
+    units = [(s, hk) for s in range(len(w.lengths)) for hk in range(w.n_heads_kv)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(units)
+    prepared = []
+    t_start = time.perf_counter()
+    for s, hk in units:  # regenerate the unit's operands (not timed)
+        L = w.lengths[s]
+        lead = _lead_index(w, s, L)
+        hq = np.arange(hk * G, (hk + 1) * G)
+        c = np.arange(d)
+        q = configs.host_slice(w, "q", _ix(lead, hq, c))
+        k = configs.host_slice(w, "k", _ix(lead, np.array([hk]), c))
+        v = configs.host_slice(w, "v", _ix(lead, np.array([hk]), c))
+        if w.n_depth > 0:
+            i = np.arange(w.n_depth)
+            kd = configs.host_slice(w, "kd", _ix(lead, i, np.array([hk]), c))[None]
+            vd = configs.host_slice(w, "vd", _ix(lead, i, np.array([hk]), c))[None]
+        else:
+            kd = vd = None
+        pairs = L * (L + 1) / 2 if w.causal else L * L
+        unit_flops = 4.0 * d * G * pairs + 4.0 * L * G * w.n_depth * d
+        prepared.append((q[None], k[None], v[None], kd, vd, unit_flops))
+        if time.perf_counter() - t_start > budget_s or len(prepared) * q.nbytes * (2 + w.n_depth) > (4 << 30):
+            break
+    flops = 0.0
+    calls = 0
+    compute_s = 0.0
+    while compute_s < budget_s:  # cycle over the prepared units until the budget is spent
+        q, k, v, kd, vd, unit_flops = prepared[calls % len(prepared)]
+        t0 = time.perf_counter()
+        oracle.joint_attention(q, k, v, kd, vd, w.n_depth, w.causal, w.scale)
+        compute_s += time.perf_counter() - t0
+        flops += unit_flops
+        calls += 1
+    done = len(prepared)
+    return {"value": flops / compute_s / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{calls} oracle calls over {done} of the {len(units)} (sequence, KV-head group) units of "
+                      f"{w.name} ({flops / 1e9:.2f} GFLOP in {compute_s:.1f} s; operands regenerated on the host, "
+                      "generation not timed)"}
+
+
+def _lead_index(w, s, L):
+    import numpy as np
+
+    if w.varlen:
+        return (np.arange(int(w.cu_seqlens()[s]), int(w.cu_seqlens()[s]) + L),)
+    return (np.array([s]), np.arange(L))
+
+
+def _ix(lead, *rest):
+    """Open-mesh index tuple over the leading token index and the remaining axes."""
+    import numpy as np
+
+    if len(lead) == 2:  # (b, t): drop the batch axis afterwards
+        idx = np.ix_(lead[0], lead[1], *rest)
+        return tuple(a[0] for a in idx)
+    return np.ix_(lead[0], *rest)
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: about 2 s of GPU time)")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="small_bf16")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (for scaling HBM counters)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU sharding of this path is a design note, not built.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return 0
+
+    from joint_sequence_depth_amd import attn_fwd, lib
+    from workloads import configs
+
+    lib()  # fail loudly before any work if the HIP library is missing
+    w = configs.WORKLOADS[args.workload]
+    batch_bytes = w.total_bytes()
+    n_batches = max(1, min(32, math.ceil(CACHE_DEFEAT_BYTES / batch_bytes)))
+    print(f"# workload {w.name}: {w.desc}; {n_batches} input batch(es) of {batch_bytes / 1e6:.1f} MB", file=sys.stderr,
+          flush=True)
+    inputs = [configs.make_device(w, dev, i) for i in range(n_batches)]
+    cu = torch.from_numpy(w.cu_seqlens()).to(dev) if w.varlen else None
+    max_len = max(w.lengths)
+    odt = torch.bfloat16 if w.bf16 else torch.float32
+    outs = [torch.empty(w.shape_q(), dtype=odt, device=dev) for _ in range(n_batches)]
+    lses = [torch.empty(w.shape_lse(), dtype=torch.float32, device=dev) for _ in range(n_batches)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        x = inputs[i % n_batches]
+        attn_fwd(x["q"], x["k"], x["v"], x["kd"], x["vd"], n_depth=w.n_depth, causal=w.causal, scale=w.scale,
+                 cu_seqlens=cu, max_seqlen=max_len, out=outs[i % n_batches], lse=lses[i % n_batches])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # rough per-step time to size the timed region
+    t0 = time.perf_counter()
+    for i in range(n_batches):
+        step(i)
+    torch.cuda.synchronize()
+    rough = (time.perf_counter() - t0) / n_batches
+    steps = args.steps or max(n_batches, int(2.0 / max(rough, 1e-6)))
+    steps = max(n_batches, (steps // n_batches) * n_batches)  # whole passes over the batches
+
+    stream = torch.cuda.current_stream(dev)
+    use_graph = not args.no_graph
+    graph = None
+    if use_graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0)  # one eager call on the capture stream before capture
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n_batches):
+                step(i)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    if use_graph:
+        for _ in range(steps // n_batches):
+            graph.replay()
+    else:
+        for i in range(steps):
+            step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    sec = ms / 1e3
+
+    # replayed results must equal an eager call on the same inputs (bitwise)
+    ref_out = torch.empty_like(outs[0])
+    ref_lse = torch.empty_like(lses[0])
+    x0 = inputs[0]
+    attn_fwd(x0["q"], x0["k"], x0["v"], x0["kd"], x0["vd"], n_depth=w.n_depth, causal=w.causal, scale=w.scale,
+             cu_seqlens=cu, max_seqlen=max_len, out=ref_out, lse=ref_lse)
+    torch.cuda.synchronize()
+    replay_ok = bool(torch.equal(ref_out, outs[0]) and torch.equal(ref_lse, lses[0]))
+    if not replay_ok:
+        print("error: timed replays differ from an eager call", file=sys.stderr)
+
+    flops = w.seq_flops() + w.depth_flops()
+    tflops = flops / sec / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.bf16 else "f32",
+        "data": "synthetic (seeded counter-based N(0,1) quantile grid)",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "seq_len": w.seqlen,
+            "seqlens": list(w.seqlens) if w.varlen else None,
+            "n_heads_q": w.n_heads_q,
+            "n_heads_kv": w.n_heads_kv,
+            "head_dim": w.head_dim,
+            "n_depth": w.n_depth,
+            "causal": w.causal,
+            "input_batches": n_batches,
+            "graph": use_graph,
+        },
+        "parts": {
+            "seq_tflops_in_fused": round(w.seq_flops() / sec / 1e12, 3),
+            "mfma_frac_of_peak": round(tflops / (PEAK_BF16_TFLOPS if w.bf16 else PEAK_F32_TFLOPS), 4),
+            "depth_kv_gbs_in_fused": round(w.depth_bytes() / sec / 1e9, 1),
+            "all_bytes_gbs": round(w.total_bytes() / sec / 1e9, 1),
+            "hbm_frac_of_peak": round(w.total_bytes() / sec / 1e9 / PEAK_HBM_GBS, 4),
+        },
+        "kernel": kernel_name(w),
+        "kernel_source_sha": kernel_source_sha(),
+        "replay_matches_eager": replay_ok,
+        "roofline": roofline(w, sec),
+        "cpu_baseline": None,
+    }
+    del inputs, outs, lses, graph
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0 if replay_ok else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

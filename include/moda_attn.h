@@ -1,0 +1,111 @@
+/*
+ * moda_attn.h - C ABI of the MoDA joint sequence/depth attention forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operator: "Mixture-of-Depths Attention" (arXiv 2603.15619), MoDA deck slide
+ * "One denominator allocates probability across both memories" (teaching form of
+ * paper Sec. 2.2 / Algorithm 1). For query head h and token t of a sequence:
+ *
+ *   a_j = scale * <q_t, k_j>             sequence keys j <= t (all j if causal == 0)
+ *   b_i = scale * <q_t, k_depth_{t,i}>   the token's own depth slots i < n_depth
+ *   out_t = (sum_j e^{a_j} v_j + sum_i e^{b_i} v_depth_{t,i})
+ *           / (sum_j e^{a_j} + sum_i e^{b_i})
+ *   lse_t = ln(sum_j e^{a_j} + sum_i e^{b_i})        (natural log, float32)
+ *
+ * One numerator and one denominator span both key sets; this is not the sum of
+ * two separate softmaxes. Query head h reads key/value head h / G (sequence and
+ * depth alike), G = n_heads_q / n_heads_kv, contiguous groups (Table 1 of the
+ * paper groups the depth cache by G).
+ *
+ * Layouts (row-major, last dimension contiguous, no padding):
+ *   q, out    [B, T, Hq, d]            varlen: [N, Hq, d]   (out in out_dtype)
+ *   k, v      [B, T, Hkv, d]           varlen: [N, Hkv, d]
+ *   k_depth,
+ *   v_depth   [B, T, S_cap, Hkv, d]    varlen: [N, S_cap, Hkv, d]
+ *   lse       [B, Hq, T] float32       varlen: [Hq, N] float32
+ * Slots [0, n_depth) of the slot axis are read; n_depth <= S_cap.
+ *
+ * Ownership: every pointer is device memory owned by the caller; the library
+ * allocates nothing, keeps no pointer after returning, and launches
+ * asynchronously on `stream` (a hipStream_t; NULL = the default stream). `out`
+ * and `lse` are fully overwritten for every valid row; nothing else is written.
+ *
+ * Errors: all checks run on the host before any device work. On a non-zero
+ * return nothing was launched and the outputs are untouched, except MODA_ERR_HIP,
+ * which reports a failed launch. moda_last_error() then describes the failure
+ * (per calling thread). The device contents of cu_seqlens are not checked on the
+ * host: offsets are clamped to [0, N] on the device, so malformed offsets give
+ * unspecified values but never an out-of-bounds access.
+ */
+#ifndef MODA_ATTN_H
+#define MODA_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MODA_ABI_VERSION 1
+
+/* status codes */
+#define MODA_OK 0
+#define MODA_ERR_NULL 1        /* a required pointer is NULL                      */
+#define MODA_ERR_SHAPE 2       /* sizes negative, inconsistent or too large       */
+#define MODA_ERR_DTYPE 3       /* unknown dtype code or unsupported dtype pair    */
+#define MODA_ERR_ALIGN 4       /* a tensor pointer is not 16-byte aligned         */
+#define MODA_ERR_UNSUPPORTED 5 /* valid request outside what is built (head_dim)  */
+#define MODA_ERR_HIP 6         /* the HIP runtime rejected the launch             */
+#define MODA_ERR_VALUE 7       /* scale not finite and positive                   */
+
+/* dtype codes. `dtype` is the storage type of q, k, v, k_depth and v_depth;
+ * `out_dtype` that of out. Supported pairs: (F32, F32); (BF16, BF16) and
+ * (BF16, F32). bf16 inputs are computed with fp32 accumulation and fp32 softmax
+ * state; the probabilities enter the P.V product rounded to bf16. A bf16 `out`
+ * is the fp32 result rounded to nearest-even once, after normalisation. */
+#define MODA_DTYPE_F32 0
+#define MODA_DTYPE_BF16 1
+
+/*
+ * Joint sequence/depth attention forward over B equal-length sequences.
+ *
+ * batch (B) >= 0, seqlen (T) >= 0: B * T == 0 returns MODA_OK with no launch.
+ * n_heads_q % n_heads_kv == 0. head_dim (d) in {64, 128}.
+ * depth_capacity (S_cap) >= n_depth >= 0; k_depth / v_depth may be NULL only when
+ * n_depth == 0. lse may be NULL (not written). scale > 0 and finite (the MoDA
+ * operator uses 1/sqrt(d)). causal: 1 = keys j <= t (the MoDA operator), 0 = all
+ * keys of the sequence.
+ * Returns MODA_OK or an error code above.
+ */
+int moda_attn_fwd(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
+                  void* out, float* lse, int32_t dtype, int32_t out_dtype, int64_t batch, int64_t seqlen,
+                  int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
+                  int32_t n_depth, int32_t causal, float scale, void* stream);
+
+/*
+ * Same operator over packed variable-length sequences.
+ *
+ * cu_seqlens: DEVICE pointer to n_seqs + 1 non-decreasing int32 offsets,
+ * cu_seqlens[0] == 0, cu_seqlens[n_seqs] == total_tokens (N); sequence s holds
+ * packed tokens [cu_seqlens[s], cu_seqlens[s+1]). max_seqlen must be >= every
+ * sequence length (rows beyond max_seqlen are not computed). Attention never
+ * crosses a sequence boundary, for the sequence keys nor for the depth slots.
+ * n_seqs == 0 or total_tokens == 0 returns MODA_OK with no launch.
+ */
+int moda_attn_fwd_varlen(const void* q, const void* k, const void* v, const void* k_depth,
+                         const void* v_depth, void* out, float* lse, int32_t dtype, int32_t out_dtype,
+                         const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen,
+                         int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
+                         int32_t n_depth, int32_t causal, float scale, void* stream);
+
+/* Description of the last non-OK status returned on the calling thread ("" if none). */
+const char* moda_last_error(void);
+
+/* MODA_ABI_VERSION of the loaded library. */
+int32_t moda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MODA_ATTN_H */

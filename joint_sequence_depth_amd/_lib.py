@@ -1,0 +1,184 @@
+"""ctypes binding of libmoda_attn.so (argument marshalling only).
+
+Every step of the computation runs in the HIP library. torch supplies device
+memory and the current stream. There is no fallback: without the built library
+(or without a GPU) the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoda_attn.so")
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+STATUS_NAMES = {
+    0: "MODA_OK",
+    1: "MODA_ERR_NULL",
+    2: "MODA_ERR_SHAPE",
+    3: "MODA_ERR_DTYPE",
+    4: "MODA_ERR_ALIGN",
+    5: "MODA_ERR_UNSUPPORTED",
+    6: "MODA_ERR_HIP",
+    7: "MODA_ERR_VALUE",
+}
+
+# every symbol include/moda_attn.h declares
+EXPORTS = ("moda_attn_fwd", "moda_attn_fwd_varlen", "moda_last_error", "moda_abi_version")
+
+_lib = None
+
+
+class ModaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the shared library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m joint_sequence_depth_amd.build` "
+                "(there is no non-HIP fallback)"
+            )
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        L.moda_attn_fwd.argtypes = [vp] * 7 + [i32, i32, i64, i64, i32, i32, i32, i32, i32, i32, f32, vp]
+        L.moda_attn_fwd.restype = ctypes.c_int
+        L.moda_attn_fwd_varlen.argtypes = [vp] * 7 + [i32, i32, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+        L.moda_attn_fwd_varlen.restype = ctypes.c_int
+        L.moda_last_error.argtypes = []
+        L.moda_last_error.restype = ctypes.c_char_p
+        L.moda_abi_version.argtypes = []
+        L.moda_abi_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise ModaError(status, lib().moda_last_error().decode(errors="replace"))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def attn_fwd(
+    q,
+    k,
+    v,
+    k_depth=None,
+    v_depth=None,
+    n_depth: Optional[int] = None,
+    causal: bool = True,
+    scale: Optional[float] = None,
+    cu_seqlens=None,
+    max_seqlen: Optional[int] = None,
+    out=None,
+    lse=None,
+    stream=None,
+    out_dtype=None,
+    return_lse: bool = True,
+):
+    """MoDA joint sequence/depth attention forward through the C ABI.
+
+    Batch layout: q [B,T,Hq,d], k/v [B,T,Hkv,d], k_depth/v_depth [B,T,S_cap,Hkv,d].
+    Packed layout (cu_seqlens, int32 [n_seqs+1] on the device): q [N,Hq,d], k/v
+    [N,Hkv,d], depth [N,S_cap,Hkv,d]. Returns (out, lse) with out like q and lse
+    float32 [B,Hq,T] or [Hq,N]. ``n_depth`` defaults to the slot capacity (0 without
+    depth tensors); ``scale`` to 1/sqrt(d). ``out_dtype`` (torch.float32 is allowed
+    for bfloat16 inputs) defaults to q's dtype, or to ``out``'s when it is given.
+    With ``return_lse=False`` no lse is written (NULL at the C ABI) and None is returned.
+    """
+    import torch
+
+    varlen = cu_seqlens is not None
+    lead = 1 if varlen else 2
+    if q.dim() != lead + 2 or k.dim() != lead + 2 or v.dim() != lead + 2:
+        raise ValueError("q, k, v must be [B,T,H,d] (or [N,H,d] with cu_seqlens)")
+    for t in (q, k, v, k_depth, v_depth, out, lse, cu_seqlens):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if t is not None and t.device.type != "cuda":
+            raise ValueError("all tensors must be on the GPU")
+    d = q.shape[-1]
+    Hq, Hkv = q.shape[-2], k.shape[-2]
+    if k.shape != v.shape or k.shape[:-2] != q.shape[:-2] or k.shape[-1] != d:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if k_depth is not None:
+        if v_depth is None or k_depth.shape != v_depth.shape:
+            raise ValueError("k_depth and v_depth must both be given with one shape")
+        if k_depth.dim() != lead + 3 or k_depth.shape[:lead] != q.shape[:lead] or k_depth.shape[-2:] != (Hkv, d):
+            raise ValueError(f"depth tensors must be [..., S_cap, Hkv, d], got {tuple(k_depth.shape)}")
+        if k_depth.dtype != q.dtype or v_depth.dtype != q.dtype:
+            raise TypeError("depth tensors must share q's dtype")
+        s_cap = k_depth.shape[lead]
+    else:
+        s_cap = 0
+    if n_depth is None:
+        n_depth = s_cap
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else q.dtype
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype:
+        raise ValueError("out must have q's shape and out_dtype")
+    if varlen:
+        N = q.shape[0]
+        lse_shape = (Hq, N)
+    else:
+        B, T = q.shape[0], q.shape[1]
+        lse_shape = (B, Hq, T)
+    if not return_lse:
+        lse = None
+    elif lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    elif tuple(lse.shape) != lse_shape or lse.dtype != torch.float32:
+        raise ValueError(f"lse must be float32 {lse_shape}")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    code = _dtype_code(q)
+    out_code = _dtype_code(out)
+    L = lib()
+    if varlen:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
+        n_seqs = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            cu_host = cu_seqlens.cpu()
+            max_seqlen = int((cu_host[1:] - cu_host[:-1]).max()) if n_seqs > 0 else 0
+        status = L.moda_attn_fwd_varlen(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(k_depth), _ptr(v_depth), _ptr(out), _ptr(lse),
+            code, out_code, _ptr(cu_seqlens), n_seqs, q.shape[0], int(max_seqlen), Hq, Hkv, d, s_cap, int(n_depth),
+            int(bool(causal)), float(scale), stream,
+        )
+    else:
+        status = L.moda_attn_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(k_depth), _ptr(v_depth), _ptr(out), _ptr(lse),
+            code, out_code, q.shape[0], q.shape[1], Hq, Hkv, d, s_cap, int(n_depth), int(bool(causal)), float(scale), stream,
+        )
+    _check(status)
+    return out, lse

@@ -1,0 +1,50 @@
+// Internal interface between the host dispatch (moda_attn.hip) and the kernels.
+// Not part of the public C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moda {
+
+// One launch of the fused joint sequence/depth attention forward.
+// Token n of segment s is packed token seg_start(s) + t, 0 <= t < seg_len(s).
+// Element offsets (in elements of the input dtype, always 64-bit):
+//   q, out : (n * Hq + h) * D + c
+//   k, v   : (n * Hkv + hk) * D + c
+//   depth  : ((n * S_cap + i) * Hkv + hk) * D + c
+//   lse    : lse_seg_base(s) + h * lse_head_stride + t
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* kd;
+  const void* vd;
+  void* out;
+  float* lse;  // may be null
+
+  const int32_t* cu_seqlens;  // device, n_seg + 1 entries; null = uniform segments
+  int64_t uniform_len;        // segment length when cu_seqlens is null
+  int64_t total_tokens;       // N: every packed index is clamped below this
+  int32_t n_seg;
+  int32_t n_qblocks;          // query blocks per (segment, head group)
+
+  int32_t Hq, Hkv, G;
+  int32_t n_hgroups;          // G / heads-per-block
+  int32_t S_cap, n_depth;
+  int32_t causal;
+  float scale_log2;           // scale * log2(e): logits go to base 2
+
+  int64_t lse_head_stride;    // T (batch layout) or N (packed layout)
+  int32_t lse_batch_layout;   // 1: base = s * Hq * T; 0: base = seg_start
+  int64_t n_tiles;
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_fwd_bf16(const Params& p, int head_dim, int heads_per_block, bool out_f32, hipStream_t stream);
+hipError_t launch_fwd_f32(const Params& p, int head_dim, hipStream_t stream);
+
+// Rows (expanded query rows = tokens x heads) covered by one bf16 workgroup.
+constexpr int kBlockRows = 128;
+constexpr int kF32BlockRows = 64;
+
+}  // namespace moda

@@ -1,0 +1,152 @@
+"""The C ABI library on the host: it loads, exports every declared symbol, and its
+host-side checks reject bad arguments before any device work (no GPU needed: no
+call here reaches a launch)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from joint_sequence_depth_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moda_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.moda_abi_version() == 1
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    codes = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (MODA_(?:OK|ERR_\w+))\s+(\d+)", text)}
+    assert {v: k for k, v in codes.items()} == _lib.STATUS_NAMES
+
+
+# Fake, 16-byte aligned addresses: every case below must fail validation, which
+# runs before any HIP call. Skipped where a GPU is present, so that a wrong
+# expectation can never turn into a launch on fake pointers.
+P = 0x10000
+A = dict(q=P, k=P, v=P, kd=P, vd=P, out=P, lse=P, dtype=1, odt=1, B=1, T=16, Hq=4, Hkv=2, d=64, Scap=4, S=4, causal=1,
+         scale=0.125)
+
+
+@pytest.fixture(autouse=True)
+def _no_gpu_here():
+    try:
+        import torch
+
+        if torch.cuda.is_available():
+            pytest.skip("host-only validation tests run where no GPU can be reached")
+    except ImportError:
+        pass
+
+
+def call(**kw):
+    a = dict(A)
+    a.update(kw)
+    L = _lib.lib()
+    return L.moda_attn_fwd(a["q"], a["k"], a["v"], a["kd"], a["vd"], a["out"], a["lse"], a["dtype"], a["odt"], a["B"], a["T"],
+                           a["Hq"], a["Hkv"], a["d"], a["Scap"], a["S"], a["causal"], a["scale"], None)
+
+
+def callv(cu=P, n_seqs=2, N=16, max_len=8, **kw):
+    a = dict(A)
+    a.update(kw)
+    L = _lib.lib()
+    return L.moda_attn_fwd_varlen(a["q"], a["k"], a["v"], a["kd"], a["vd"], a["out"], a["lse"], a["dtype"], a["odt"], cu,
+                                  n_seqs, N, max_len, a["Hq"], a["Hkv"], a["d"], a["Scap"], a["S"], a["causal"],
+                                  a["scale"], None)
+
+
+def err():
+    return _lib.lib().moda_last_error().decode()
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(q=None), 1),
+        (dict(out=None), 1),
+        (dict(kd=None), 1),
+        (dict(dtype=2), 3),
+        (dict(dtype=-1), 3),
+        (dict(odt=5), 3),
+        (dict(dtype=0, odt=1), 3),
+        (dict(Hq=3, Hkv=2), 2),
+        (dict(Hkv=0), 2),
+        (dict(d=96), 5),
+        (dict(d=256), 5),
+        (dict(S=5, Scap=4), 2),
+        (dict(S=-1), 2),
+        (dict(B=-1), 2),
+        (dict(T=-5), 2),
+        (dict(q=P + 8), 4),
+        (dict(vd=P + 2), 4),
+        (dict(lse=P + 2), 4),
+        (dict(scale=0.0), 7),
+        (dict(scale=-1.0), 7),
+        (dict(scale=math.inf), 7),
+        (dict(scale=math.nan), 7),
+        (dict(causal=2), 7),
+    ],
+)
+def test_validation_rejects(kw, code):
+    assert call(**kw) == code
+    assert err()
+
+
+def test_depth_pointers_optional_without_slots():
+    # n_depth == 0 with NULL depth pointers passes the depth checks; make it fail
+    # later on purpose (bad head_dim) to stay host-only.
+    assert call(kd=None, vd=None, S=0, Scap=0, d=96) == 5
+
+
+def test_empty_problems_are_ok_without_launch():
+    assert call(B=0) == 0
+    assert call(T=0, q=None) == 0
+    assert callv(n_seqs=0) == 0
+    assert callv(N=0) == 0
+    assert err() == ""
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(cu=None), 1),
+        (dict(cu=P + 2), 4),
+        (dict(max_len=17), 2),
+        (dict(n_seqs=-1), 2),
+        (dict(N=-3), 2),
+        (dict(d=32), 5),
+    ],
+)
+def test_varlen_validation_rejects(kw, code):
+    assert callv(**kw) == code
+    assert err()
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libmoda_attn.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()
+
+
+def test_ctypes_signatures():
+    L = _lib.lib()
+    assert len(L.moda_attn_fwd.argtypes) == 19
+    assert len(L.moda_attn_fwd_varlen.argtypes) == 21
+    assert L.moda_last_error.restype is ctypes.c_char_p
