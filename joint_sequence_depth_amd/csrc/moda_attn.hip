@@ -23,14 +23,17 @@ int fail(int code, const char* fmt, ...) {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 // Query heads handled together by one bf16 workgroup: the largest power of two
-// (at most 8) dividing the group size, so that every workgroup's heads share one
-// KV head and its depth slots are read once for all of them.
+// (at most 4) dividing the group size. A workgroup's heads share one KV head, so
+// its depth slot rows are read once for all of them; the head groups of one KV
+// head run side by side and meet in L2.
 int heads_per_block(int G) {
-  if (G % 8 == 0) return 8;
   if (G % 4 == 0) return 4;
   if (G % 2 == 0) return 2;
   return 1;
 }
+
+struct Common;
+int depth_mode(const Common& c, int waves);
 
 struct Common {
   const void *q, *k, *v, *kd, *vd;
@@ -63,6 +66,21 @@ int check_common(const Common& c) {
   return MODA_OK;
 }
 
+// Depth scheduling of the bf16 kernel when n_depth > 0: 1 = depth waves beside
+// the sequence waves, 2 = each wave runs the depth pass and the sequence loop in
+// turn (two workgroups per CU, alternating order).
+int depth_mode(const Common& c, int waves) {
+#ifdef MODA_FORCE_DEPTH_MODE
+  (void)c;
+  (void)waves;
+  return MODA_FORCE_DEPTH_MODE;
+#else
+  (void)c;
+  (void)waves;
+  return 2;
+#endif
+}
+
 moda::Params base_params(const Common& c) {
   moda::Params p{};
   p.q = c.q;
@@ -88,13 +106,31 @@ int dispatch(moda::Params& p, const Common& c, int64_t n_seg, int64_t max_len, h
   hipError_t err;
   if (c.dtype == MODA_DTYPE_BF16) {
     const int gb = heads_per_block(p.G);
-    const int tok = moda::kBlockRows / gb;
-    const int64_t nqb = (max_len + tok - 1) / tok;
     p.n_hgroups = p.G / gb;
+    const int64_t n_pairs = n_seg * p.Hkv;
+    // Waves per workgroup: the largest of 4, 2, 1 that still gives every CU two
+    // workgroups (fewer rows per workgroup for small problems).
+    int waves = 1;
+    for (int w = 4; w >= 2; w /= 2) {
+      const int tok = moda::kWaveRows * w / gb;
+      if (n_pairs * p.n_hgroups * ((max_len + tok - 1) / tok) >= 512) {
+        waves = w;
+        break;
+      }
+    }
+    const int tok = moda::kWaveRows * waves / gb;
+    const int64_t nqb = (max_len + tok - 1) / tok;
     p.n_qblocks = (int32_t)nqb;
-    p.n_tiles = n_seg * p.Hkv * p.n_hgroups * nqb;
+    p.n_tiles = n_pairs * p.n_hgroups * nqb;
+    p.xcd_interleave = (n_pairs % 8 == 0) ? 1 : 0;
+    p.depth_mode = depth_mode(c, waves);
+#ifdef MODA_FORCE_SERIAL_ORDER
+    p.serial_order = MODA_FORCE_SERIAL_ORDER;
+#else
+    p.serial_order = 0;
+#endif
     if (nqb > kMaxTiles || p.n_tiles > kMaxTiles) return fail(MODA_ERR_SHAPE, "problem too large for one launch");
-    err = moda::launch_fwd_bf16(p, c.d, gb, c.out_dtype == MODA_DTYPE_F32, stream);
+    err = moda::launch_fwd_bf16(p, c.d, gb, waves, c.out_dtype == MODA_DTYPE_F32, stream);
   } else {
     const int64_t nqb = (max_len + moda::kF32BlockRows - 1) / moda::kF32BlockRows;
     p.n_hgroups = 1;

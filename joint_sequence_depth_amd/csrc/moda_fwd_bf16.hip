@@ -7,26 +7,40 @@
 // The running state (m, acc, o) of slide "Shared online-softmax states preserve
 // the joint operator" is carried in base 2: logits are multiplied by
 // scale * log2(e) so that exp2 reproduces the natural exponential (deck backup
-// slide "pseudocode needs implementation-level checks").
+// slide "pseudocode needs implementation-level checks"). The slide processes the
+// sequence blocks, then the depth blocks, through one state; here the two key
+// sets are folded into two partial states by different waves at the same time
+// and merged by one more application of the same update before the single
+// normalisation, which is the same operator up to the order of rounding.
 //
-// Work unit: one workgroup (4 waves, 256 threads) owns 128 expanded query rows:
-// TOK = 128 / GB tokens x GB query heads of one KV head (rows ordered token-major,
-// row r -> token r / GB, head r % GB, as in the expanded-row map of the deck's
-// backup slide on grouped indexing). Wave w owns rows [32 w, 32 w + 32).
+// Work unit: one workgroup owns 32 NW expanded query rows (NW in {1, 2, 4}):
+// TOK = 32 NW / GB tokens x GB query heads of one KV head (rows ordered
+// token-major, row r -> token r / GB, head r % GB, as in the expanded-row map of
+// the deck's backup slide on grouped indexing). The workgroup has two roles:
 //
-// Phase 1, depth (HBM-bound): each wave streams the depth K/V of its tokens.
-// LPR = D / 8 lanes hold one 16-byte slice of a slot row, so one 128-bit load per
-// lane covers 64 / LPR slot rows (one per token group). A token's slot row is
-// read ONCE and dotted with all GB query heads of the group. The per-row depth
-// state (m, acc, o) goes through LDS into the MFMA accumulator layout below.
+//  * NW sequence waves (MFMA-bound). Wave w owns rows [32 w, 32 w + 32). A
+//    flash-style loop over 64-key blocks of K and V^T staged in LDS (double
+//    buffered, one barrier per block). S^T = K Q^T on v_mfma_f32_32x32x16_bf16
+//    puts one query row per lane (lanes l and l + 32 hold the two halves of its
+//    64 keys), so the row max needs one cross-half exchange and the rescale by
+//    alpha is a per-lane multiply. O^T += V^T P^T takes the probabilities straight
+//    from the S^T registers: the contraction index (keys) is permuted identically
+//    in both operands.
 //
-// Phase 2, sequence (MFMA-bound): flash-style loop over 64-key blocks of K and
-// V^T staged in LDS (double buffered, one barrier per block). S^T = K Q^T on
-// v_mfma_f32_32x32x16_bf16 puts one query row per lane (lanes l and l + 32 hold
-// the two halves of its 64 keys), so the row max needs one cross-half exchange
-// and the rescale by alpha is a per-lane multiply. O^T += V^T P^T reuses the
-// probabilities straight from the S^T registers: the contraction index (keys) is
-// permuted identically in both operands.
+//  * NW depth waves (HBM-bound), present when n_depth > 0. Depth wave w streams
+//    the depth K/V of the tokens of rows [32 w, 32 w + 32). LPR = D / 8 lanes hold
+//    one 16-byte slice of a slot row, so one 128-bit load per lane covers 64 / LPR
+//    slot rows (one per token). Each slot row is read ONCE and dotted with all GB
+//    query heads of the group (v_dot2_f32_bf16 on the packed operands). Loads run
+//    NBUF - 1 batches of U slots ahead of the arithmetic in register buffers (the
+//    depth waves have the sequence waves' register budget). Finished row states
+//    (m, acc, o) go to a dedicated LDS area. The depth waves take part in the
+//    sequence loop's barriers with an even share of their steps between any two,
+//    so both roles progress together: the workgroup's time is close to the larger
+//    of its HBM time and its MFMA time rather than their sum.
+//
+// After the last barrier the sequence waves merge the depth state of their rows,
+// normalise once and write.
 //
 // Rounding: QK^T and PV accumulate in fp32; P is rounded to bf16 (RNE) before PV;
 // the output is written in fp32, or rounded to bf16 (RNE) once, after the single
@@ -37,21 +51,29 @@ namespace moda {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BN = 64;  // keys per sequence block
-constexpr int WAVES = 4;
-constexpr int WROWS = 32;  // rows per wave
+constexpr int BN = 64;     // keys per sequence block
+constexpr int WROWS = 32;  // query rows per wave
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.693147180559945309417f;
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// (a, b) -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const uint32_t x = __builtin_bit_cast(uint16_t, (__bf16)a);
-  const uint32_t y = __builtin_bit_cast(uint16_t, (__bf16)b);
-  return x | (y << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// a.lo * b.lo + a.hi * b.hi + c, bf16 pairs, fp32 accumulation
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -60,16 +82,61 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// Workgroups are handed to the 8 XCDs round-robin (id % 8). Give each XCD one
-// contiguous range of logical tiles, so the query blocks of one (segment, KV head)
-// run on one XCD and share its L2 for the K/V blocks they all read.
-__device__ __forceinline__ int64_t xcd_remap(int64_t id, int64_t n) {
-  const int64_t x = id & 7, j = id >> 3;
-  const int64_t q = n >> 3, r = n & 7;
-  return x * q + (x < r ? x : r) + j;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-template <int D, int GB>
+// Sum over aligned groups of LPR (8 or 16) lanes with DPP moves. Every step adds
+// a lane pair in both orders, so all lanes of a group end with the same bits.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float s) {
+  s += dpp_f<0xB1>(s);   // quad_perm [1,0,3,2]
+  s += dpp_f<0x4E>(s);   // quad_perm [2,3,0,1]
+  s += dpp_f<0x141>(s);  // row_half_mirror: the other quad of the 8-lane half
+  if constexpr (LPR == 16) s += dpp_f<0x140>(s);  // row_mirror: the other half of the row
+  return s;
+}
+
+struct Tile {
+  int seg, hk, hg, qb;
+};
+
+// A pair = (segment, KV head); its tiles are (query block, head group), head group
+// fastest, so the workgroups of a KV head's head groups run side by side and share
+// that token block's depth rows in L2. Workgroups go to the 8 XCDs round-robin
+// (id % 8). With a multiple of 8 pairs, pair p runs all of its tiles on XCD p % 8:
+// its K/V blocks, read by every query block, stay in that XCD's L2, and every XCD
+// gets an equal share of every segment, whatever the segment lengths. Within a
+// pair, late (heavy causal) query blocks go first.
+__device__ __forceinline__ Tile decode_tile(const Params& p) {
+  const int64_t id = blockIdx.x;
+  const int64_t per_pair = (int64_t)p.n_qblocks * p.n_hgroups;
+  int64_t pair, r;
+  if (p.xcd_interleave) {
+    const int64_t x = id & 7, j = id >> 3;
+    pair = (j / per_pair) * 8 + x;
+    r = j % per_pair;
+  } else {
+    pair = id / per_pair;
+    r = id % per_pair;
+  }
+  Tile t;
+  t.hg = (int)(r % p.n_hgroups);
+  t.qb = p.n_qblocks - 1 - (int)(r / p.n_hgroups);
+  t.hk = (int)(pair % p.Hkv);
+  t.seg = (int)(pair / p.Hkv);
+  return t;
+}
+
+// How the depth slots are scheduled against the sequence loop.
+enum Mode : int {
+  kNoDepth = 0,  // n_depth == 0: sequence waves only
+  kSplit = 1,    // NW extra depth waves run beside the NW sequence waves (one barrier schedule)
+  kSerial = 2,   // every wave runs a depth pass and the sequence loop, one after the other
+};
+
+template <int D, int NW, int MODE>
 struct Smem {
   static constexpr int KS = D + 8;   // K tile row stride (bf16): 16 B skew per row
   static constexpr int VS = BN + 4;  // V^T tile row stride (bf16)
@@ -77,22 +144,36 @@ struct Smem {
   static constexpr int K_BYTES = 2 * BN * KS * 2;
   static constexpr int V_BYTES = 2 * D * VS * 2;
   static constexpr int SEQ_BYTES = K_BYTES + V_BYTES;
-  static constexpr int DEPTH_BYTES = (WAVES * WROWS * OS + 2 * WAVES * WROWS) * 4;
-  static constexpr int BYTES = SEQ_BYTES > DEPTH_BYTES ? SEQ_BYTES : DEPTH_BYTES;
+  // kSplit: a dedicated hand-off area; kSerial: the hand-off reuses the K/V area
+  static constexpr int OD_OFF = MODE == kSplit ? SEQ_BYTES : 0;
+  static constexpr int MD_OFF = OD_OFF + NW * WROWS * OS * 4;
+  static constexpr int AD_OFF = MD_OFF + NW * WROWS * 4;
+  static constexpr int END = AD_OFF + NW * WROWS * 4;
+  static constexpr int BYTES = MODE == kNoDepth ? SEQ_BYTES : (END > SEQ_BYTES ? END : SEQ_BYTES);
 };
 
-template <int D, int GB, bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
-  constexpr int TOK = kBlockRows / GB;  // tokens per workgroup
-  constexpr int TW = WROWS / GB;        // tokens per wave
-  constexpr int LPR = D / 8;            // lanes per 16-byte-sliced row of D
-  constexpr int NGRP = 64 / LPR;        // depth token groups per wave
-  constexpr int KPT = BN * LPR / 256;   // keys per thread per K/V block load
-  constexpr int KC = D / 16;            // k-chunks of Q K^T
-  constexpr int DT = D / 32;            // 32-wide d tiles of O^T
-  constexpr int U = 4;                  // depth slots per load batch
-  using SM = Smem<D, GB>;
-  static_assert(KPT >= 1 && (BN * LPR) % 256 == 0, "tile shape");
+template <int D, int GB, int NW, int MODE, bool OUT_F32>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW * (MODE == kSplit ? 2 : 1),
+                                                      64 * NW * (MODE == kSplit ? 2 : 1)),
+                          amdgpu_waves_per_eu(2, 2))) void
+moda_fwd_bf16_kernel(const Params p) {
+  constexpr int NSEQ = 64 * NW;                // threads of the sequence role
+  constexpr int TOK = WROWS * NW / GB;         // tokens per workgroup
+  constexpr int TW = WROWS / GB;               // tokens per wave
+  constexpr int LPR = D / 8;                   // lanes per 16-byte-sliced row of D
+  constexpr int NGRP = 64 / LPR;               // tokens per wave-wide depth load
+  constexpr int NTG = (TW + NGRP - 1) / NGRP;  // depth token groups per depth wave
+  constexpr int KPT = BN * LPR / NSEQ;         // keys per thread per K/V block load
+  constexpr int KC = D / 16;                   // k-chunks of Q K^T
+  constexpr int DT = D / 32;                   // 32-wide d tiles of O^T
+  constexpr int U = GB == 1 ? 8 : (GB == 2 ? 4 : 2);  // depth slots per load batch
+  constexpr bool QPRE = GB <= 2;               // prefetch a token's q rows with its first batch
+  constexpr int QBUF = QPRE ? GB : 1;
+  // depth load buffers (steps in flight + 1); a serial pass keeps the O^T
+  // accumulators live, so it gets fewer
+  constexpr int NBUF = MODE == kSplit ? (GB == 1 ? 3 : (GB == 2 ? 4 : 6)) : (GB == 1 ? 2 : (GB == 2 ? 3 : 4));
+  using SM = Smem<D, NW, MODE>;
+  static_assert(KPT >= 2 && KPT % 2 == 0 && BN * LPR == KPT * NSEQ, "tile shape");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[SM::BYTES];
 
@@ -100,14 +181,10 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  // ---- tile decode ------------------------------------------------------------
-  int64_t rest = xcd_remap(blockIdx.x, p.n_tiles);
-  const int qb = p.n_qblocks - 1 - (int)(rest % p.n_qblocks);  // heavy (late) blocks first
-  rest /= p.n_qblocks;
-  const int hg = (int)(rest % p.n_hgroups);
-  rest /= p.n_hgroups;
-  const int hk = (int)(rest % p.Hkv);
-  const int seg = (int)(rest / p.Hkv);
+  // ---- tile decode (uniform over the workgroup) ---------------------------------
+  const Tile tile = decode_tile(p);
+  const int qb = tile.qb, hg = tile.hg, hk = tile.hk, seg = tile.seg;
+  if (seg >= p.n_seg) return;
 
   int64_t seg_start, len;
   if (p.cu_seqlens) {
@@ -127,53 +204,72 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
   const int hbase = hk * p.G + hg * GB;  // first query head of this workgroup
   const float c2 = p.scale_log2;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(p.q);
-  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(p.k);
-  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(p.v);
+  const int64_t kend = p.causal ? (len < t0 + TOK ? len : t0 + TOK) : len;
+  const int nkb = (int)((kend + BN - 1) / BN);  // sequence key blocks; nkb + 1 barriers
 
-  float* od = reinterpret_cast<float*>(smem);  // [WAVES*WROWS][OS]
-  float* md = od + WAVES * WROWS * SM::OS;     // [WAVES*WROWS]
-  float* ad = md + WAVES * WROWS;              // [WAVES*WROWS]
+  float* od = reinterpret_cast<float*>(smem + SM::OD_OFF);  // [NW*WROWS][OS]
+  float* md = reinterpret_cast<float*>(smem + SM::MD_OFF);  // [NW*WROWS]
+  float* ad = reinterpret_cast<float*>(smem + SM::AD_OFF);  // [NW*WROWS]
 
-  // ---- phase 1: depth slots of each token --------------------------------------
-  const int n_depth = p.n_depth;
-  if (n_depth > 0) {
-    const uint16_t* __restrict__ KD = static_cast<const uint16_t*>(p.kd);
-    const uint16_t* __restrict__ VD = static_cast<const uint16_t*>(p.vd);
-    const int grp = lane / LPR, cl = lane % LPR;
-    const int64_t slot_stride = (int64_t)Hkv * D;
-    for (int tb = 0; tb < TW; tb += NGRP) {
-      const int tl = tb + grp;  // token index within the wave
-      const int64_t t = t0 + (int64_t)wave * TW + tl;
-      const bool valid = (tl < TW) && (t < len);
-      const int64_t n = seg_start + (valid ? t : 0);
-      float qf[GB][8];
-#pragma unroll
-      for (int g = 0; g < GB; ++g) {
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (valid) w = ldg16(Q + ((n * Hq + hbase + g) * D + 8 * cl));
-        qf[g][0] = lo_bf16(w.x); qf[g][1] = hi_bf16(w.x);
-        qf[g][2] = lo_bf16(w.y); qf[g][3] = hi_bf16(w.y);
-        qf[g][4] = lo_bf16(w.z); qf[g][5] = hi_bf16(w.z);
-        qf[g][6] = lo_bf16(w.w); qf[g][7] = hi_bf16(w.w);
-      }
-      float m[GB], a[GB], o[GB][8];
-#pragma unroll
-      for (int g = 0; g < GB; ++g) {
-        m[g] = NEG_INF;
-        a[g] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
-      }
-      const int64_t base = ((n * p.S_cap) * Hkv + hk) * (int64_t)D + 8 * cl;
-      for (int i0 = 0; i0 < n_depth; i0 += U) {
-        uint4 kw[U], vw[U];
+  // ================================================================ depth pass
+  // Folds the depth slots of the tokens of rows [32 dw, 32 dw + 32) into partial
+  // row states (m, acc, o) in LDS. With kSplit it also takes part in the sequence
+  // loop's nkb + 1 barriers, one even share of its steps between any two.
+  auto depth_pass = [&](const int dw) {
+    {
+      const int n_depth = p.n_depth;
+      const uint16_t* __restrict__ KD = static_cast<const uint16_t*>(p.kd);
+      const uint16_t* __restrict__ VD = static_cast<const uint16_t*>(p.vd);
+      const int grp = lane / LPR, cl = lane % LPR;
+      const int64_t slot_stride = (int64_t)Hkv * D;
+      const int nch = (n_depth + U - 1) / U;  // slot batches per token
+      const int n_it = NTG * nch;             // (token group, slot batch) steps
+
+      // Loads for step `it`: U slot rows of K and V (and the token's q rows at its
+      // first batch) into one of two register buffers. The loads are unconditional
+      // so the compiler keeps them in flight across the arithmetic: a slot past
+      // n_depth re-reads the last slot and a token past the segment re-reads its
+      // last token (cache hits); such logits are masked and such rows discarded.
+      auto issue = [&](int it, uint4(&kw)[U], uint4(&vw)[U], uint4(&qw)[QBUF]) {
+        it = it < n_it ? it : n_it - 1;  // the steps past the end re-load the last one (never processed)
+        const int tg = it / nch, ch = it - tg * nch;
+        const int tl = tg * NGRP + grp;
+        int64_t t = t0 + (int64_t)dw * TW + (tl < TW ? tl : TW - 1);
+        t = t < len ? t : len - 1;
+        const int64_t n = seg_start + t;
+        const int64_t base = (n * p.S_cap * Hkv + hk) * (int64_t)D + 8 * cl;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          kw[u] = make_uint4(0, 0, 0, 0);
-          vw[u] = make_uint4(0, 0, 0, 0);
-          if (valid && i0 + u < n_depth) {
-            kw[u] = ldg16(KD + base + (int64_t)(i0 + u) * slot_stride);
-            vw[u] = ldg16(VD + base + (int64_t)(i0 + u) * slot_stride);
+          const int slot = ch * U + u < n_depth ? ch * U + u : n_depth - 1;
+          kw[u] = ldg16(KD + base + slot * slot_stride);
+          vw[u] = ldg16(VD + base + slot * slot_stride);
+        }
+        if constexpr (QPRE) {  // every step: a fixed load count keeps the wait counts exact
+#pragma unroll
+          for (int g = 0; g < QBUF; ++g) qw[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * cl));
+        }
+      };
+
+      uint4 qc[GB];  // q rows of the current token, packed bf16
+      float m[GB], a[GB], o[GB][8];
+      auto process = [&](int it, const uint4(&kw)[U], const uint4(&vw)[U], const uint4(&qw)[QBUF]) {
+        const int tg = it / nch, ch = it - tg * nch;
+        const int tl = tg * NGRP + grp;
+        if (ch == 0) {
+          int64_t t = t0 + (int64_t)dw * TW + (tl < TW ? tl : TW - 1);
+          t = t < len ? t : len - 1;
+          const int64_t n = seg_start + t;
+#pragma unroll
+          for (int g = 0; g < GB; ++g) {
+            if constexpr (QPRE) {
+              qc[g] = qw[g < QBUF ? g : 0];
+            } else {
+              qc[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * cl));
+            }
+            m[g] = NEG_INF;
+            a[g] = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
           }
         }
 #pragma unroll
@@ -181,17 +277,12 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
           float b[U];
 #pragma unroll
           for (int u = 0; u < U; ++u) {
-            float s = qf[g][0] * lo_bf16(kw[u].x);
-            s = fmaf(qf[g][1], hi_bf16(kw[u].x), s);
-            s = fmaf(qf[g][2], lo_bf16(kw[u].y), s);
-            s = fmaf(qf[g][3], hi_bf16(kw[u].y), s);
-            s = fmaf(qf[g][4], lo_bf16(kw[u].z), s);
-            s = fmaf(qf[g][5], hi_bf16(kw[u].z), s);
-            s = fmaf(qf[g][6], lo_bf16(kw[u].w), s);
-            s = fmaf(qf[g][7], hi_bf16(kw[u].w), s);
-#pragma unroll
-            for (int off = LPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-            b[u] = (i0 + u < n_depth) ? s * c2 : NEG_INF;
+            float s = dot2(qc[g].x, kw[u].x, 0.f);
+            s = dot2(qc[g].y, kw[u].y, s);
+            s = dot2(qc[g].z, kw[u].z, s);
+            s = dot2(qc[g].w, kw[u].w, s);
+            s = group_sum<LPR>(s);
+            b[u] = (ch * U + u < n_depth) ? s * c2 : NEG_INF;
           }
           float mx = b[0];
 #pragma unroll
@@ -217,25 +308,63 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
           }
           m[g] = m_new;
         }
-      }
-      if (tl < TW) {
+        if (ch == nch - 1 && tl < TW) {
 #pragma unroll
-        for (int g = 0; g < GB; ++g) {
-          const int row = wave * WROWS + tl * GB + g;
-          float4* dst = reinterpret_cast<float4*>(od + row * SM::OS + 8 * cl);
-          dst[0] = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
-          dst[1] = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);
-          if (cl == 0) {
-            md[row] = m[g];
-            ad[row] = a[g];
+          for (int g = 0; g < GB; ++g) {
+            const int row = dw * WROWS + tl * GB + g;
+            float4* dst = reinterpret_cast<float4*>(od + row * SM::OS + 8 * cl);
+            dst[0] = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
+            dst[1] = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);
+            if (cl == 0) {
+              md[row] = m[g];
+              ad[row] = a[g];
+            }
+          }
+        }
+      };
+
+      // Barrier b closes the b-th of nkb + 1 equal shares of the n_it steps.
+      const int nbar = nkb + 1;
+      int bars = 0;
+      auto sync_until = [&](int it) {
+        if constexpr (MODE == kSplit) {
+          while (bars < nbar && (int)(((int64_t)n_it * (bars + 1)) / nbar) <= it) {
+            __syncthreads();
+            ++bars;
+          }
+        }
+      };
+
+      // NBUF register buffers, loads NBUF - 1 steps ahead. Every step issues the
+      // same number of loads, so the compiler waits exactly for the buffer it reads
+      // and leaves the others in flight.
+      uint4 kb[NBUF][U], vb[NBUF][U], qb[NBUF][QBUF];
+#pragma unroll
+      for (int j = 0; j < NBUF - 1; ++j) issue(j, kb[j], vb[j], qb[j]);
+      for (int it = 0; it < n_it; it += NBUF) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          issue(it + j + NBUF - 1, kb[(j + NBUF - 1) % NBUF], vb[(j + NBUF - 1) % NBUF], qb[(j + NBUF - 1) % NBUF]);
+          if (it + j < n_it) {
+            sync_until(it + j);
+            process(it + j, kb[j], vb[j], qb[j]);
           }
         }
       }
+      sync_until(n_it);  // kSplit: the remaining barriers; the last one publishes every row state
     }
-    __syncthreads();
+  };
+
+  if constexpr (MODE == kSplit) {
+    if (wave >= NW) {
+      depth_pass(wave - NW);
+      return;
+    }
   }
 
-  // ---- phase 2 set-up: this lane's query row -----------------------------------
+  // ============================================================ sequence role
+  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(p.k);
+  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(p.v);
   const int r = lane & 31;   // row within the wave (column of the 32x32 tiles)
   const int hh = lane >> 5;  // which half of each 16-wide contraction chunk
   const int rowb = wave * WROWS + r;
@@ -244,28 +373,48 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
   const bool row_valid = tq < len;
 
   f32x16 acc[DT];
-  float m_run, l_run;
-  if (n_depth > 0) {
-    m_run = md[rowb];
-    l_run = hh == 0 ? ad[rowb] : 0.f;
+  // running max (base 2), denominator of the unrounded p (for lse) and of the
+  // weights actually applied to V (for the output); one half of the keys per lane
+  float m_run = NEG_INF, l_run = 0.f, r_run = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+  // Folds this row's depth state (published in LDS) into (m_run, l_run, acc).
+  auto depth_fold = [&]() {
+    const float m_d = md[rowb];
+    const float m_new = fmaxf(m_run, m_d);
+    const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+    const float f_seq = fast_exp2(m_run - m_use);
+    const float f_dep = fast_exp2(m_d - m_use);
+    const float a_d = hh == 0 ? ad[rowb] * f_dep : 0.f;
+    l_run = l_run * f_seq + a_d;
+    r_run = r_run * f_seq + a_d;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const float4 x = *reinterpret_cast<const float4*>(od + rowb * SM::OS + 32 * dt + 8 * q4 + 4 * hh);
-        acc[dt][4 * q4 + 0] = x.x;
-        acc[dt][4 * q4 + 1] = x.y;
-        acc[dt][4 * q4 + 2] = x.z;
-        acc[dt][4 * q4 + 3] = x.w;
+        acc[dt][4 * q4 + 0] = fmaf(x.x, f_dep, acc[dt][4 * q4 + 0] * f_seq);
+        acc[dt][4 * q4 + 1] = fmaf(x.y, f_dep, acc[dt][4 * q4 + 1] * f_seq);
+        acc[dt][4 * q4 + 2] = fmaf(x.z, f_dep, acc[dt][4 * q4 + 2] * f_seq);
+        acc[dt][4 * q4 + 3] = fmaf(x.w, f_dep, acc[dt][4 * q4 + 3] * f_seq);
       }
-    __syncthreads();  // the hand-off area is reused for K/V blocks below
-  } else {
-    m_run = NEG_INF;
-    l_run = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+    m_run = m_new;
+  };
+
+  // kSerial: the two workgroups that share a CU run the depth pass first and
+  // last in turn (the first round of workgroups on an XCD's 32 CUs starts with
+  // it, the second with the sequence loop), so one streams from HBM while the
+  // other keeps the matrix cores busy.
+  const bool depth_first =
+      MODE == kSerial && (p.serial_order == 0 ? (((blockIdx.x >> 3) >> 5) & 1) == 0 : p.serial_order == 1);
+  if (MODE == kSerial && depth_first) {
+    depth_pass(wave);
+    __syncthreads();
+    depth_fold();
+    __syncthreads();  // the hand-off area is the K/V area
   }
 
   bf16x8 qf[KC];
@@ -280,25 +429,23 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
     }
   }
 
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);                  // [2][BN][KS]
-  uint16_t* Vt = reinterpret_cast<uint16_t*>(smem + SM::K_BYTES);    // [2][D][VS]
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);                // [2][BN][KS]
+  uint16_t* Vt = reinterpret_cast<uint16_t*>(smem + SM::K_BYTES);  // [2][D][VS]
 
-  const int64_t kend = p.causal ? (len < t0 + TOK ? len : t0 + TOK) : len;
-  const int nkb = (int)((kend + BN - 1) / BN);
   const int ld_cl = tid % LPR, ld_kg = tid / LPR;
   uint4 pk[KPT], pv[KPT];
 
+  // Unconditional loads (kept in flight by the compiler): a key past kend re-reads
+  // key kend - 1. Every such key lies beyond the causal limit of all rows of the
+  // workgroup or beyond the segment, so its score is masked and its p is 0.
   auto gload = [&](int kb) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int64_t key = (int64_t)kb * BN + ld_kg * KPT + j;
-      pk[j] = make_uint4(0, 0, 0, 0);
-      pv[j] = make_uint4(0, 0, 0, 0);
-      if (key < kend) {
-        const int64_t off = ((seg_start + key) * Hkv + hk) * (int64_t)D + 8 * ld_cl;
-        pk[j] = ldg16(K + off);
-        pv[j] = ldg16(V + off);
-      }
+      int64_t key = (int64_t)kb * BN + ld_kg * KPT + j;
+      key = key < kend ? key : kend - 1;
+      const int64_t off = ((seg_start + key) * Hkv + hk) * (int64_t)D + 8 * ld_cl;
+      pk[j] = ldg16(K + off);
+      pv[j] = ldg16(V + off);
     }
   };
   auto swrite = [&](int buf) {
@@ -318,13 +465,12 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
         w[j] = hi ? (x >> 16) : (x & 0xffffu);
       }
       uint16_t* dst = vt + (8 * ld_cl + e) * SM::VS;
-      if constexpr (KPT == 4) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
-      } else if constexpr (KPT == 2) {
+      if constexpr (KPT == 2) {
         *reinterpret_cast<uint32_t*>(dst) = w[0] | (w[1] << 16);
       } else {
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) dst[j] = (uint16_t)w[j];
+        for (int j = 0; j < KPT; j += 4)  // 8-byte stores: V^T rows are 8-byte aligned
+          *reinterpret_cast<uint2*>(dst + j) = make_uint2(w[j] | (w[j + 1] << 16), w[j + 2] | (w[j + 3] << 16));
       }
     }
   };
@@ -358,13 +504,15 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
       }
       const bool need_mask = (p.causal && k0 + BN - 1 > wave_tmin) || (k0 + BN > len);
       if (need_mask) {
+        // key k0 + off is visible iff off <= lim (32-bit offsets within the block)
+        const int64_t last = p.causal ? (tq < len - 1 ? tq : len - 1) : len - 1;
+        const int lim = (int)(last - k0 < BN ? last - k0 : BN);
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int64_t key = k0 + 32 * st + 8 * (i >> 2) + 4 * hh + (i & 3);
-            const bool vis = key < len && (!p.causal || key <= tq);
-            if (!vis) s[st][i] = NEG_INF;
+            const int off = 32 * st + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if (off > lim) s[st][i] = NEG_INF;
           }
       }
       float mx = NEG_INF;
@@ -372,17 +520,29 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c2);
-      const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      l_run *= alpha;
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+      // Lazy rescale: the reference max m_run only moves (and O, l are rescaled)
+      // when some row's block max exceeds it by more than 2^8; otherwise the
+      // probabilities, bounded by 2^8, accumulate against the old reference. The
+      // final o / l is the same; only the order of roundings differs.
+      if (__any(mx > m_run + 8.f)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);  // m_run = -inf at first: alpha = 0
+        l_run *= alpha;
+        r_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+          for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
+      // p rounded to bf16 feeds the P.V product. The output is normalised by the sum
+      // of exactly those rounded values (a bf16 dot with (1, 1)), so the weights on V
+      // sum to one and a dominant key keeps weight 1 whatever the reference max; lse
+      // uses the sum of the unrounded p.
       uint32_t pp[2][8];
-      float lsum = 0.f;
+      float lsum = 0.f, rsum = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -391,9 +551,10 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
           const float p1 = fast_exp2(fmaf(s[st][i + 1], c2, -m_use));
           lsum += p0 + p1;
           pp[st][i >> 1] = pack_bf16(p0, p1);
+          rsum = dot2(pp[st][i >> 1], 0x3F803F80u, rsum);
         }
       l_run += lsum;
-      m_run = m_new;
+      r_run += rsum;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -414,10 +575,19 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
     __syncthreads();
   }
 
+  // ---- fold in the depth state of this row ------------------------------------
+  if constexpr (MODE == kSplit) depth_fold();  // published by the loop's last barrier
+  if (MODE == kSerial && !depth_first) {        // the loop's last barrier freed the K/V area
+    depth_pass(wave);
+    __syncthreads();
+    depth_fold();
+  }
+
   // ---- normalise once and write ------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float r_tot = r_run + __shfl_xor(r_run, 32);
   if (row_valid) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = r_tot > 0.f ? 1.f / r_tot : 0.f;
     const int64_t obase = ((seg_start + tq) * Hq + hq) * (int64_t)D + 4 * hh;
     if constexpr (OUT_F32) {
       float* orow = static_cast<float*>(p.out) + obase;
@@ -446,33 +616,49 @@ __global__ __launch_bounds__(256, 2) void moda_fwd_bf16_kernel(const Params p) {
   }
 }
 
-template <int D, int GB>
+template <int D, int GB, int NW, int MODE>
 hipError_t launch_t(const Params& p, bool out_f32, hipStream_t stream) {
+  const dim3 grid((unsigned)p.n_tiles), block(64 * NW * (MODE == kSplit ? 2 : 1));
   if (out_f32)
-    hipLaunchKernelGGL((moda_fwd_bf16_kernel<D, GB, true>), dim3((unsigned)p.n_tiles), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((moda_fwd_bf16_kernel<D, GB, NW, MODE, true>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((moda_fwd_bf16_kernel<D, GB, false>), dim3((unsigned)p.n_tiles), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((moda_fwd_bf16_kernel<D, GB, NW, MODE, false>), grid, block, 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D, int GB, int NW>
+hipError_t launch_d(const Params& p, bool out_f32, hipStream_t stream) {
+  if (p.n_depth == 0) return launch_t<D, GB, NW, kNoDepth>(p, out_f32, stream);
+  if (p.depth_mode == kSplit) return launch_t<D, GB, NW, kSplit>(p, out_f32, stream);
+  return launch_t<D, GB, NW, kSerial>(p, out_f32, stream);
+}
+
+template <int D, int GB>
+hipError_t launch_w(const Params& p, int waves, bool out_f32, hipStream_t stream) {
+  switch (waves) {
+    case 1: return launch_d<D, GB, 1>(p, out_f32, stream);
+    case 2: return launch_d<D, GB, 2>(p, out_f32, stream);
+    case 4: return launch_d<D, GB, 4>(p, out_f32, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_g(const Params& p, int heads_per_block, int waves, bool out_f32, hipStream_t stream) {
+  switch (heads_per_block) {
+    case 1: return launch_w<D, 1>(p, waves, out_f32, stream);
+    case 2: return launch_w<D, 2>(p, waves, out_f32, stream);
+    case 4: return launch_w<D, 4>(p, waves, out_f32, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const Params& p, int head_dim, int heads_per_block, bool out_f32, hipStream_t stream) {
-  if (head_dim == 128) {
-    switch (heads_per_block) {
-      case 1: return launch_t<128, 1>(p, out_f32, stream);
-      case 2: return launch_t<128, 2>(p, out_f32, stream);
-      case 4: return launch_t<128, 4>(p, out_f32, stream);
-      case 8: return launch_t<128, 8>(p, out_f32, stream);
-    }
-  } else if (head_dim == 64) {
-    switch (heads_per_block) {
-      case 1: return launch_t<64, 1>(p, out_f32, stream);
-      case 2: return launch_t<64, 2>(p, out_f32, stream);
-      case 4: return launch_t<64, 4>(p, out_f32, stream);
-      case 8: return launch_t<64, 8>(p, out_f32, stream);
-    }
-  }
+hipError_t launch_fwd_bf16(const Params& p, int head_dim, int heads_per_block, int waves, bool out_f32,
+                           hipStream_t stream) {
+  if (head_dim == 128) return launch_g<128>(p, heads_per_block, waves, out_f32, stream);
+  if (head_dim == 64) return launch_g<64>(p, heads_per_block, waves, out_f32, stream);
   return hipErrorInvalidValue;
 }
 

@@ -36,15 +36,22 @@ struct Params {
 
   int64_t lse_head_stride;    // T (batch layout) or N (packed layout)
   int32_t lse_batch_layout;   // 1: base = s * Hq * T; 0: base = seg_start
+  int32_t xcd_interleave;     // 1: (segment, KV head) pairs go round-robin to the 8 XCDs
+  int32_t depth_mode;         // bf16 kernel with n_depth > 0: 1 = depth waves beside the
+                              // sequence waves, 2 = depth pass and sequence loop in turn
+  int32_t serial_order;       // depth_mode 2: 0 = alternate by workgroup round, 1 = depth
+                              // pass first, 2 = sequence loop first
   int64_t n_tiles;
 };
 
 // Launchers (return the hipError_t of the launch).
-hipError_t launch_fwd_bf16(const Params& p, int head_dim, int heads_per_block, bool out_f32, hipStream_t stream);
+hipError_t launch_fwd_bf16(const Params& p, int head_dim, int heads_per_block, int waves, bool out_f32,
+                           hipStream_t stream);
 hipError_t launch_fwd_f32(const Params& p, int head_dim, hipStream_t stream);
 
-// Rows (expanded query rows = tokens x heads) covered by one bf16 workgroup.
-constexpr int kBlockRows = 128;
+// Expanded query rows (tokens x grouped heads) per bf16 wave; a workgroup has 1,
+// 2 or 4 waves.
+constexpr int kWaveRows = 32;
 constexpr int kF32BlockRows = 64;
 
 }  // namespace moda
