@@ -45,6 +45,8 @@
 // Rounding: QK^T and PV accumulate in fp32; P is rounded to bf16 (RNE) before PV;
 // the output is written in fp32, or rounded to bf16 (RNE) once, after the single
 // normalisation.
+#include <type_traits>
+
 #include "moda_internal.h"
 
 namespace moda {
@@ -78,7 +80,18 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The value of lane l ^ 32 (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float other_half(float x, int lane) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, lane < 32 ? sw[1] : sw[0]);
+}
+
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// An LDS pointer from a generic pointer into __shared__ memory: the low 32 bits
+// of the flat address are the LDS offset (no null check needed or emitted).
+#define MODA_TO_LDS(p) ((__attribute__((address_space(3))) void*)(uint32_t)(uintptr_t)(p))
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -138,7 +151,7 @@ enum Mode : int {
 
 template <int D, int NW, int MODE>
 struct Smem {
-  static constexpr int KS = D + 8;   // K tile row stride (bf16): 16 B skew per row
+  static constexpr int KS = D;       // K tile row stride (bf16): 16-byte chunks XOR-swizzled per row
   static constexpr int VS = BN + 4;  // V^T tile row stride (bf16)
   static constexpr int OS = D + 4;   // depth hand-off row stride (fp32)
   static constexpr int K_BYTES = 2 * BN * KS * 2;
@@ -432,147 +445,302 @@ moda_fwd_bf16_kernel(const Params p) {
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);                // [2][BN][KS]
   uint16_t* Vt = reinterpret_cast<uint16_t*>(smem + SM::K_BYTES);  // [2][D][VS]
 
-  const int ld_cl = tid % LPR, ld_kg = tid / LPR;
-  uint4 pk[KPT], pv[KPT];
-
-  // Unconditional loads (kept in flight by the compiler): a key past kend re-reads
-  // key kend - 1. Every such key lies beyond the causal limit of all rows of the
-  // workgroup or beyond the segment, so its score is masked and its p is 0.
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      int64_t key = (int64_t)kb * BN + ld_kg * KPT + j;
-      key = key < kend ? key : kend - 1;
-      const int64_t off = ((seg_start + key) * Hkv + hk) * (int64_t)D + 8 * ld_cl;
-      pk[j] = ldg16(K + off);
-      pv[j] = ldg16(V + off);
-    }
+  // K and V rows of this (segment, KV head) are read through buffer resources
+  // rebased at every key block, whose range ends with key kend - 1: loads past it
+  // return zeros (those keys are masked, their p is 0), so no clamp or branch is
+  // needed and all offsets stay 32-bit. K: direct to LDS (see below). V: keys
+  // v_kg * KPT + j,
+  // chunk v_cl (key groups fastest, so the transposed stores of 16 lanes fill one
+  // contiguous 128-byte stretch of a V^T row: no bank conflicts).
+  constexpr int NKG = BN / KPT;  // key groups per block
+  const int v_kg = tid % NKG, v_cl = tid / NKG;
+  const int64_t row_bytes = (int64_t)Hkv * D * 2;  // bytes from one key's row to the next
+  const char* kbase = static_cast<const char*>(p.k) + ((seg_start * Hkv + hk) * (int64_t)D) * 2;
+  const char* vbase = static_cast<const char*>(p.v) + ((seg_start * Hkv + hk) * (int64_t)D) * 2;
+  const uint32_t v_voff = (uint32_t)(v_kg * KPT * row_bytes + 16 * v_cl);
+  auto block_rsrc = [&](const char* base, int kb) {
+    const int64_t keys_left = kend - (int64_t)kb * BN;  // >= 1 for blocks that hold keys
+    int64_t nrec = keys_left > 0 ? (keys_left - 1) * row_bytes + D * 2 : 0;
+    nrec = nrec < 0x7fffffff ? nrec : 0x7fffffff;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kb * BN * row_bytes), (short)0, (int)nrec,
+                                             0x00020000);
   };
-  auto swrite = [&](int buf) {
+  // K goes from memory straight into LDS (buffer_load ... lds: lane l of a wave
+  // fills bytes [16 l, 16 l + 16) of a 1 KB run, i.e. RPI whole K rows). Chunk c of
+  // key row k is stored at chunk c ^ (k % CPR) of that row, so the MFMA operand
+  // reads of 16 lanes (16 rows, one chunk) hit 16 different bank groups.
+  constexpr int CPR = D / 8;    // 16-byte chunks per K row
+  constexpr int RPI = 64 / CPR;  // K rows per wave-wide direct load
+  const int kl_row = lane / CPR, kl_chunk = lane % CPR;
+  auto kload_lds = [&](int kb, int buf) {
+    const __amdgpu_buffer_rsrc_t rs = block_rsrc(kbase, kb);
     uint16_t* ks = Ks + buf * BN * SM::KS;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      *reinterpret_cast<uint4*>(ks + (ld_kg * KPT + j) * SM::KS + 8 * ld_cl) = pk[j];
-    uint16_t* vt = Vt + buf * D * SM::VS + ld_kg * KPT;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int word = e >> 1;
-      const bool hi = e & 1;
-      uint32_t w[KPT];
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const uint32_t x = word == 0 ? pv[j].x : word == 1 ? pv[j].y : word == 2 ? pv[j].z : pv[j].w;
-        w[j] = hi ? (x >> 16) : (x & 0xffffu);
-      }
-      uint16_t* dst = vt + (8 * ld_cl + e) * SM::VS;
-      if constexpr (KPT == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = w[0] | (w[1] << 16);
-      } else {
-#pragma unroll
-        for (int j = 0; j < KPT; j += 4)  // 8-byte stores: V^T rows are 8-byte aligned
-          *reinterpret_cast<uint2*>(dst + j) = make_uint2(w[j] | (w[j + 1] << 16), w[j + 2] | (w[j + 3] << 16));
-      }
+    for (int j = 0; j < KPT; ++j) {
+      const int row = (wave * KPT + j) * RPI + kl_row;  // key within the block
+      const uint32_t voff = (uint32_t)(row * row_bytes + 16 * (kl_chunk ^ (row % CPR)));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MODA_TO_LDS(ks + (wave * KPT + j) * RPI * SM::KS), 16, voff, 0, 0, 0);
     }
+  };
+  // wait for this wave's direct-to-LDS loads (not tracked by the compiler)
+  auto kload_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  uint4 pv[KPT];
+  auto gload_v = [&](int kb) {
+    const __amdgpu_buffer_rsrc_t rs = block_rsrc(vbase, kb);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      pv[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, v_voff, (int)(j * row_bytes), 0));
+  };
+  // Transposed store of bf16 number e of every staged V chunk (KPT keys) into V^T.
+  auto swrite_v_e = [&](int buf, int e) {
+    uint16_t* vt = Vt + buf * D * SM::VS + v_kg * KPT;
+    // keys in pairs: v_perm picks the 16-bit halves
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    const int word = e >> 1;
+    uint32_t w[KPT / 2];
+#pragma unroll
+    for (int j = 0; j < KPT; j += 2) {
+      const uint32_t x0 = word == 0 ? pv[j].x : word == 1 ? pv[j].y : word == 2 ? pv[j].z : pv[j].w;
+      const uint32_t x1 = word == 0 ? pv[j + 1].x : word == 1 ? pv[j + 1].y : word == 2 ? pv[j + 1].z : pv[j + 1].w;
+      w[j / 2] = __builtin_amdgcn_perm(x1, x0, sel);
+    }
+    uint16_t* dst = vt + (8 * v_cl + e) * SM::VS;
+    if constexpr (KPT == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = w[0];
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPT / 2; j += 2)  // 8-byte stores: V^T rows are 8-byte aligned
+        *reinterpret_cast<uint2*>(dst + 2 * j) = make_uint2(w[j], w[j + 1]);
+    }
+  };
+  auto swrite_v = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) swrite_v_e(buf, e);
   };
 
   const int64_t wave_tmin = t0 + (wave * WROWS) / GB;
   const int64_t wave_tmax = t0 + (wave * WROWS + WROWS - 1) / GB;
+  // a wave's rows see key block kb at all (monotone in kb)
+  auto active = [&](int kb) { return !p.causal || (int64_t)kb * BN <= wave_tmax; };
 
-  gload(0);
-  swrite(0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
-    if (kb + 1 < nkb) gload(kb + 1);
-    const int64_t k0 = (int64_t)kb * BN;
-    if (!p.causal || k0 <= wave_tmax) {
-      const uint16_t* ks = Ks + cur * BN * SM::KS;
-      const uint16_t* vt = Vt + cur * D * SM::VS;
-      f32x16 s[2];
+  // S^T = K Q^T for one key block: two 32-key tiles, fp32.
+  auto qk = [&](int buf, f32x16(&s)[2]) {
+    const uint16_t* ks = Ks + buf * BN * SM::KS;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+        const int row = 32 * st + r;
+        const int chunk = (2 * kc + hh) ^ (row % CPR);
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(ks + row * SM::KS + 8 * chunk));
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[st], 0, 0, 0);
       }
+  };
+
+  // ---- online softmax of one key block, in pieces ------------------------------
+  // Scores of keys past the causal limit of this lane's row or past the segment
+  // end become -inf (blocks crossing the diagonal or the segment end only).
+  auto mask_block = [&](int kb, f32x16(&s)[2]) {
+    const int64_t k0 = (int64_t)kb * BN;
+    // key k0 + off is visible iff off <= lim (32-bit offsets within the block)
+    const int64_t last = p.causal ? (tq < len - 1 ? tq : len - 1) : len - 1;
+    const int lim = (int)(last - k0 < BN ? last - k0 : BN);
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(ks + (32 * st + r) * SM::KS + 16 * kc + 8 * hh));
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[st], 0, 0, 0);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int off = 32 * st + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (off > lim) s[st][i] = NEG_INF;
       }
-      const bool need_mask = (p.causal && k0 + BN - 1 > wave_tmin) || (k0 + BN > len);
-      if (need_mask) {
-        // key k0 + off is visible iff off <= lim (32-bit offsets within the block)
-        const int64_t last = p.causal ? (tq < len - 1 ? tq : len - 1) : len - 1;
-        const int lim = (int)(last - k0 < BN ? last - k0 : BN);
+  };
+  // Row max of the block (base-2 units) and the lazy rescale: the reference max
+  // m_run only moves (and O, l are rescaled) when some row's block max exceeds it
+  // by more than 2^8; otherwise the probabilities, bounded by 2^8, accumulate
+  // against the old reference. The final o / l is the same; only the order of
+  // roundings differs. Returns the reference to subtract.
+  auto max_and_rescale = [&](const f32x16(&s)[2]) {
+    float mx = NEG_INF;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int off = 32 * st + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if (off > lim) s[st][i] = NEG_INF;
-          }
-      }
-      float mx = NEG_INF;
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
+    mx = fmaxf(mx, other_half(mx, lane)) * c2;
+    if (__any(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);  // m_run = -inf at first: alpha = 0
+      l_run *= alpha;
+      r_run *= alpha;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
-      // Lazy rescale: the reference max m_run only moves (and O, l are rescaled)
-      // when some row's block max exceeds it by more than 2^8; otherwise the
-      // probabilities, bounded by 2^8, accumulate against the old reference. The
-      // final o / l is the same; only the order of roundings differs.
-      if (__any(mx > m_run + 8.f)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);  // m_run = -inf at first: alpha = 0
-        l_run *= alpha;
-        r_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
-      // p rounded to bf16 feeds the P.V product. The output is normalised by the sum
-      // of exactly those rounded values (a bf16 dot with (1, 1)), so the weights on V
-      // sum to one and a dominant key keeps weight 1 whatever the reference max; lse
-      // uses the sum of the unrounded p.
-      uint32_t pp[2][8];
-      float lsum = 0.f, rsum = 0.f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = fast_exp2(fmaf(s[st][i], c2, -m_use));
-          const float p1 = fast_exp2(fmaf(s[st][i + 1], c2, -m_use));
-          lsum += p0 + p1;
-          pp[st][i >> 1] = pack_bf16(p0, p1);
-          rsum = dot2(pp[st][i >> 1], 0x3F803F80u, rsum);
-        }
-      l_run += lsum;
-      r_run += rsum;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int part = 0; part < 2; ++part) {
-          const bf16x8 bfrag = as_bf16x8(
-              make_uint4(pp[st][4 * part + 0], pp[st][4 * part + 1], pp[st][4 * part + 2], pp[st][4 * part + 3]));
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const uint16_t* vrow = vt + (32 * dt + r) * SM::VS + 32 * st + 16 * part + 4 * hh;
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-            const bf16x8 afrag = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, bfrag, acc[dt], 0, 0, 0);
-          }
-        }
+        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+      m_run = m_new;
     }
-    if (kb + 1 < nkb) swrite(cur ^ 1);
+    return (m_run == NEG_INF) ? 0.f : m_run;
+  };
+  // p = 2^(s c2 - m) rounded to bf16 (packed pairs) for the P.V product. The
+  // output is normalised by the sum of exactly those rounded values (a bf16 dot
+  // with (1, 1)), so the weights on V sum to one and a dominant key keeps weight 1
+  // whatever the reference max; lse uses the sum of the unrounded p.
+  auto exp_pack = [&](const f32x16(&s)[2], float m_use, uint32_t(&pp)[2][8]) {
+    float lsum = 0.f, rsum = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = fast_exp2(fmaf(s[st][i], c2, -m_use));
+        const float p1 = fast_exp2(fmaf(s[st][i + 1], c2, -m_use));
+        lsum += p0 + p1;
+        pp[st][i >> 1] = pack_bf16(p0, p1);
+        rsum = dot2(pp[st][i >> 1], 0x3F803F80u, rsum);
+      }
+    l_run += lsum;
+    r_run += rsum;
+  };
+  // O^T += V^T P^T with V^T from buffer vbuf.
+  auto pv_mma = [&](const uint32_t(&pp)[2][8], int vbuf) {
+    const uint16_t* vt = Vt + vbuf * D * SM::VS;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const bf16x8 bfrag = as_bf16x8(
+            make_uint4(pp[st][4 * part + 0], pp[st][4 * part + 1], pp[st][4 * part + 2], pp[st][4 * part + 3]));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint16_t* vrow = vt + (32 * dt + r) * SM::VS + 32 * st + 16 * part + 4 * hh;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+          const bf16x8 afrag = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, bfrag, acc[dt], 0, 0, 0);
+        }
+      }
+  };
+
+  // Pipeline: while the softmax and P.V of block kb run, the scores of block
+  // kb + 1 are already on the matrix cores (its K was staged one block earlier),
+  // V of block kb + 1 and K of block kb + 2 are in flight from memory. LDS holds
+  // two K and two V^T blocks; one barrier per block.
+  kload_lds(0, 0);
+  if (nkb > 1) kload_lds(1, 1);
+  gload_v(0);
+  swrite_v(0);
+  kload_wait();
+  __syncthreads();
+  f32x16 sA[2], sB[2];
+  if (active(0)) qk(0, sA);
+  // Blocks [0, n_full) are fully visible to every row of this wave: a
+  // straight-line step (no mask, the next block's scores always issued) lets the
+  // compiler interleave the matrix-core and vector work. The rest (diagonal,
+  // segment end, blocks beyond the wave's rows) take the generic step.
+  const int64_t full_keys = p.causal ? (wave_tmin + 1 < len ? wave_tmin + 1 : len) : len;
+  const int n_full = (int)(full_keys / BN);
+  // Operand readers for the hand-interleaved step. QK MFMA i: k-chunk i / 2, key
+  // tile i % 2. PV MFMA i: key tile i / (2 DT), half (i / DT) % 2, d tile i % DT.
+  constexpr int NQK = 2 * KC;  // score MFMAs per block
+  constexpr int NPV = 4 * DT;  // P.V MFMAs per block
+  auto kread = [&](const uint16_t* ks, int i) {
+    const int kc = i >> 1, row = 32 * (i & 1) + r;
+    const int chunk = (2 * kc + hh) ^ (row % CPR);
+    return as_bf16x8(*reinterpret_cast<const uint4*>(ks + row * SM::KS + 8 * chunk));
+  };
+  auto vread = [&](const uint16_t* vt, int i) {
+    const int st = i / (2 * DT), part = (i / DT) % 2, dt = i % DT;
+    const uint16_t* vrow = vt + (32 * dt + r) * SM::VS + 32 * st + 16 * part + 4 * hh;
+    const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+    const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+  };
+
+  // Step for a block fully visible to every row of the wave, written in issue
+  // order: each score MFMA of the next block is followed by the exponentials of
+  // pairs of this block's scores, each P.V MFMA by part of the next block's V^T
+  // staging, with operands read two MFMAs ahead. sched_barrier keeps that order,
+  // so the vector work runs while the matrix core is busy. When kb + 1 == nkb the
+  // next scores read a stale buffer and are never used.
+  auto fast_step = [&](int kb, f32x16(&scur)[2], f32x16(&snext)[2]) {
+    kload_lds(kb + 2, kb & 1);  // K(kb) was last read for block kb's scores, in the previous step
+    gload_v(kb + 1);
+    const float m_use = max_and_rescale(scur);
+    const uint16_t* ks = Ks + ((kb + 1) & 1) * BN * SM::KS;
+    const uint16_t* vt = Vt + (kb & 1) * D * SM::VS;
+    uint32_t pp[2][8];
+    float lsum = 0.f, rsum = 0.f;
+    bf16x8 a0 = kread(ks, 0), a1 = kread(ks, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      bf16x8 a2 = a1;
+      if (i + 2 < NQK) a2 = kread(ks, i + 2);
+      const int kc = i >> 1, st = i & 1;
+      if (kc == 0) {
+        f32x16 zero;
+#pragma unroll
+        for (int z = 0; z < 16; ++z) zero[z] = 0.f;
+        snext[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kc], zero, 0, 0, 0);
+      } else {
+        snext[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kc], snext[st], 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = i * 16 / NQK; q < (i + 1) * 16 / NQK; ++q) {
+        const int se = q >> 3, j = q & 7;
+        const float p0 = fast_exp2(fmaf(scur[se][2 * j], c2, -m_use));
+        const float p1 = fast_exp2(fmaf(scur[se][2 * j + 1], c2, -m_use));
+        lsum += p0 + p1;
+        pp[se][j] = pack_bf16(p0, p1);
+        rsum = dot2(pp[se][j], 0x3F803F80u, rsum);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      a0 = a1;
+      a1 = a2;
+    }
+    l_run += lsum;
+    r_run += rsum;
+    bf16x8 b0 = vread(vt, 0), b1 = vread(vt, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      bf16x8 b2 = b1;
+      if (i + 2 < NPV) b2 = vread(vt, i + 2);
+      const int st = i / (2 * DT), part = (i / DT) % 2, dt = i % DT;
+      const bf16x8 bfrag = as_bf16x8(
+          make_uint4(pp[st][4 * part + 0], pp[st][4 * part + 1], pp[st][4 * part + 2], pp[st][4 * part + 3]));
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, bfrag, acc[dt], 0, 0, 0);
+#pragma unroll
+      for (int e = i * 8 / NPV; e < (i + 1) * 8 / NPV; ++e) swrite_v_e((kb + 1) & 1, e);
+      __builtin_amdgcn_sched_barrier(0);
+      b0 = b1;
+      b1 = b2;
+    }
+    kload_wait();
     __syncthreads();
+  };
+  auto step = [&](int kb, f32x16(&scur)[2], f32x16(&snext)[2]) {
+    if (kb < n_full) {
+      fast_step(kb, scur, snext);
+      return;
+    }
+    if (kb + 2 < nkb) kload_lds(kb + 2, kb & 1);
+    gload_v(kb + 1);
+    if (kb + 1 < nkb && active(kb + 1)) qk((kb + 1) & 1, snext);
+    if (active(kb)) {
+      mask_block(kb, scur);
+      const float m_use = max_and_rescale(scur);
+      uint32_t pp[2][8];
+      exp_pack(scur, m_use, pp);
+      pv_mma(pp, kb & 1);
+    }
+    if (kb + 1 < nkb) swrite_v((kb + 1) & 1);
+    kload_wait();
+    __syncthreads();
+  };
+  for (int kb = 0; kb < nkb; kb += 2) {
+    step(kb, sA, sB);
+    if (kb + 1 < nkb) step(kb + 1, sB, sA);
   }
 
   // ---- fold in the depth state of this row ------------------------------------
