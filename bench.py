@@ -46,11 +46,23 @@ def kernel_source_sha() -> str:
 
 
 def kernel_name(w) -> str:
+    """The kernel instance the library launches for this workload (mirrors the
+    host dispatch: heads per workgroup, waves per workgroup, depth schedule)."""
     if not w.bf16:
         return f"moda_fwd_f32_kernel<{w.head_dim}>"
     G = w.group
-    gb = 8 if G % 8 == 0 else 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
-    return f"moda_fwd_bf16_kernel<{w.head_dim}, {gb}, false>"
+    gb = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+    n_hg = G // gb
+    n_pairs = len(w.lengths) * w.n_heads_kv
+    max_len = max(w.lengths)
+    waves = 1
+    for nw in (4, 2):
+        tok = 32 * nw // gb
+        if n_pairs * n_hg * ((max_len + tok - 1) // tok) >= 512:
+            waves = nw
+            break
+    mode = 0 if w.n_depth == 0 else 2
+    return f"moda_fwd_bf16_kernel<{w.head_dim}, {gb}, {waves}, {mode}, false>"
 
 
 def roofline(w, sec_per_launch: float) -> dict:
@@ -79,6 +91,99 @@ def traffic_from_profile(w, algorithmic_bytes):
     if rec.get("kernel_source_sha") != kernel_source_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ profile summaries
+
+
+def _read_csv(path):
+    import csv
+
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_kib(run_dir, counter, name_part):
+    """Mean per-dispatch value of `counter` over the dispatches whose kernel name
+    contains `name_part` (rocprofv3 --pmc csv output)."""
+    vals = [float(r["Counter_Value"]) for r in _read_csv(os.path.join(run_dir, "run_counter_collection.csv"))
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for '{name_part}' in {run_dir}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(w, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cmds) -> None:
+    """profiles/traffic_<workload>.json and a text summary from four rocprofv3 --pmc
+    runs: FETCH_SIZE and WRITE_SIZE on the workload and on the 1 GiB copy."""
+    kname = kernel_name(w).split("<")[0]
+    copy_name = "copyBuffer"
+    f_k, n_fk = _counter_kib(fetch_dir, "FETCH_SIZE", kname)
+    w_k, n_wk = _counter_kib(write_dir, "WRITE_SIZE", kname)
+    f_c, _ = _counter_kib(copy_fetch_dir, "FETCH_SIZE", copy_name)
+    w_c, _ = _counter_kib(copy_write_dir, "WRITE_SIZE", copy_name)
+    copy_bytes = float(1 << 30)
+    scale_f = copy_bytes / (f_c * 1024.0)
+    scale_w = copy_bytes / (w_c * 1024.0)
+    rd = f_k * 1024.0 * scale_f
+    wr = w_k * 1024.0 * scale_w
+    alg_rd = w.total_bytes() - w.n_tokens * w.n_heads_q * (w.head_dim * w.elem_bytes() + 4)
+    alg_wr = w.total_bytes() - alg_rd
+    rec = {"workload": w.name, "kernel": kernel_name(w), "kernel_source_sha": kernel_source_sha(),
+           "hbm_bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+           "algorithmic_read_bytes": alg_rd, "algorithmic_write_bytes": alg_wr,
+           "fetch_size_kib": f_k, "write_size_kib": w_k, "dispatches": [n_fk, n_wk],
+           "copy_fetch_size_kib": f_c, "copy_write_size_kib": w_c, "scale_fetch": scale_f, "scale_write": scale_w}
+    with open(os.path.join(ROOT, "profiles", f"traffic_{w.name}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    lines = [f"# HBM traffic of {kernel_name(w)} on {w.name} ({w.desc})", "",
+             "Commands (on the GPU host, from the repository root; R = repository root):"]
+    lines += [f"    {c}" for c in cmds]
+    lines += ["",
+              "Calibration: a plain 1 GiB device-to-device copy (bench.py --copy-calibration) reads",
+              f"FETCH_SIZE = {f_c:.1f} KiB and WRITE_SIZE = {w_c:.1f} KiB per copy; scale factors",
+              f"{scale_f:.4f} (reads) and {scale_w:.4f} (writes) turn counter KiB into bytes.", "",
+              "| per launch | counter (KiB) | scaled bytes | algorithmic bytes | ratio |", "|---|---|---|---|---|",
+              f"| read | {f_k:.1f} | {rd / 1e6:.2f} MB | {alg_rd / 1e6:.2f} MB | {rd / alg_rd:.3f} |",
+              f"| write | {w_k:.1f} | {wr / 1e6:.2f} MB | {alg_wr / 1e6:.2f} MB | {wr / alg_wr:.3f} |",
+              f"| total | | {(rd + wr) / 1e6:.2f} MB | {w.total_bytes() / 1e6:.2f} MB | {(rd + wr) / w.total_bytes():.3f} |",
+              "", f"Means over {n_fk} and {n_wk} dispatches; kernel sources sha {kernel_source_sha()}.",
+              "Algorithmic reads: q, k, v and the depth K/V rows once; writes: out and lse once."]
+    with open(os.path.join(ROOT, "profiles", f"moda_fwd_{w.name}_hbm_counters.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def write_trace_summary(w, trace_dir, log_path, cmd) -> None:
+    """Text summary of a rocprofv3 --kernel-trace --stats run of bench.py."""
+    stats = _read_csv(os.path.join(trace_dir, "run_kernel_stats.csv"))
+    bench_line = None
+    with open(log_path) as f:
+        for line in f:
+            if line.startswith("{") and '"metric"' in line:
+                bench_line = json.loads(line)
+    kname = kernel_name(w)
+    row = next((r for r in stats if kname in r["Name"]), None)
+    if row is None or bench_line is None:
+        raise SystemExit(f"kernel {kname} or the bench line missing in {trace_dir}")
+    avg_us = float(row["AverageNs"]) / 1e3
+    bench_us = bench_line["ms_per_step"] * 1e3
+    lines = [f"# rocprofv3 kernel trace: {kname} on {w.name} ({w.desc})", "",
+             "Command (on the GPU host; R = repository root):", f"    {cmd}", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in stats[:6]:
+        name = r["Name"]
+        short = name if len(name) < 90 else name[:87] + "..."
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} "
+                     f"| {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} % |")
+    lines += ["", f"bench.py (same run, HIP events over {bench_line['steps']} graph-replayed steps): "
+                  f"{bench_us:.2f} us per step; trace average {avg_us:.2f} us "
+                  f"({100 * (bench_us / avg_us - 1):+.1f} %).",
+              f"value {bench_line['value']} {bench_line['unit']}; roofline {bench_line['roofline']['bound']} "
+              f"{bench_line['roofline']['achieved']:.1f} {bench_line['roofline']['unit']} "
+              f"(frac {bench_line['roofline']['frac']:.3f}); kernel sources sha {bench_line['kernel_source_sha']}."]
+    with open(os.path.join(ROOT, "profiles", f"moda_fwd_{w.name}_kernel_trace.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
@@ -166,7 +271,22 @@ def main(argv=None) -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "LOG"),
+                    help="write the profiles/ summary of a rocprofv3 --kernel-trace --stats run (no GPU)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/traffic_<workload>.json from four rocprofv3 --pmc runs (no GPU)")
+    ap.add_argument("--profile-cmd", action="append", default=[], help="command text recorded in a summary")
     args = ap.parse_args(argv)
+
+    if args.summarize_trace or args.write_traffic:
+        from workloads import configs
+
+        w = configs.WORKLOADS[args.workload]
+        if args.summarize_trace:
+            write_trace_summary(w, args.summarize_trace[0], args.summarize_trace[1], " ".join(args.profile_cmd))
+        if args.write_traffic:
+            write_traffic(w, *args.write_traffic, args.profile_cmd)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
