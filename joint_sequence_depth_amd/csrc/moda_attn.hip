@@ -32,9 +32,6 @@ int heads_per_block(int G) {
   return 1;
 }
 
-struct Common;
-int depth_mode(const Common& c, int waves);
-
 struct Common {
   const void *q, *k, *v, *kd, *vd;
   void* out;
@@ -64,21 +61,6 @@ int check_common(const Common& c) {
     return fail(MODA_ERR_ALIGN, "k_depth and v_depth must be 16-byte aligned");
   if (c.lse && (reinterpret_cast<uintptr_t>(c.lse) & 3u)) return fail(MODA_ERR_ALIGN, "lse must be 4-byte aligned");
   return MODA_OK;
-}
-
-// Depth scheduling of the bf16 kernel when n_depth > 0: 1 = depth waves beside
-// the sequence waves, 2 = each wave runs the depth pass and the sequence loop in
-// turn (two workgroups per CU, alternating order).
-int depth_mode(const Common& c, int waves) {
-#ifdef MODA_FORCE_DEPTH_MODE
-  (void)c;
-  (void)waves;
-  return MODA_FORCE_DEPTH_MODE;
-#else
-  (void)c;
-  (void)waves;
-  return 2;
-#endif
 }
 
 moda::Params base_params(const Common& c) {
@@ -123,7 +105,6 @@ int dispatch(moda::Params& p, const Common& c, int64_t n_seg, int64_t max_len, h
     p.n_qblocks = (int32_t)nqb;
     p.n_tiles = n_pairs * p.n_hgroups * nqb;
     p.xcd_interleave = (n_pairs % 8 == 0) ? 1 : 0;
-    p.depth_mode = depth_mode(c, waves);
 #ifdef MODA_FORCE_SERIAL_ORDER
     p.serial_order = MODA_FORCE_SERIAL_ORDER;
 #else

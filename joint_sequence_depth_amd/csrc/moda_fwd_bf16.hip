@@ -8,43 +8,44 @@
 // the joint operator" is carried in base 2: logits are multiplied by
 // scale * log2(e) so that exp2 reproduces the natural exponential (deck backup
 // slide "pseudocode needs implementation-level checks"). The slide processes the
-// sequence blocks, then the depth blocks, through one state; here the two key
-// sets are folded into two partial states by different waves at the same time
-// and merged by one more application of the same update before the single
-// normalisation, which is the same operator up to the order of rounding.
+// sequence blocks, then the depth blocks, through one state; here the depth slots
+// are folded into a partial state of their own, merged with the sequence state by
+// one more application of the same update before the single normalisation: the
+// same operator up to the order of rounding.
 //
 // Work unit: one workgroup owns 32 NW expanded query rows (NW in {1, 2, 4}):
 // TOK = 32 NW / GB tokens x GB query heads of one KV head (rows ordered
 // token-major, row r -> token r / GB, head r % GB, as in the expanded-row map of
-// the deck's backup slide on grouped indexing). The workgroup has two roles:
+// the deck's backup slide on grouped indexing). Wave w owns rows [32 w, 32 w + 32)
+// and runs two parts, one after the other:
 //
-//  * NW sequence waves (MFMA-bound). Wave w owns rows [32 w, 32 w + 32). A
-//    flash-style loop over 64-key blocks of K and V^T staged in LDS (double
-//    buffered, one barrier per block). S^T = K Q^T on v_mfma_f32_32x32x16_bf16
-//    puts one query row per lane (lanes l and l + 32 hold the two halves of its
-//    64 keys), so the row max needs one cross-half exchange and the rescale by
-//    alpha is a per-lane multiply. O^T += V^T P^T takes the probabilities straight
-//    from the S^T registers: the contraction index (keys) is permuted identically
-//    in both operands.
+//  * the depth pass (HBM-bound): the depth K/V rows of the wave's tokens. LPR =
+//    D / 8 lanes hold one 16-byte slice of a slot row, so one 128-bit load per lane
+//    covers 64 / LPR slot rows (one per token). Each slot row is read ONCE and
+//    dotted with all GB query heads of the group (v_dot2_f32_bf16 on the packed
+//    operands, DPP group sums). Loads run NBUF - 1 batches of U slots ahead of the
+//    arithmetic in register buffers. Finished row states (m, acc, o) go to LDS.
 //
-//  * NW depth waves (HBM-bound), present when n_depth > 0. Depth wave w streams
-//    the depth K/V of the tokens of rows [32 w, 32 w + 32). LPR = D / 8 lanes hold
-//    one 16-byte slice of a slot row, so one 128-bit load per lane covers 64 / LPR
-//    slot rows (one per token). Each slot row is read ONCE and dotted with all GB
-//    query heads of the group (v_dot2_f32_bf16 on the packed operands). Loads run
-//    NBUF - 1 batches of U slots ahead of the arithmetic in register buffers (the
-//    depth waves have the sequence waves' register budget). Finished row states
-//    (m, acc, o) go to a dedicated LDS area. The depth waves take part in the
-//    sequence loop's barriers with an even share of their steps between any two,
-//    so both roles progress together: the workgroup's time is close to the larger
-//    of its HBM time and its MFMA time rather than their sum.
+//  * the sequence loop (MFMA-bound): a flash-style loop over 64-key blocks.
+//    S^T = K Q^T on v_mfma_f32_32x32x16_bf16 puts one query row per lane (lanes l
+//    and l + 32 hold the two halves of its 64 keys), so the row max needs one
+//    cross-half exchange and the rescale by alpha is a per-lane multiply.
+//    O^T += V^T P^T takes the probabilities straight from the S^T registers: the
+//    contraction index (keys) is permuted identically in both operands. K and V
+//    blocks go from memory straight into LDS (buffer loads with the LDS flag),
+//    NST - 1 blocks ahead, and are read back as MFMA operands, V through the
+//    gfx950 transposing LDS read.
 //
-// After the last barrier the sequence waves merge the depth state of their rows,
-// normalise once and write.
+// The two workgroups that share a CU run the two parts in opposite order, so one
+// streams depth rows from HBM while the other keeps the matrix cores busy; each
+// wave then merges its two partial states, normalises once and writes.
 //
 // Rounding: QK^T and PV accumulate in fp32; P is rounded to bf16 (RNE) before PV;
 // the output is written in fp32, or rounded to bf16 (RNE) once, after the single
 // normalisation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
 #include <type_traits>
 
 #include "moda_internal.h"
@@ -55,6 +56,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;     // keys per sequence block
 constexpr int WROWS = 32;  // query rows per wave
@@ -89,11 +91,51 @@ __device__ __forceinline__ float other_half(float x, int lane) {
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// An LDS pointer from a generic pointer into __shared__ memory: the low 32 bits
-// of the flat address are the LDS offset (no null check needed or emitted).
-#define MODA_TO_LDS(p) ((__attribute__((address_space(3))) void*)(uint32_t)(uintptr_t)(p))
+// The low 32 bits of a generic pointer into __shared__ memory are its LDS byte
+// address.
+// 8 bytes read with the gfx950 transposing LDS load (ds_read_b64_tr_b16): within
+// each group of 16 lanes, lane 4 e + q supplies 4 consecutive 16-bit values, row e
+// and columns 4 q .. 4 q + 3 of a 4 x 16 tile, and lane j receives column j.
+// The argument is a 32-bit LDS byte address; constant parts added to it in 32-bit
+// arithmetic become the instruction's offset field.
+#define MODA_TR_READ(a) __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a))
+
+// Lambdas of the kernel are always inlined: an outlined call would reload its
+// captures through memory and spill the live accumulators around the call.
+#define MODA_INL __attribute__((always_inline))
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// s_waitcnt immediate: wait until at most n vector-memory loads are outstanding
+// (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and
+// lgkmcnt at their maximum, i.e. not waited for).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource (raw, no stride): byte range [base, base + nrec); reads past it
+// return zeros without touching memory.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t nrec) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = (int)(uint32_t)b;
+  r[1] = (int)((uint32_t)(b >> 32) & 0xffffu);
+  r[2] = (int)nrec;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One wave-wide 16-byte-per-lane load from memory straight into LDS: lane l reads
+// bytes [voff, voff + 16) of the resource and writes them to LDS bytes
+// [lds + 16 l, lds + 16 l + 16) (lds is uniform; the compiler puts it in M0).
+// Written as inline assembly so that the compiler's wait insertion does not see
+// an LDS write in flight and drain all loads before every later LDS read: the
+// kernel waits for these loads itself (vector-memory loads complete in issue
+// order, so the compiler's own waits for other loads only become more
+// conservative).
+__device__ __forceinline__ void load_to_lds16(uint32_t lds, uint32_t voff, i32x4 rsrc) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
@@ -142,23 +184,24 @@ __device__ __forceinline__ Tile decode_tile(const Params& p) {
   return t;
 }
 
-// How the depth slots are scheduled against the sequence loop.
 enum Mode : int {
-  kNoDepth = 0,  // n_depth == 0: sequence waves only
-  kSplit = 1,    // NW extra depth waves run beside the NW sequence waves (one barrier schedule)
-  kSerial = 2,   // every wave runs a depth pass and the sequence loop, one after the other
+  kNoDepth = 0,  // n_depth == 0: sequence loop only
+  kSerial = 1,   // every wave runs a depth pass and the sequence loop, one after the other
 };
 
+// LDS: NST stages of one K block and NST stages of one V block, each BN rows of D
+// bf16 without padding; the 16-byte chunks of a row are XOR-swizzled (K and V with
+// different patterns, chosen for their readers). The depth hand-off reuses the
+// same bytes between the two parts.
 template <int D, int NW, int MODE>
 struct Smem {
-  static constexpr int KS = D;       // K tile row stride (bf16): 16-byte chunks XOR-swizzled per row
-  static constexpr int VS = BN + 4;  // V^T tile row stride (bf16)
-  static constexpr int OS = D + 4;   // depth hand-off row stride (fp32)
-  static constexpr int K_BYTES = 2 * BN * KS * 2;
-  static constexpr int V_BYTES = 2 * D * VS * 2;
-  static constexpr int SEQ_BYTES = K_BYTES + V_BYTES;
-  // kSplit: a dedicated hand-off area; kSerial: the hand-off reuses the K/V area
-  static constexpr int OD_OFF = MODE == kSplit ? SEQ_BYTES : 0;
+  static constexpr int NST = D == 64 ? 3 : 2;  // loads run NST - 1 blocks ahead
+  static constexpr int STAGE = BN * D * 2;     // bytes of one K or V block
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = NST * STAGE;
+  static constexpr int SEQ_BYTES = 2 * NST * STAGE;
+  static constexpr int OS = D + 4;  // depth hand-off row stride (fp32)
+  static constexpr int OD_OFF = 0;
   static constexpr int MD_OFF = OD_OFF + NW * WROWS * OS * 4;
   static constexpr int AD_OFF = MD_OFF + NW * WROWS * 4;
   static constexpr int END = AD_OFF + NW * WROWS * 4;
@@ -166,27 +209,29 @@ struct Smem {
 };
 
 template <int D, int GB, int NW, int MODE, bool OUT_F32>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW * (MODE == kSplit ? 2 : 1),
-                                                      64 * NW * (MODE == kSplit ? 2 : 1)),
-                          amdgpu_waves_per_eu(2, 2))) void
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2))) void
 moda_fwd_bf16_kernel(const Params p) {
-  constexpr int NSEQ = 64 * NW;                // threads of the sequence role
-  constexpr int TOK = WROWS * NW / GB;         // tokens per workgroup
   constexpr int TW = WROWS / GB;               // tokens per wave
+  constexpr int TOK = TW * NW;                 // tokens per workgroup
   constexpr int LPR = D / 8;                   // lanes per 16-byte-sliced row of D
   constexpr int NGRP = 64 / LPR;               // tokens per wave-wide depth load
-  constexpr int NTG = (TW + NGRP - 1) / NGRP;  // depth token groups per depth wave
-  constexpr int KPT = BN * LPR / NSEQ;         // keys per thread per K/V block load
+  constexpr int NTG = (TW + NGRP - 1) / NGRP;  // depth token groups per wave
+  constexpr int CPR = D / 8;                   // 16-byte chunks per K/V row
+  constexpr int RPI = 64 / CPR;                // K/V rows per wave-wide direct-to-LDS load (1 KB)
+  constexpr int KPT = BN / (NW * RPI);         // such loads per wave per K (or V) block
   constexpr int KC = D / 16;                   // k-chunks of Q K^T
   constexpr int DT = D / 32;                   // 32-wide d tiles of O^T
   constexpr int U = GB == 1 ? 8 : (GB == 2 ? 4 : 2);  // depth slots per load batch
   constexpr bool QPRE = GB <= 2;               // prefetch a token's q rows with its first batch
   constexpr int QBUF = QPRE ? GB : 1;
-  // depth load buffers (steps in flight + 1); a serial pass keeps the O^T
-  // accumulators live, so it gets fewer
-  constexpr int NBUF = MODE == kSplit ? (GB == 1 ? 3 : (GB == 2 ? 4 : 6)) : (GB == 1 ? 2 : (GB == 2 ? 3 : 4));
+  // depth load buffers (batches in flight + 1); when the depth pass follows the
+  // sequence loop the O^T accumulators are live, so the count stays small
+  constexpr int NBUF = GB == 1 ? 2 : (GB == 2 ? 3 : 4);
   using SM = Smem<D, NW, MODE>;
-  static_assert(KPT >= 2 && KPT % 2 == 0 && BN * LPR == KPT * NSEQ, "tile shape");
+  constexpr int NST = SM::NST;
+  constexpr int P = NST - 1;                 // load groups in flight ahead of the current block
+  constexpr int WAIT_N = (P - 1) * 2 * KPT;  // loads allowed outstanding at the end of a block
+  static_assert(KPT >= 1 && KPT * NW * RPI == BN && RPI % 4 == 0, "tile shape");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[SM::BYTES];
 
@@ -218,7 +263,7 @@ moda_fwd_bf16_kernel(const Params p) {
   const float c2 = p.scale_log2;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(p.q);
   const int64_t kend = p.causal ? (len < t0 + TOK ? len : t0 + TOK) : len;
-  const int nkb = (int)((kend + BN - 1) / BN);  // sequence key blocks; nkb + 1 barriers
+  const int nkb = (int)((kend + BN - 1) / BN);  // sequence key blocks
 
   float* od = reinterpret_cast<float*>(smem + SM::OD_OFF);  // [NW*WROWS][OS]
   float* md = reinterpret_cast<float*>(smem + SM::MD_OFF);  // [NW*WROWS]
@@ -226,158 +271,130 @@ moda_fwd_bf16_kernel(const Params p) {
 
   // ================================================================ depth pass
   // Folds the depth slots of the tokens of rows [32 dw, 32 dw + 32) into partial
-  // row states (m, acc, o) in LDS. With kSplit it also takes part in the sequence
-  // loop's nkb + 1 barriers, one even share of its steps between any two.
-  auto depth_pass = [&](const int dw) {
-    {
-      const int n_depth = p.n_depth;
-      const uint16_t* __restrict__ KD = static_cast<const uint16_t*>(p.kd);
-      const uint16_t* __restrict__ VD = static_cast<const uint16_t*>(p.vd);
-      const int grp = lane / LPR, cl = lane % LPR;
-      const int64_t slot_stride = (int64_t)Hkv * D;
-      const int nch = (n_depth + U - 1) / U;  // slot batches per token
-      const int n_it = NTG * nch;             // (token group, slot batch) steps
+  // row states (m, acc, o) in LDS.
+  auto depth_pass = [&](const int dw) MODA_INL {
+    const int n_depth = p.n_depth;
+    const uint16_t* __restrict__ KD = static_cast<const uint16_t*>(p.kd);
+    const uint16_t* __restrict__ VD = static_cast<const uint16_t*>(p.vd);
+    const int grp = lane / LPR, cl = lane % LPR;
+    const int64_t slot_stride = (int64_t)Hkv * D;
+    const int nch = (n_depth + U - 1) / U;  // slot batches per token
+    const int n_it = NTG * nch;             // (token group, slot batch) steps
 
-      // Loads for step `it`: U slot rows of K and V (and the token's q rows at its
-      // first batch) into one of two register buffers. The loads are unconditional
-      // so the compiler keeps them in flight across the arithmetic: a slot past
-      // n_depth re-reads the last slot and a token past the segment re-reads its
-      // last token (cache hits); such logits are masked and such rows discarded.
-      auto issue = [&](int it, uint4(&kw)[U], uint4(&vw)[U], uint4(&qw)[QBUF]) {
-        it = it < n_it ? it : n_it - 1;  // the steps past the end re-load the last one (never processed)
-        const int tg = it / nch, ch = it - tg * nch;
-        const int tl = tg * NGRP + grp;
+    // Loads for step `it`: U slot rows of K and V (and the token's q rows at its
+    // first batch) into one of the register buffers. The loads are unconditional
+    // so the compiler keeps them in flight across the arithmetic: a slot past
+    // n_depth re-reads the last slot and a token past the segment re-reads its
+    // last token (cache hits); such logits are masked and such rows discarded.
+    auto issue = [&](int it, uint4(&kw)[U], uint4(&vw)[U], uint4(&qw)[QBUF]) MODA_INL {
+      it = it < n_it ? it : n_it - 1;  // the steps past the end re-load the last one (never processed)
+      const int tg = it / nch, ch = it - tg * nch;
+      const int tl = tg * NGRP + grp;
+      int64_t t = t0 + (int64_t)dw * TW + (tl < TW ? tl : TW - 1);
+      t = t < len ? t : len - 1;
+      const int64_t n = seg_start + t;
+      const int64_t base = (n * p.S_cap * Hkv + hk) * (int64_t)D + 8 * cl;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int slot = ch * U + u < n_depth ? ch * U + u : n_depth - 1;
+        kw[u] = ldg16(KD + base + slot * slot_stride);
+        vw[u] = ldg16(VD + base + slot * slot_stride);
+      }
+      if constexpr (QPRE) {  // every step: a fixed load count keeps the wait counts exact
+#pragma unroll
+        for (int g = 0; g < QBUF; ++g) qw[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * cl));
+      }
+    };
+
+    uint4 qc[GB];  // q rows of the current token, packed bf16
+    float m[GB], a[GB], o[GB][8];
+    auto process = [&](int it, const uint4(&kw)[U], const uint4(&vw)[U], const uint4(&qw)[QBUF]) MODA_INL {
+      const int tg = it / nch, ch = it - tg * nch;
+      const int tl = tg * NGRP + grp;
+      if (ch == 0) {
         int64_t t = t0 + (int64_t)dw * TW + (tl < TW ? tl : TW - 1);
         t = t < len ? t : len - 1;
         const int64_t n = seg_start + t;
-        const int64_t base = (n * p.S_cap * Hkv + hk) * (int64_t)D + 8 * cl;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int slot = ch * U + u < n_depth ? ch * U + u : n_depth - 1;
-          kw[u] = ldg16(KD + base + slot * slot_stride);
-          vw[u] = ldg16(VD + base + slot * slot_stride);
-        }
-        if constexpr (QPRE) {  // every step: a fixed load count keeps the wait counts exact
-#pragma unroll
-          for (int g = 0; g < QBUF; ++g) qw[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * cl));
-        }
-      };
-
-      uint4 qc[GB];  // q rows of the current token, packed bf16
-      float m[GB], a[GB], o[GB][8];
-      auto process = [&](int it, const uint4(&kw)[U], const uint4(&vw)[U], const uint4(&qw)[QBUF]) {
-        const int tg = it / nch, ch = it - tg * nch;
-        const int tl = tg * NGRP + grp;
-        if (ch == 0) {
-          int64_t t = t0 + (int64_t)dw * TW + (tl < TW ? tl : TW - 1);
-          t = t < len ? t : len - 1;
-          const int64_t n = seg_start + t;
-#pragma unroll
-          for (int g = 0; g < GB; ++g) {
-            if constexpr (QPRE) {
-              qc[g] = qw[g < QBUF ? g : 0];
-            } else {
-              qc[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * cl));
-            }
-            m[g] = NEG_INF;
-            a[g] = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
-          }
-        }
 #pragma unroll
         for (int g = 0; g < GB; ++g) {
-          float b[U];
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            float s = dot2(qc[g].x, kw[u].x, 0.f);
-            s = dot2(qc[g].y, kw[u].y, s);
-            s = dot2(qc[g].z, kw[u].z, s);
-            s = dot2(qc[g].w, kw[u].w, s);
-            s = group_sum<LPR>(s);
-            b[u] = (ch * U + u < n_depth) ? s * c2 : NEG_INF;
+          if constexpr (QPRE) {
+            qc[g] = qw[g < QBUF ? g : 0];
+          } else {
+            qc[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * cl));
           }
-          float mx = b[0];
+          m[g] = NEG_INF;
+          a[g] = 0.f;
 #pragma unroll
-          for (int u = 1; u < U; ++u) mx = fmaxf(mx, b[u]);
-          const float m_new = fmaxf(m[g], mx);
-          const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-          const float alpha = fast_exp2(m[g] - m_use);
-          a[g] *= alpha;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) o[g][j] *= alpha;
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const float pu = fast_exp2(b[u] - m_use);
-            a[g] += pu;
-            o[g][0] = fmaf(pu, lo_bf16(vw[u].x), o[g][0]);
-            o[g][1] = fmaf(pu, hi_bf16(vw[u].x), o[g][1]);
-            o[g][2] = fmaf(pu, lo_bf16(vw[u].y), o[g][2]);
-            o[g][3] = fmaf(pu, hi_bf16(vw[u].y), o[g][3]);
-            o[g][4] = fmaf(pu, lo_bf16(vw[u].z), o[g][4]);
-            o[g][5] = fmaf(pu, hi_bf16(vw[u].z), o[g][5]);
-            o[g][6] = fmaf(pu, lo_bf16(vw[u].w), o[g][6]);
-            o[g][7] = fmaf(pu, hi_bf16(vw[u].w), o[g][7]);
-          }
-          m[g] = m_new;
+          for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
         }
-        if (ch == nch - 1 && tl < TW) {
+      }
 #pragma unroll
-          for (int g = 0; g < GB; ++g) {
-            const int row = dw * WROWS + tl * GB + g;
-            float4* dst = reinterpret_cast<float4*>(od + row * SM::OS + 8 * cl);
-            dst[0] = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
-            dst[1] = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);
-            if (cl == 0) {
-              md[row] = m[g];
-              ad[row] = a[g];
-            }
-          }
+      for (int g = 0; g < GB; ++g) {
+        float b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float s = dot2(qc[g].x, kw[u].x, 0.f);
+          s = dot2(qc[g].y, kw[u].y, s);
+          s = dot2(qc[g].z, kw[u].z, s);
+          s = dot2(qc[g].w, kw[u].w, s);
+          s = group_sum<LPR>(s);
+          b[u] = (ch * U + u < n_depth) ? s * c2 : NEG_INF;
         }
-      };
-
-      // Barrier b closes the b-th of nkb + 1 equal shares of the n_it steps.
-      const int nbar = nkb + 1;
-      int bars = 0;
-      auto sync_until = [&](int it) {
-        if constexpr (MODE == kSplit) {
-          while (bars < nbar && (int)(((int64_t)n_it * (bars + 1)) / nbar) <= it) {
-            __syncthreads();
-            ++bars;
-          }
+        float mx = b[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) mx = fmaxf(mx, b[u]);
+        const float m_new = fmaxf(m[g], mx);
+        const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+        const float alpha = fast_exp2(m[g] - m_use);
+        a[g] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[g][j] *= alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float pu = fast_exp2(b[u] - m_use);
+          a[g] += pu;
+          o[g][0] = fmaf(pu, lo_bf16(vw[u].x), o[g][0]);
+          o[g][1] = fmaf(pu, hi_bf16(vw[u].x), o[g][1]);
+          o[g][2] = fmaf(pu, lo_bf16(vw[u].y), o[g][2]);
+          o[g][3] = fmaf(pu, hi_bf16(vw[u].y), o[g][3]);
+          o[g][4] = fmaf(pu, lo_bf16(vw[u].z), o[g][4]);
+          o[g][5] = fmaf(pu, hi_bf16(vw[u].z), o[g][5]);
+          o[g][6] = fmaf(pu, lo_bf16(vw[u].w), o[g][6]);
+          o[g][7] = fmaf(pu, hi_bf16(vw[u].w), o[g][7]);
         }
-      };
-
-      // NBUF register buffers, loads NBUF - 1 steps ahead. Every step issues the
-      // same number of loads, so the compiler waits exactly for the buffer it reads
-      // and leaves the others in flight.
-      uint4 kb[NBUF][U], vb[NBUF][U], qb[NBUF][QBUF];
+        m[g] = m_new;
+      }
+      if (ch == nch - 1 && tl < TW) {
 #pragma unroll
-      for (int j = 0; j < NBUF - 1; ++j) issue(j, kb[j], vb[j], qb[j]);
-      for (int it = 0; it < n_it; it += NBUF) {
-#pragma unroll
-        for (int j = 0; j < NBUF; ++j) {
-          issue(it + j + NBUF - 1, kb[(j + NBUF - 1) % NBUF], vb[(j + NBUF - 1) % NBUF], qb[(j + NBUF - 1) % NBUF]);
-          if (it + j < n_it) {
-            sync_until(it + j);
-            process(it + j, kb[j], vb[j], qb[j]);
+        for (int g = 0; g < GB; ++g) {
+          const int row = dw * WROWS + tl * GB + g;
+          float4* dst = reinterpret_cast<float4*>(od + row * SM::OS + 8 * cl);
+          dst[0] = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
+          dst[1] = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);
+          if (cl == 0) {
+            md[row] = m[g];
+            ad[row] = a[g];
           }
         }
       }
-      sync_until(n_it);  // kSplit: the remaining barriers; the last one publishes every row state
+    };
+
+    // NBUF register buffers, loads NBUF - 1 steps ahead. Every step issues the
+    // same number of loads, so the compiler waits exactly for the buffer it reads
+    // and leaves the others in flight.
+    uint4 kb[NBUF][U], vb[NBUF][U], qb[NBUF][QBUF];
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j) issue(j, kb[j], vb[j], qb[j]);
+    for (int it = 0; it < n_it; it += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        issue(it + j + NBUF - 1, kb[(j + NBUF - 1) % NBUF], vb[(j + NBUF - 1) % NBUF], qb[(j + NBUF - 1) % NBUF]);
+        if (it + j < n_it) process(it + j, kb[j], vb[j], qb[j]);
+      }
     }
   };
 
-  if constexpr (MODE == kSplit) {
-    if (wave >= NW) {
-      depth_pass(wave - NW);
-      return;
-    }
-  }
-
-  // ============================================================ sequence role
-  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(p.k);
-  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(p.v);
+  // ============================================================ sequence state
   const int r = lane & 31;   // row within the wave (column of the 32x32 tiles)
   const int hh = lane >> 5;  // which half of each 16-wide contraction chunk
   const int rowb = wave * WROWS + r;
@@ -395,7 +412,7 @@ moda_fwd_bf16_kernel(const Params p) {
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
   // Folds this row's depth state (published in LDS) into (m_run, l_run, acc).
-  auto depth_fold = [&]() {
+  auto depth_fold = [&]() MODA_INL {
     const float m_d = md[rowb];
     const float m_new = fmaxf(m_run, m_d);
     const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
@@ -417,10 +434,10 @@ moda_fwd_bf16_kernel(const Params p) {
     m_run = m_new;
   };
 
-  // kSerial: the two workgroups that share a CU run the depth pass first and
-  // last in turn (the first round of workgroups on an XCD's 32 CUs starts with
-  // it, the second with the sequence loop), so one streams from HBM while the
-  // other keeps the matrix cores busy.
+  // The two workgroups that share a CU run the depth pass first and last in turn
+  // (the first round of workgroups on an XCD's 32 CUs starts with it, the second
+  // with the sequence loop), so one streams from HBM while the other keeps the
+  // matrix cores busy.
   const bool depth_first =
       MODE == kSerial && (p.serial_order == 0 ? (((blockIdx.x >> 3) >> 5) & 1) == 0 : p.serial_order == 1);
   if (MODE == kSerial && depth_first) {
@@ -442,109 +459,124 @@ moda_fwd_bf16_kernel(const Params p) {
     }
   }
 
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);                // [2][BN][KS]
-  uint16_t* Vt = reinterpret_cast<uint16_t*>(smem + SM::K_BYTES);  // [2][D][VS]
-
+  // ---- K/V staging ---------------------------------------------------------------
   // K and V rows of this (segment, KV head) are read through buffer resources
-  // rebased at every key block, whose range ends with key kend - 1: loads past it
-  // return zeros (those keys are masked, their p is 0), so no clamp or branch is
-  // needed and all offsets stay 32-bit. K: direct to LDS (see below). V: keys
-  // v_kg * KPT + j,
-  // chunk v_cl (key groups fastest, so the transposed stores of 16 lanes fill one
-  // contiguous 128-byte stretch of a V^T row: no bank conflicts).
-  constexpr int NKG = BN / KPT;  // key groups per block
-  const int v_kg = tid % NKG, v_cl = tid / NKG;
+  // rebased at every key block, whose range ends with key kend - 1. Each wave-wide
+  // load moves RPI whole rows (1 KB) into LDS: lane l fills bytes [16 l, 16 l + 16)
+  // of the run, i.e. chunk position l % CPR of row l / CPR, with the chunk of the
+  // row that the swizzle puts there. Rows past the last key load the last key's
+  // row, so the masked tail of the last block holds finite values (their p is
+  // exactly 0). Blocks past the end, issued by the fixed-count pipeline, have an
+  // empty range: those loads return zeros and touch no memory; their stages are
+  // never read.
+  //   K: chunk c of row k sits at position c ^ (k % CPR): the score operand reads
+  //      (16 lanes = 16 rows, one chunk) hit 16 different bank groups.
+  //   V: chunk c of row k sits at position c ^ sv(k), sv(k) = 4 (k % 4) (D = 128)
+  //      or 4 ((k / 2) % 2) (D = 64): the transposing reads of 32 lanes (4 rows x 4
+  //      chunks) cover every bank once.
   const int64_t row_bytes = (int64_t)Hkv * D * 2;  // bytes from one key's row to the next
   const char* kbase = static_cast<const char*>(p.k) + ((seg_start * Hkv + hk) * (int64_t)D) * 2;
   const char* vbase = static_cast<const char*>(p.v) + ((seg_start * Hkv + hk) * (int64_t)D) * 2;
-  const uint32_t v_voff = (uint32_t)(v_kg * KPT * row_bytes + 16 * v_cl);
-  auto block_rsrc = [&](const char* base, int kb) {
-    const int64_t keys_left = kend - (int64_t)kb * BN;  // >= 1 for blocks that hold keys
+  auto sv = [](int k) MODA_INL { return D == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); };
+  const int ld_row = lane / CPR, ld_pos = lane % CPR;  // this lane's place in a 1 KB run
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // the wave index as a scalar
+  const uint32_t row_bytes32 = (uint32_t)Hkv * (uint32_t)(D * 2);  // scalar: a full block's offsets fit 32 bits
+  auto stage_of = [](int kb) MODA_INL { return kb - (kb / NST) * NST; };
+  // Per-lane parts of the load offsets of a full block (loop-invariant): the LDS
+  // row of load j is (wave KPT + j) RPI + ld_row, whose uniform part is added per
+  // load (no multiply in the loop). The K swizzle at D = 128 also depends on that row's bits 2-3,
+  // a uniform XOR of bits 6-7 of the chunk offset; row_bytes is then a multiple of
+  // 256, so the XOR never meets a carry from the row part.
+  const uint32_t k_lane = (uint32_t)(ld_row * row_bytes + 16 * (ld_pos ^ (ld_row % CPR)));
+  const uint32_t v_lane = (uint32_t)(ld_row * row_bytes + 16 * (ld_pos ^ sv(ld_row)));
+  // one block of K (or V) into `stage`: KPT wave-wide loads per wave
+  auto load_block = [&](const char* base, int kb, unsigned char* stage, bool is_v) MODA_INL {
+    const int64_t keys_left = kend - (int64_t)kb * BN;
     int64_t nrec = keys_left > 0 ? (keys_left - 1) * row_bytes + D * 2 : 0;
     nrec = nrec < 0x7fffffff ? nrec : 0x7fffffff;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kb * BN * row_bytes), (short)0, (int)nrec,
-                                             0x00020000);
-  };
-  // K goes from memory straight into LDS (buffer_load ... lds: lane l of a wave
-  // fills bytes [16 l, 16 l + 16) of a 1 KB run, i.e. RPI whole K rows). Chunk c of
-  // key row k is stored at chunk c ^ (k % CPR) of that row, so the MFMA operand
-  // reads of 16 lanes (16 rows, one chunk) hit 16 different bank groups.
-  constexpr int CPR = D / 8;    // 16-byte chunks per K row
-  constexpr int RPI = 64 / CPR;  // K rows per wave-wide direct load
-  const int kl_row = lane / CPR, kl_chunk = lane % CPR;
-  auto kload_lds = [&](int kb, int buf) {
-    const __amdgpu_buffer_rsrc_t rs = block_rsrc(kbase, kb);
-    uint16_t* ks = Ks + buf * BN * SM::KS;
+    const i32x4 rs = make_rsrc(base + (int64_t)kb * BN * row_bytes, (uint32_t)nrec);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)stage + (uint32_t)(wave_u * KPT) * 1024u;
+    if (keys_left >= BN) {  // full block: every row in range, no clamp
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int row = (wave * KPT + j) * RPI + kl_row;  // key within the block
-      const uint32_t voff = (uint32_t)(row * row_bytes + 16 * (kl_chunk ^ (row % CPR)));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, MODA_TO_LDS(ks + (wave * KPT + j) * RPI * SM::KS), 16, voff, 0, 0, 0);
+      for (int j = 0; j < KPT; ++j) {
+        const uint32_t rg = (uint32_t)(wave_u * KPT + j);  // uniform: which RPI-row run
+        uint32_t voff = is_v ? v_lane : k_lane;
+        if (D == 128 && !is_v) voff ^= 64u * (rg & 3u);
+        load_to_lds16(lds0 + 1024u * j, voff + rg * (uint32_t)RPI * row_bytes32, rs);
+      }
+    } else {  // the segment's last block (or a block past it): clamp rows to the last key
+      const int last = keys_left > 0 ? (int)keys_left - 1 : 0;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int row = (wave_u * KPT + j) * RPI + ld_row;  // key within the block = LDS row
+        const int src = row < last ? row : last;            // key whose row is loaded there
+        const int chunk = ld_pos ^ (is_v ? sv(row) : (row % CPR));
+        load_to_lds16(lds0 + 1024u * j, (uint32_t)(src * row_bytes + 16 * chunk), rs);
+      }
     }
   };
-  // wait for this wave's direct-to-LDS loads (not tracked by the compiler)
-  auto kload_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
-  uint4 pv[KPT];
-  auto gload_v = [&](int kb) {
-    const __amdgpu_buffer_rsrc_t rs = block_rsrc(vbase, kb);
-#pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      pv[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, v_voff, (int)(j * row_bytes), 0));
+  unsigned char* const kst = smem + SM::K_OFF;
+  unsigned char* const vst = smem + SM::V_OFF;
+  // Load group j: K of block j + 1 and V of block j, both read in the step of
+  // block j (the scores run one block ahead). Group j + P is issued at the top of
+  // step j, into the stages of K(j) and V(j - 1), which step j - 1 released.
+  auto issue_group = [&](int j) MODA_INL {
+    load_block(kbase, j + 1, kst + stage_of(j + 1) * SM::STAGE, false);
+    load_block(vbase, j, vst + stage_of(j) * SM::STAGE, true);
   };
-  // Transposed store of bf16 number e of every staged V chunk (KPT keys) into V^T.
-  auto swrite_v_e = [&](int buf, int e) {
-    uint16_t* vt = Vt + buf * D * SM::VS + v_kg * KPT;
-    // keys in pairs: v_perm picks the 16-bit halves
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    const int word = e >> 1;
-    uint32_t w[KPT / 2];
-#pragma unroll
-    for (int j = 0; j < KPT; j += 2) {
-      const uint32_t x0 = word == 0 ? pv[j].x : word == 1 ? pv[j].y : word == 2 ? pv[j].z : pv[j].w;
-      const uint32_t x1 = word == 0 ? pv[j + 1].x : word == 1 ? pv[j + 1].y : word == 2 ? pv[j + 1].z : pv[j + 1].w;
-      w[j / 2] = __builtin_amdgcn_perm(x1, x0, sel);
-    }
-    uint16_t* dst = vt + (8 * v_cl + e) * SM::VS;
-    if constexpr (KPT == 2) {
-      *reinterpret_cast<uint32_t*>(dst) = w[0];
-    } else {
-#pragma unroll
-      for (int j = 0; j < KPT / 2; j += 2)  // 8-byte stores: V^T rows are 8-byte aligned
-        *reinterpret_cast<uint2*>(dst + 2 * j) = make_uint2(w[j], w[j + 1]);
-    }
-  };
-  auto swrite_v = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) swrite_v_e(buf, e);
+  // the end of a block: load group kb + 1 has landed (only later groups may still
+  // be in flight), and every wave is done with block kb's stages
+  auto block_end = [&]() MODA_INL {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAIT_N));
+    __syncthreads();
   };
 
   const int64_t wave_tmin = t0 + (wave * WROWS) / GB;
   const int64_t wave_tmax = t0 + (wave * WROWS + WROWS - 1) / GB;
   // a wave's rows see key block kb at all (monotone in kb)
-  auto active = [&](int kb) { return !p.causal || (int64_t)kb * BN <= wave_tmax; };
+  auto active = [&](int kb) MODA_INL { return !p.causal || (int64_t)kb * BN <= wave_tmax; };
+
+  // Score operand reads: QK MFMA i uses k-chunk i / 2 of key tile i % 2.
+  auto kread = [&](const unsigned char* ks, int i) MODA_INL {
+    const int kc = i >> 1, row = 32 * (i & 1) + r;
+    const int chunk = (2 * kc + hh) ^ (row % CPR);
+    return as_bf16x8(*reinterpret_cast<const uint4*>(ks + row * (D * 2) + 16 * chunk));
+  };
+  // V^T operand reads: PV MFMA i = (key tile st, half part, d tile dt). Lane
+  // 16 g + 4 e + q reads keys key0 + e and key0 + 8 + e, key0 = 32 st + 16 part +
+  // 4 (g / 2), columns 32 dt + 16 (g % 2) + 4 q .. + 3: after the transpose, lane
+  // (r, hh) holds column 32 dt + r at keys 32 st + 16 part + 4 hh + {0..3, 8..11},
+  // the key order of the P^T registers.
+  const int tr_g = lane >> 4, tr_e = (lane >> 2) & 3, tr_q = lane & 3;
+  const int tr_row = 4 * (tr_g >> 1) + tr_e;       // row within a 16-key half; rows + 8 share sv
+  const int tr_lo = 2 * (tr_g & 1) + (tr_q >> 1);  // chunk within the 4 of a d tile
+  uint32_t tr_off[DT];                             // this lane's byte offset in a stage, per d tile
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    tr_off[dt] = (uint32_t)(tr_row * (D * 2) + 8 * (tr_q & 1) + 16 * (((4 * dt) ^ sv(tr_row)) + tr_lo));
+  auto vread = [&](const unsigned char* vs, int i) MODA_INL {
+    const int st = i / (2 * DT), part = (i / DT) % 2, dt = i % DT;
+    const uint32_t a = (uint32_t)(uintptr_t)vs + tr_off[dt];
+    const i16x4 x0 = MODA_TR_READ(a + (32 * st + 16 * part) * (D * 2));
+    const i16x4 x1 = MODA_TR_READ(a + (32 * st + 16 * part + 8) * (D * 2));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
   // S^T = K Q^T for one key block: two 32-key tiles, fp32.
-  auto qk = [&](int buf, f32x16(&s)[2]) {
-    const uint16_t* ks = Ks + buf * BN * SM::KS;
+  auto qk = [&](const unsigned char* ks, f32x16(&s)[2]) MODA_INL {
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int row = 32 * st + r;
-        const int chunk = (2 * kc + hh) ^ (row % CPR);
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(ks + row * SM::KS + 8 * chunk));
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[st], 0, 0, 0);
-      }
+    for (int i = 0; i < 2 * KC; ++i)
+      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(ks, i), qf[i >> 1], s[i & 1], 0, 0, 0);
   };
 
   // ---- online softmax of one key block, in pieces ------------------------------
   // Scores of keys past the causal limit of this lane's row or past the segment
   // end become -inf (blocks crossing the diagonal or the segment end only).
-  auto mask_block = [&](int kb, f32x16(&s)[2]) {
+  auto mask_block = [&](int kb, f32x16(&s)[2]) MODA_INL {
     const int64_t k0 = (int64_t)kb * BN;
     // key k0 + off is visible iff off <= lim (32-bit offsets within the block)
     const int64_t last = p.causal ? (tq < len - 1 ? tq : len - 1) : len - 1;
@@ -562,7 +594,7 @@ moda_fwd_bf16_kernel(const Params p) {
   // by more than 2^8; otherwise the probabilities, bounded by 2^8, accumulate
   // against the old reference. The final o / l is the same; only the order of
   // roundings differs. Returns the reference to subtract.
-  auto max_and_rescale = [&](const f32x16(&s)[2]) {
+  auto max_and_rescale = [&](const f32x16(&s)[2]) MODA_INL {
     float mx = NEG_INF;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -582,92 +614,56 @@ moda_fwd_bf16_kernel(const Params p) {
     }
     return (m_run == NEG_INF) ? 0.f : m_run;
   };
-  // p = 2^(s c2 - m) rounded to bf16 (packed pairs) for the P.V product. The
-  // output is normalised by the sum of exactly those rounded values (a bf16 dot
-  // with (1, 1)), so the weights on V sum to one and a dominant key keeps weight 1
-  // whatever the reference max; lse uses the sum of the unrounded p.
-  auto exp_pack = [&](const f32x16(&s)[2], float m_use, uint32_t(&pp)[2][8]) {
-    float lsum = 0.f, rsum = 0.f;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float p0 = fast_exp2(fmaf(s[st][i], c2, -m_use));
-        const float p1 = fast_exp2(fmaf(s[st][i + 1], c2, -m_use));
-        lsum += p0 + p1;
-        pp[st][i >> 1] = pack_bf16(p0, p1);
-        rsum = dot2(pp[st][i >> 1], 0x3F803F80u, rsum);
-      }
-    l_run += lsum;
-    r_run += rsum;
+  // p = 2^(s c2 - m) rounded to bf16 (packed pairs) for the P.V product, pair q of
+  // the 16 per lane. The output is normalised by the sum of exactly those rounded
+  // values (a bf16 dot with (1, 1)), so the weights on V sum to one and a dominant
+  // key keeps weight 1 whatever the reference max; lse uses the sum of the
+  // unrounded p.
+  auto exp_pair = [&](const f32x16(&s)[2], float m_use, int q, uint32_t(&pp)[2][8], float& lsum, float& rsum) MODA_INL {
+    const int se = q >> 3, j = q & 7;
+    const float p0 = fast_exp2(fmaf(s[se][2 * j], c2, -m_use));
+    const float p1 = fast_exp2(fmaf(s[se][2 * j + 1], c2, -m_use));
+    lsum += p0 + p1;
+    pp[se][j] = pack_bf16(p0, p1);
+    rsum = dot2(pp[se][j], 0x3F803F80u, rsum);
   };
-  // O^T += V^T P^T with V^T from buffer vbuf.
-  auto pv_mma = [&](const uint32_t(&pp)[2][8], int vbuf) {
-    const uint16_t* vt = Vt + vbuf * D * SM::VS;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const bf16x8 bfrag = as_bf16x8(
-            make_uint4(pp[st][4 * part + 0], pp[st][4 * part + 1], pp[st][4 * part + 2], pp[st][4 * part + 3]));
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint16_t* vrow = vt + (32 * dt + r) * SM::VS + 32 * st + 16 * part + 4 * hh;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          const bf16x8 afrag = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, bfrag, acc[dt], 0, 0, 0);
-        }
-      }
+  // B operand of PV MFMA i: the packed probabilities of key tile st, half part.
+  auto pfrag = [](const uint32_t(&pp)[2][8], int i) MODA_INL {
+    const int st = i / (2 * DT), part = (i / DT) % 2;
+    return as_bf16x8(
+        make_uint4(pp[st][4 * part + 0], pp[st][4 * part + 1], pp[st][4 * part + 2], pp[st][4 * part + 3]));
   };
+  constexpr int NQK = 2 * KC;  // score MFMAs per block
+  constexpr int NPV = 4 * DT;  // P.V MFMAs per block
 
-  // Pipeline: while the softmax and P.V of block kb run, the scores of block
-  // kb + 1 are already on the matrix cores (its K was staged one block earlier),
-  // V of block kb + 1 and K of block kb + 2 are in flight from memory. LDS holds
-  // two K and two V^T blocks; one barrier per block.
-  kload_lds(0, 0);
-  if (nkb > 1) kload_lds(1, 1);
-  gload_v(0);
-  swrite_v(0);
-  kload_wait();
-  __syncthreads();
+  // Prologue: K(0) and load groups 0 .. P - 1, then the scores of block 0. The
+  // barrier after them keeps step 0 from reloading K(0)'s stage under a wave that
+  // is still reading it.
+  load_block(kbase, 0, kst, false);
+#pragma unroll
+  for (int j = 0; j < P; ++j) issue_group(j);
+  block_end();
   f32x16 sA[2], sB[2];
-  if (active(0)) qk(0, sA);
+  qk(kst, sA);  // every wave sees block 0 (unconditional, so the q loads are waited for here only)
+  __syncthreads();
+
   // Blocks [0, n_full) are fully visible to every row of this wave: a
   // straight-line step (no mask, the next block's scores always issued) lets the
   // compiler interleave the matrix-core and vector work. The rest (diagonal,
   // segment end, blocks beyond the wave's rows) take the generic step.
   const int64_t full_keys = p.causal ? (wave_tmin + 1 < len ? wave_tmin + 1 : len) : len;
   const int n_full = (int)(full_keys / BN);
-  // Operand readers for the hand-interleaved step. QK MFMA i: k-chunk i / 2, key
-  // tile i % 2. PV MFMA i: key tile i / (2 DT), half (i / DT) % 2, d tile i % DT.
-  constexpr int NQK = 2 * KC;  // score MFMAs per block
-  constexpr int NPV = 4 * DT;  // P.V MFMAs per block
-  auto kread = [&](const uint16_t* ks, int i) {
-    const int kc = i >> 1, row = 32 * (i & 1) + r;
-    const int chunk = (2 * kc + hh) ^ (row % CPR);
-    return as_bf16x8(*reinterpret_cast<const uint4*>(ks + row * SM::KS + 8 * chunk));
-  };
-  auto vread = [&](const uint16_t* vt, int i) {
-    const int st = i / (2 * DT), part = (i / DT) % 2, dt = i % DT;
-    const uint16_t* vrow = vt + (32 * dt + r) * SM::VS + 32 * st + 16 * part + 4 * hh;
-    const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-    const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-  };
 
-  // Step for a block fully visible to every row of the wave, written in issue
-  // order: each score MFMA of the next block is followed by the exponentials of
-  // pairs of this block's scores, each P.V MFMA by part of the next block's V^T
-  // staging, with operands read two MFMAs ahead. sched_barrier keeps that order,
-  // so the vector work runs while the matrix core is busy. When kb + 1 == nkb the
-  // next scores read a stale buffer and are never used.
-  auto fast_step = [&](int kb, f32x16(&scur)[2], f32x16(&snext)[2]) {
-    kload_lds(kb + 2, kb & 1);  // K(kb) was last read for block kb's scores, in the previous step
-    gload_v(kb + 1);
+  // Step for a fully visible block, written in issue order: each score MFMA of
+  // the next block is followed by the exponentials of pairs of this block's
+  // scores; operands are read two MFMAs ahead. sched_barrier keeps that order, so
+  // the vector work runs while the matrix core is busy. When kb + 1 == nkb the
+  // next scores read a stage that holds no keys and are never used.
+  auto fast_step = [&](int kb, f32x16(&scur)[2], f32x16(&snext)[2]) MODA_INL {
+    issue_group(kb + P);
     const float m_use = max_and_rescale(scur);
-    const uint16_t* ks = Ks + ((kb + 1) & 1) * BN * SM::KS;
-    const uint16_t* vt = Vt + (kb & 1) * D * SM::VS;
+    const unsigned char* ks = kst + stage_of(kb + 1) * SM::STAGE;
+    const unsigned char* vs = vst + stage_of(kb) * SM::STAGE;
     uint32_t pp[2][8];
     float lsum = 0.f, rsum = 0.f;
     bf16x8 a0 = kread(ks, 0), a1 = kread(ks, 1);
@@ -686,66 +682,61 @@ moda_fwd_bf16_kernel(const Params p) {
         snext[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kc], snext[st], 0, 0, 0);
       }
 #pragma unroll
-      for (int q = i * 16 / NQK; q < (i + 1) * 16 / NQK; ++q) {
-        const int se = q >> 3, j = q & 7;
-        const float p0 = fast_exp2(fmaf(scur[se][2 * j], c2, -m_use));
-        const float p1 = fast_exp2(fmaf(scur[se][2 * j + 1], c2, -m_use));
-        lsum += p0 + p1;
-        pp[se][j] = pack_bf16(p0, p1);
-        rsum = dot2(pp[se][j], 0x3F803F80u, rsum);
-      }
+      for (int q = i * 16 / NQK; q < (i + 1) * 16 / NQK; ++q) exp_pair(scur, m_use, q, pp, lsum, rsum);
       __builtin_amdgcn_sched_barrier(0);
       a0 = a1;
       a1 = a2;
     }
     l_run += lsum;
     r_run += rsum;
-    bf16x8 b0 = vread(vt, 0), b1 = vread(vt, 1);
+    bf16x8 b0 = vread(vs, 0), b1 = vread(vs, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       bf16x8 b2 = b1;
-      if (i + 2 < NPV) b2 = vread(vt, i + 2);
-      const int st = i / (2 * DT), part = (i / DT) % 2, dt = i % DT;
-      const bf16x8 bfrag = as_bf16x8(
-          make_uint4(pp[st][4 * part + 0], pp[st][4 * part + 1], pp[st][4 * part + 2], pp[st][4 * part + 3]));
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, bfrag, acc[dt], 0, 0, 0);
-#pragma unroll
-      for (int e = i * 8 / NPV; e < (i + 1) * 8 / NPV; ++e) swrite_v_e((kb + 1) & 1, e);
+      if (i + 2 < NPV) b2 = vread(vs, i + 2);
+      acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, pfrag(pp, i), acc[i % DT], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       b0 = b1;
       b1 = b2;
     }
-    kload_wait();
-    __syncthreads();
+    block_end();
   };
-  auto step = [&](int kb, f32x16(&scur)[2], f32x16(&snext)[2]) {
+  // Generic step (the diagonal block, the segment end, blocks beyond some of the
+  // wave's rows): the same loads and barriers as the fast step.
+  auto step = [&](int kb, f32x16(&scur)[2], f32x16(&snext)[2]) MODA_INL {
     if (kb < n_full) {
       fast_step(kb, scur, snext);
       return;
     }
-    if (kb + 2 < nkb) kload_lds(kb + 2, kb & 1);
-    gload_v(kb + 1);
-    if (kb + 1 < nkb && active(kb + 1)) qk((kb + 1) & 1, snext);
+    issue_group(kb + P);
+    if (kb + 1 < nkb && active(kb + 1)) qk(kst + stage_of(kb + 1) * SM::STAGE, snext);
     if (active(kb)) {
       mask_block(kb, scur);
       const float m_use = max_and_rescale(scur);
       uint32_t pp[2][8];
-      exp_pack(scur, m_use, pp);
-      pv_mma(pp, kb & 1);
+      float lsum = 0.f, rsum = 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) exp_pair(scur, m_use, q, pp, lsum, rsum);
+      l_run += lsum;
+      r_run += rsum;
+      const unsigned char* vs = vst + stage_of(kb) * SM::STAGE;
+#pragma unroll
+      for (int i = 0; i < NPV; ++i)
+        acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vs, i), pfrag(pp, i), acc[i % DT], 0, 0, 0);
     }
-    if (kb + 1 < nkb) swrite_v((kb + 1) & 1);
-    kload_wait();
-    __syncthreads();
+    block_end();
   };
   for (int kb = 0; kb < nkb; kb += 2) {
     step(kb, sA, sB);
     if (kb + 1 < nkb) step(kb + 1, sB, sA);
   }
+  // the groups issued past the last block must land before their LDS is reused
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // ---- fold in the depth state of this row ------------------------------------
-  if constexpr (MODE == kSplit) depth_fold();  // published by the loop's last barrier
-  if (MODE == kSerial && !depth_first) {        // the loop's last barrier freed the K/V area
+  if (MODE == kSerial && !depth_first) {
+    __syncthreads();  // every wave's loads have landed: the K/V area is free
     depth_pass(wave);
     __syncthreads();
     depth_fold();
@@ -786,7 +777,7 @@ moda_fwd_bf16_kernel(const Params p) {
 
 template <int D, int GB, int NW, int MODE>
 hipError_t launch_t(const Params& p, bool out_f32, hipStream_t stream) {
-  const dim3 grid((unsigned)p.n_tiles), block(64 * NW * (MODE == kSplit ? 2 : 1));
+  const dim3 grid((unsigned)p.n_tiles), block(64 * NW);
   if (out_f32)
     hipLaunchKernelGGL((moda_fwd_bf16_kernel<D, GB, NW, MODE, true>), grid, block, 0, stream, p);
   else
@@ -797,7 +788,6 @@ hipError_t launch_t(const Params& p, bool out_f32, hipStream_t stream) {
 template <int D, int GB, int NW>
 hipError_t launch_d(const Params& p, bool out_f32, hipStream_t stream) {
   if (p.n_depth == 0) return launch_t<D, GB, NW, kNoDepth>(p, out_f32, stream);
-  if (p.depth_mode == kSplit) return launch_t<D, GB, NW, kSplit>(p, out_f32, stream);
   return launch_t<D, GB, NW, kSerial>(p, out_f32, stream);
 }
 

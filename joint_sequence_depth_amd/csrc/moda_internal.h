@@ -37,10 +37,8 @@ struct Params {
   int64_t lse_head_stride;    // T (batch layout) or N (packed layout)
   int32_t lse_batch_layout;   // 1: base = s * Hq * T; 0: base = seg_start
   int32_t xcd_interleave;     // 1: (segment, KV head) pairs go round-robin to the 8 XCDs
-  int32_t depth_mode;         // bf16 kernel with n_depth > 0: 1 = depth waves beside the
-                              // sequence waves, 2 = depth pass and sequence loop in turn
-  int32_t serial_order;       // depth_mode 2: 0 = alternate by workgroup round, 1 = depth
-                              // pass first, 2 = sequence loop first
+  int32_t serial_order;       // bf16 with depth slots: 0 = depth pass first and last in turn
+                              // (by workgroup round), 1 = depth pass first, 2 = last
   int64_t n_tiles;
 };
 
