@@ -47,7 +47,8 @@ def kernel_source_sha() -> str:
 
 def kernel_name(w) -> str:
     """The kernel instance the library launches for this workload (mirrors the
-    host dispatch: heads per workgroup, waves per workgroup, depth schedule)."""
+    host dispatch: heads per workgroup, waves per workgroup, depth schedule,
+    shared or split tiles)."""
     if not w.bf16:
         return f"moda_fwd_f32_kernel<{w.head_dim}>"
     G = w.group
@@ -55,14 +56,16 @@ def kernel_name(w) -> str:
     n_hg = G // gb
     n_pairs = len(w.lengths) * w.n_heads_kv
     max_len = max(w.lengths)
-    waves = 1
+    waves, split = 0, False
     for nw in (4, 2):
         tok = 32 * nw // gb
         if n_pairs * n_hg * ((max_len + tok - 1) // tok) >= 512:
             waves = nw
             break
-    mode = 0 if w.n_depth == 0 else 2
-    return f"moda_fwd_bf16_kernel<{w.head_dim}, {gb}, {waves}, {mode}, false>"
+    if waves == 0:
+        waves, split = 2, True
+    mode = 0 if w.n_depth == 0 else 1
+    return f"moda_fwd_bf16_kernel<{w.head_dim}, {gb}, {waves}, {mode}, false, {str(split).lower()}>"
 
 
 def roofline(w, sec_per_launch: float) -> dict:

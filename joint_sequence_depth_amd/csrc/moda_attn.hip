@@ -90,7 +90,7 @@ int dispatch(moda::Params& p, const Common& c, int64_t n_seg, int64_t max_len, h
     const int gb = heads_per_block(p.G);
     p.n_hgroups = p.G / gb;
     const int64_t n_pairs = n_seg * p.Hkv;
-    // Waves per workgroup: the largest of 4, 2, 1 that still gives every CU two
+    // Waves per workgroup: the largest of 4, 2 that still gives every CU two
     // workgroups (fewer rows per workgroup for small problems).
     int waves = 1;
     for (int w = 4; w >= 2; w /= 2) {
@@ -100,18 +100,24 @@ int dispatch(moda::Params& p, const Common& c, int64_t n_seg, int64_t max_len, h
         break;
       }
     }
-    const int tok = moda::kWaveRows * waves / gb;
+    // Too few tiles for two waves per CU even with one-wave tiles: split tiles,
+    // whose waves share a 32-row tile and divide its key blocks, ordered heaviest
+    // first across all pairs.
+    const bool split = waves == 1;
+    if (split) waves = c.d == 64 ? moda::kSplitWaves<64> : moda::kSplitWaves<128>;  // both 2
+    const int tok = split ? moda::kWaveRows / gb : moda::kWaveRows * waves / gb;
     const int64_t nqb = (max_len + tok - 1) / tok;
     p.n_qblocks = (int32_t)nqb;
     p.n_tiles = n_pairs * p.n_hgroups * nqb;
-    p.xcd_interleave = (n_pairs % 8 == 0) ? 1 : 0;
+    p.xcd_interleave = (!split && n_pairs % 8 == 0) ? 1 : 0;
+    p.qb_major = split ? 1 : 0;
 #ifdef MODA_FORCE_SERIAL_ORDER
     p.serial_order = MODA_FORCE_SERIAL_ORDER;
 #else
     p.serial_order = 0;
 #endif
     if (nqb > kMaxTiles || p.n_tiles > kMaxTiles) return fail(MODA_ERR_SHAPE, "problem too large for one launch");
-    err = moda::launch_fwd_bf16(p, c.d, gb, waves, c.out_dtype == MODA_DTYPE_F32, stream);
+    err = moda::launch_fwd_bf16(p, c.d, gb, waves, split, c.out_dtype == MODA_DTYPE_F32, stream);
   } else {
     const int64_t nqb = (max_len + moda::kF32BlockRows - 1) / moda::kF32BlockRows;
     p.n_hgroups = 1;

@@ -134,6 +134,8 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t nrec) {
 // order, so the compiler's own waits for other loads only become more
 // conservative).
 __device__ __forceinline__ void load_to_lds16(uint32_t lds, uint32_t voff, i32x4 rsrc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);  // uniform: no-op when scalar
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
@@ -163,12 +165,19 @@ struct Tile {
 // (id % 8). With a multiple of 8 pairs, pair p runs all of its tiles on XCD p % 8:
 // its K/V blocks, read by every query block, stay in that XCD's L2, and every XCD
 // gets an equal share of every segment, whatever the segment lengths. Within a
-// pair, late (heavy causal) query blocks go first.
+// pair, late (heavy causal) query blocks go first. With qb_major (used when the
+// grid runs in few rounds) the order is by query block across all pairs instead,
+// heaviest first, so the first round holds the longest causal tiles.
 __device__ __forceinline__ Tile decode_tile(const Params& p) {
   const int64_t id = blockIdx.x;
   const int64_t per_pair = (int64_t)p.n_qblocks * p.n_hgroups;
   int64_t pair, r;
-  if (p.xcd_interleave) {
+  if (p.qb_major) {
+    const int64_t units = (int64_t)p.n_seg * p.Hkv * p.n_hgroups;  // (pair, head group) per query block
+    const int64_t qrank = id / units, u = id % units;
+    pair = u / p.n_hgroups;
+    r = qrank * p.n_hgroups + u % p.n_hgroups;
+  } else if (p.xcd_interleave) {
     const int64_t x = id & 7, j = id >> 3;
     pair = (j / per_pair) * 8 + x;
     r = j % per_pair;
@@ -189,49 +198,68 @@ enum Mode : int {
   kSerial = 1,   // every wave runs a depth pass and the sequence loop, one after the other
 };
 
-// LDS: NST stages of one K block and NST stages of one V block, each BN rows of D
-// bf16 without padding; the 16-byte chunks of a row are XOR-swizzled (K and V with
-// different patterns, chosen for their readers). The depth hand-off reuses the
-// same bytes between the two parts.
-template <int D, int NW, int MODE>
+// LDS. Stages hold one K or V block each: BN rows of D bf16 without padding, the
+// 16-byte chunks of a row XOR-swizzled (K and V with different patterns, chosen
+// for their readers).
+//  * Shared tiles (SPLIT false): NST K and NST V stages shared by the NW waves;
+//    the depth hand-off reuses the stage bytes between the two parts.
+//  * Split tiles (SPLIT true): each wave has its own NST K and V stages; the depth
+//    hand-off has its own area; the partial states of waves 1 .. NW - 1 reuse the
+//    stage bytes for the final merge.
+template <int D, int NW, int MODE, bool SPLIT>
 struct Smem {
-  static constexpr int NST = D == 64 ? 3 : 2;  // loads run NST - 1 blocks ahead
-  static constexpr int STAGE = BN * D * 2;     // bytes of one K or V block
+  static constexpr int NST = SPLIT ? 2 : (D == 64 ? 3 : 2);  // loads run NST - 1 blocks ahead
+  static constexpr int STAGE = BN * D * 2;                    // bytes of one K or V block
+  static constexpr int SETS = SPLIT ? NW : 1;                 // stage sets
   static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = NST * STAGE;
-  static constexpr int SEQ_BYTES = 2 * NST * STAGE;
-  static constexpr int OS = D + 4;  // depth hand-off row stride (fp32)
-  static constexpr int OD_OFF = 0;
-  static constexpr int MD_OFF = OD_OFF + NW * WROWS * OS * 4;
-  static constexpr int AD_OFF = MD_OFF + NW * WROWS * 4;
-  static constexpr int END = AD_OFF + NW * WROWS * 4;
+  static constexpr int V_OFF = SETS * NST * STAGE;
+  static constexpr int SEQ_BYTES = 2 * SETS * NST * STAGE;
+  static constexpr int ROWS = SPLIT ? WROWS : NW * WROWS;  // query rows of the workgroup
+  static constexpr int OS = D + 4;                          // depth hand-off row stride (fp32)
+  static constexpr int OD_OFF = SPLIT ? SEQ_BYTES : 0;
+  static constexpr int MD_OFF = OD_OFF + ROWS * OS * 4;
+  static constexpr int AD_OFF = MD_OFF + ROWS * 4;
+  static constexpr int END = AD_OFF + ROWS * 4;
+  static constexpr int MG = 16 * (D / 32) + 4;  // merge record per lane (fp32): acc, m, l, r
+  static constexpr int MG_BYTES = SPLIT ? (NW - 1) * 64 * MG * 4 : 0;
   static constexpr int BYTES = MODE == kNoDepth ? SEQ_BYTES : (END > SEQ_BYTES ? END : SEQ_BYTES);
+  static_assert(MG_BYTES <= SEQ_BYTES, "merge area");
 };
 
-template <int D, int GB, int NW, int MODE, bool OUT_F32>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2))) void
+// SPLIT: the NW waves of a workgroup share one 32-row tile and split its key
+// blocks (wave w takes blocks w, w + NW, ...), each through its own stages and
+// without workgroup barriers; their partial states merge at the end. For problems
+// with too few tiles to give every SIMD a wave: it shortens the longest chain of
+// dependent blocks (the last causal tile) NW times.
+template <int D, int GB, int NW, int MODE, bool OUT_F32, bool SPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
+                          amdgpu_waves_per_eu(SPLIT ? 1 : 2, SPLIT ? 1 : 2))) void
 moda_fwd_bf16_kernel(const Params p) {
-  constexpr int TW = WROWS / GB;               // tokens per wave
-  constexpr int TOK = TW * NW;                 // tokens per workgroup
-  constexpr int LPR = D / 8;                   // lanes per 16-byte-sliced row of D
-  constexpr int NGRP = 64 / LPR;               // tokens per wave-wide depth load
-  constexpr int NTG = (TW + NGRP - 1) / NGRP;  // depth token groups per wave
-  constexpr int CPR = D / 8;                   // 16-byte chunks per K/V row
-  constexpr int RPI = 64 / CPR;                // K/V rows per wave-wide direct-to-LDS load (1 KB)
-  constexpr int KPT = BN / (NW * RPI);         // such loads per wave per K (or V) block
+  constexpr int TW = WROWS / GB;                 // tokens of a 32-row tile
+  constexpr int TOK = SPLIT ? TW : TW * NW;      // tokens per workgroup
+  constexpr int TPW = SPLIT ? TW / NW : TW;      // tokens of each wave's depth pass
+  constexpr int LPR = D / 8;                     // lanes per 16-byte-sliced row of D
+  constexpr int NGRP = 64 / LPR;                 // tokens per wave-wide depth load
+  constexpr int NTG = (TPW + NGRP - 1) / NGRP;   // depth token groups per wave
+  constexpr int CPR = D / 8;                     // 16-byte chunks per K/V row
+  constexpr int RPI = 64 / CPR;                  // K/V rows per wave-wide direct-to-LDS load (1 KB)
+  constexpr int KPT = SPLIT ? BN / RPI : BN / (NW * RPI);  // such loads per wave per K (or V) block
   constexpr int KC = D / 16;                   // k-chunks of Q K^T
   constexpr int DT = D / 32;                   // 32-wide d tiles of O^T
   constexpr int U = GB == 1 ? 8 : (GB == 2 ? 4 : 2);  // depth slots per load batch
   constexpr bool QPRE = GB <= 2;               // prefetch a token's q rows with its first batch
   constexpr int QBUF = QPRE ? GB : 1;
   // depth load buffers (batches in flight + 1); when the depth pass follows the
-  // sequence loop the O^T accumulators are live, so the count stays small
+  // sequence loop the O^T accumulators are live, so the count stays small (more
+  // batches issued before a split tile's loop only add to the HBM burst at its
+  // start)
   constexpr int NBUF = GB == 1 ? 2 : (GB == 2 ? 3 : 4);
-  using SM = Smem<D, NW, MODE>;
+  using SM = Smem<D, NW, MODE, SPLIT>;
   constexpr int NST = SM::NST;
   constexpr int P = NST - 1;                 // load groups in flight ahead of the current block
   constexpr int WAIT_N = (P - 1) * 2 * KPT;  // loads allowed outstanding at the end of a block
-  static_assert(KPT >= 1 && KPT * NW * RPI == BN && RPI % 4 == 0, "tile shape");
+  static_assert(KPT >= 1 && KPT * (SPLIT ? 1 : NW) * RPI == BN && RPI % 4 == 0, "tile shape");
+  static_assert(!SPLIT || (TW % NW == 0 && NW >= 2), "split tile shape");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[SM::BYTES];
 
@@ -265,131 +293,139 @@ moda_fwd_bf16_kernel(const Params p) {
   const int64_t kend = p.causal ? (len < t0 + TOK ? len : t0 + TOK) : len;
   const int nkb = (int)((kend + BN - 1) / BN);  // sequence key blocks
 
-  float* od = reinterpret_cast<float*>(smem + SM::OD_OFF);  // [NW*WROWS][OS]
-  float* md = reinterpret_cast<float*>(smem + SM::MD_OFF);  // [NW*WROWS]
-  float* ad = reinterpret_cast<float*>(smem + SM::AD_OFF);  // [NW*WROWS]
+  float* od = reinterpret_cast<float*>(smem + SM::OD_OFF);  // [ROWS][OS]
+  float* md = reinterpret_cast<float*>(smem + SM::MD_OFF);  // [ROWS]
+  float* ad = reinterpret_cast<float*>(smem + SM::AD_OFF);  // [ROWS]
 
   // ================================================================ depth pass
-  // Folds the depth slots of the tokens of rows [32 dw, 32 dw + 32) into partial
-  // row states (m, acc, o) in LDS.
-  auto depth_pass = [&](const int dw) MODA_INL {
-    const int n_depth = p.n_depth;
-    const uint16_t* __restrict__ KD = static_cast<const uint16_t*>(p.kd);
-    const uint16_t* __restrict__ VD = static_cast<const uint16_t*>(p.vd);
-    const int grp = lane / LPR, cl = lane % LPR;
-    const int64_t slot_stride = (int64_t)Hkv * D;
-    const int nch = (n_depth + U - 1) / U;  // slot batches per token
-    const int n_it = NTG * nch;             // (token group, slot batch) steps
+  // Folds the depth slots of the workgroup's tokens [dt0, dt0 + TPW) (its rows
+  // [dt0 GB, (dt0 + TPW) GB)) into partial row states (m, acc, o) in LDS.
+  // depth_begin issues the first NBUF - 1 load batches, depth_end runs the rest.
+  const int dt0 = wave * TPW;
+  const int n_depth = p.n_depth;
+  const uint16_t* __restrict__ KD = static_cast<const uint16_t*>(p.kd);
+  const uint16_t* __restrict__ VD = static_cast<const uint16_t*>(p.vd);
+  const int d_grp = lane / LPR, d_cl = lane % LPR;
+  const int64_t slot_stride = (int64_t)Hkv * D;
+  const int nch = (n_depth + U - 1) / U;  // slot batches per token
+  const int n_it = NTG * nch;             // (token group, slot batch) steps
+  // depth load buffers: shared by depth_begin and depth_end (always written
+  // before they are read)
+  uint4 dkb[NBUF][U], dvb[NBUF][U], dqb[NBUF][QBUF];
 
-    // Loads for step `it`: U slot rows of K and V (and the token's q rows at its
-    // first batch) into one of the register buffers. The loads are unconditional
-    // so the compiler keeps them in flight across the arithmetic: a slot past
-    // n_depth re-reads the last slot and a token past the segment re-reads its
-    // last token (cache hits); such logits are masked and such rows discarded.
-    auto issue = [&](int it, uint4(&kw)[U], uint4(&vw)[U], uint4(&qw)[QBUF]) MODA_INL {
-      it = it < n_it ? it : n_it - 1;  // the steps past the end re-load the last one (never processed)
-      const int tg = it / nch, ch = it - tg * nch;
-      const int tl = tg * NGRP + grp;
-      int64_t t = t0 + (int64_t)dw * TW + (tl < TW ? tl : TW - 1);
+  // Loads for step `it`: U slot rows of K and V (and the token's q rows at its
+  // first batch) into one of the register buffers. The loads are unconditional so
+  // the compiler keeps them in flight across the arithmetic: a slot past n_depth
+  // re-reads the last slot and a token past the segment re-reads its last token
+  // (cache hits); such logits are masked and such rows discarded.
+  auto issue = [&](int it, uint4(&kw)[U], uint4(&vw)[U], uint4(&qw)[QBUF]) MODA_INL {
+    it = it < n_it ? it : n_it - 1;  // the steps past the end re-load the last one (never processed)
+    const int tg = it / nch, ch = it - tg * nch;
+    const int tl = tg * NGRP + d_grp;
+    int64_t t = t0 + dt0 + (tl < TPW ? tl : TPW - 1);
+    t = t < len ? t : len - 1;
+    const int64_t n = seg_start + t;
+    const int64_t base = (n * p.S_cap * Hkv + hk) * (int64_t)D + 8 * d_cl;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int slot = ch * U + u < n_depth ? ch * U + u : n_depth - 1;
+      kw[u] = ldg16(KD + base + slot * slot_stride);
+      vw[u] = ldg16(VD + base + slot * slot_stride);
+    }
+    if constexpr (QPRE) {  // every step: a fixed load count keeps the wait counts exact
+#pragma unroll
+      for (int g = 0; g < QBUF; ++g) qw[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * d_cl));
+    }
+  };
+  // One step of the pass on the loaded batch; the row states (qc: q rows of the
+  // current token, dm / da / dacc: max, sum and weighted sum per head) belong to
+  // one call of depth_end, so none of them lives across the sequence loop.
+  auto process = [&](int it, const uint4(&kw)[U], const uint4(&vw)[U], const uint4(&qw)[QBUF], uint4(&qc)[GB],
+                     float(&dm)[GB], float(&da)[GB], float(&dacc)[GB][8]) MODA_INL {
+    const int tg = it / nch, ch = it - tg * nch;
+    const int tl = tg * NGRP + d_grp;
+    if (ch == 0) {
+      int64_t t = t0 + dt0 + (tl < TPW ? tl : TPW - 1);
       t = t < len ? t : len - 1;
       const int64_t n = seg_start + t;
-      const int64_t base = (n * p.S_cap * Hkv + hk) * (int64_t)D + 8 * cl;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int slot = ch * U + u < n_depth ? ch * U + u : n_depth - 1;
-        kw[u] = ldg16(KD + base + slot * slot_stride);
-        vw[u] = ldg16(VD + base + slot * slot_stride);
-      }
-      if constexpr (QPRE) {  // every step: a fixed load count keeps the wait counts exact
-#pragma unroll
-        for (int g = 0; g < QBUF; ++g) qw[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * cl));
-      }
-    };
-
-    uint4 qc[GB];  // q rows of the current token, packed bf16
-    float m[GB], a[GB], o[GB][8];
-    auto process = [&](int it, const uint4(&kw)[U], const uint4(&vw)[U], const uint4(&qw)[QBUF]) MODA_INL {
-      const int tg = it / nch, ch = it - tg * nch;
-      const int tl = tg * NGRP + grp;
-      if (ch == 0) {
-        int64_t t = t0 + (int64_t)dw * TW + (tl < TW ? tl : TW - 1);
-        t = t < len ? t : len - 1;
-        const int64_t n = seg_start + t;
-#pragma unroll
-        for (int g = 0; g < GB; ++g) {
-          if constexpr (QPRE) {
-            qc[g] = qw[g < QBUF ? g : 0];
-          } else {
-            qc[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * cl));
-          }
-          m[g] = NEG_INF;
-          a[g] = 0.f;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
-        }
-      }
 #pragma unroll
       for (int g = 0; g < GB; ++g) {
-        float b[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float s = dot2(qc[g].x, kw[u].x, 0.f);
-          s = dot2(qc[g].y, kw[u].y, s);
-          s = dot2(qc[g].z, kw[u].z, s);
-          s = dot2(qc[g].w, kw[u].w, s);
-          s = group_sum<LPR>(s);
-          b[u] = (ch * U + u < n_depth) ? s * c2 : NEG_INF;
+        if constexpr (QPRE) {
+          qc[g] = qw[g < QBUF ? g : 0];
+        } else {
+          qc[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * d_cl));
         }
-        float mx = b[0];
+        dm[g] = NEG_INF;
+        da[g] = 0.f;
 #pragma unroll
-        for (int u = 1; u < U; ++u) mx = fmaxf(mx, b[u]);
-        const float m_new = fmaxf(m[g], mx);
-        const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-        const float alpha = fast_exp2(m[g] - m_use);
-        a[g] *= alpha;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[g][j] *= alpha;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float pu = fast_exp2(b[u] - m_use);
-          a[g] += pu;
-          o[g][0] = fmaf(pu, lo_bf16(vw[u].x), o[g][0]);
-          o[g][1] = fmaf(pu, hi_bf16(vw[u].x), o[g][1]);
-          o[g][2] = fmaf(pu, lo_bf16(vw[u].y), o[g][2]);
-          o[g][3] = fmaf(pu, hi_bf16(vw[u].y), o[g][3]);
-          o[g][4] = fmaf(pu, lo_bf16(vw[u].z), o[g][4]);
-          o[g][5] = fmaf(pu, hi_bf16(vw[u].z), o[g][5]);
-          o[g][6] = fmaf(pu, lo_bf16(vw[u].w), o[g][6]);
-          o[g][7] = fmaf(pu, hi_bf16(vw[u].w), o[g][7]);
-        }
-        m[g] = m_new;
+        for (int j = 0; j < 8; ++j) dacc[g][j] = 0.f;
       }
-      if (ch == nch - 1 && tl < TW) {
+    }
 #pragma unroll
-        for (int g = 0; g < GB; ++g) {
-          const int row = dw * WROWS + tl * GB + g;
-          float4* dst = reinterpret_cast<float4*>(od + row * SM::OS + 8 * cl);
-          dst[0] = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
-          dst[1] = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);
-          if (cl == 0) {
-            md[row] = m[g];
-            ad[row] = a[g];
-          }
+    for (int g = 0; g < GB; ++g) {
+      float b[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float sc = dot2(qc[g].x, kw[u].x, 0.f);
+        sc = dot2(qc[g].y, kw[u].y, sc);
+        sc = dot2(qc[g].z, kw[u].z, sc);
+        sc = dot2(qc[g].w, kw[u].w, sc);
+        sc = group_sum<LPR>(sc);
+        b[u] = (ch * U + u < n_depth) ? sc * c2 : NEG_INF;
+      }
+      float mx = b[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mx = fmaxf(mx, b[u]);
+      const float m_new = fmaxf(dm[g], mx);
+      const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+      const float alpha = fast_exp2(dm[g] - m_use);
+      da[g] *= alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dacc[g][j] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float pu = fast_exp2(b[u] - m_use);
+        da[g] += pu;
+        dacc[g][0] = fmaf(pu, lo_bf16(vw[u].x), dacc[g][0]);
+        dacc[g][1] = fmaf(pu, hi_bf16(vw[u].x), dacc[g][1]);
+        dacc[g][2] = fmaf(pu, lo_bf16(vw[u].y), dacc[g][2]);
+        dacc[g][3] = fmaf(pu, hi_bf16(vw[u].y), dacc[g][3]);
+        dacc[g][4] = fmaf(pu, lo_bf16(vw[u].z), dacc[g][4]);
+        dacc[g][5] = fmaf(pu, hi_bf16(vw[u].z), dacc[g][5]);
+        dacc[g][6] = fmaf(pu, lo_bf16(vw[u].w), dacc[g][6]);
+        dacc[g][7] = fmaf(pu, hi_bf16(vw[u].w), dacc[g][7]);
+      }
+      dm[g] = m_new;
+    }
+    if (ch == nch - 1 && tl < TPW) {
+#pragma unroll
+      for (int g = 0; g < GB; ++g) {
+        const int row = (dt0 + tl) * GB + g;
+        float4* dst = reinterpret_cast<float4*>(od + row * SM::OS + 8 * d_cl);
+        dst[0] = make_float4(dacc[g][0], dacc[g][1], dacc[g][2], dacc[g][3]);
+        dst[1] = make_float4(dacc[g][4], dacc[g][5], dacc[g][6], dacc[g][7]);
+        if (d_cl == 0) {
+          md[row] = dm[g];
+          ad[row] = da[g];
         }
       }
-    };
-
-    // NBUF register buffers, loads NBUF - 1 steps ahead. Every step issues the
-    // same number of loads, so the compiler waits exactly for the buffer it reads
-    // and leaves the others in flight.
-    uint4 kb[NBUF][U], vb[NBUF][U], qb[NBUF][QBUF];
+    }
+  };
+  // NBUF register buffers, loads NBUF - 1 steps ahead. Every step issues the same
+  // number of loads, so the compiler waits exactly for the buffer it reads and
+  // leaves the others in flight.
+  auto depth_begin = [&]() MODA_INL {
 #pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) issue(j, kb[j], vb[j], qb[j]);
+    for (int j = 0; j < NBUF - 1; ++j) issue(j, dkb[j], dvb[j], dqb[j]);
+  };
+  auto depth_end = [&]() MODA_INL {
+    uint4 qc[GB];
+    float dm[GB], da[GB], dacc[GB][8];
     for (int it = 0; it < n_it; it += NBUF) {
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
-        issue(it + j + NBUF - 1, kb[(j + NBUF - 1) % NBUF], vb[(j + NBUF - 1) % NBUF], qb[(j + NBUF - 1) % NBUF]);
-        if (it + j < n_it) process(it + j, kb[j], vb[j], qb[j]);
+        issue(it + j + NBUF - 1, dkb[(j + NBUF - 1) % NBUF], dvb[(j + NBUF - 1) % NBUF], dqb[(j + NBUF - 1) % NBUF]);
+        if (it + j < n_it) process(it + j, dkb[j], dvb[j], dqb[j], qc, dm, da, dacc);
       }
     }
   };
@@ -397,7 +433,8 @@ moda_fwd_bf16_kernel(const Params p) {
   // ============================================================ sequence state
   const int r = lane & 31;   // row within the wave (column of the 32x32 tiles)
   const int hh = lane >> 5;  // which half of each 16-wide contraction chunk
-  const int rowb = wave * WROWS + r;
+  const int wrow0 = SPLIT ? 0 : wave * WROWS;  // first row of this wave's 32
+  const int rowb = wrow0 + r;
   const int64_t tq = t0 + rowb / GB;
   const int hq = hbase + rowb % GB;
   const bool row_valid = tq < len;
@@ -434,14 +471,18 @@ moda_fwd_bf16_kernel(const Params p) {
     m_run = m_new;
   };
 
-  // The two workgroups that share a CU run the depth pass first and last in turn
-  // (the first round of workgroups on an XCD's 32 CUs starts with it, the second
-  // with the sequence loop), so one streams from HBM while the other keeps the
-  // matrix cores busy.
-  const bool depth_first =
-      MODE == kSerial && (p.serial_order == 0 ? (((blockIdx.x >> 3) >> 5) & 1) == 0 : p.serial_order == 1);
+  // Shared tiles: the two workgroups that share a CU run the depth pass first and
+  // last in turn (the first round of workgroups on an XCD's 32 CUs starts with it,
+  // the second with the sequence loop), so one streams from HBM while the other
+  // keeps the matrix cores busy. Split tiles at D = 64: the depth loads are issued
+  // as the sequence loop starts and consumed after it, which hides their latency
+  // (at D = 128 the loop needs those registers; the pass follows the loop).
+  constexpr bool EARLY_DEPTH = MODE == kSerial && SPLIT && D == 64;
+  const bool depth_first = MODE == kSerial && !SPLIT &&
+                           (p.serial_order == 0 ? (((blockIdx.x >> 3) >> 5) & 1) == 0 : p.serial_order == 1);
   if (MODE == kSerial && depth_first) {
-    depth_pass(wave);
+    depth_begin();
+    depth_end();
     __syncthreads();
     depth_fold();
     __syncthreads();  // the hand-off area is the K/V area
@@ -480,26 +521,28 @@ moda_fwd_bf16_kernel(const Params p) {
   auto sv = [](int k) MODA_INL { return D == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); };
   const int ld_row = lane / CPR, ld_pos = lane % CPR;  // this lane's place in a 1 KB run
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // the wave index as a scalar
+  const int run0 = SPLIT ? 0 : wave_u * KPT;  // this wave's first 1 KB run of a block
   const uint32_t row_bytes32 = (uint32_t)Hkv * (uint32_t)(D * 2);  // scalar: a full block's offsets fit 32 bits
   auto stage_of = [](int kb) MODA_INL { return kb - (kb / NST) * NST; };
   // Per-lane parts of the load offsets of a full block (loop-invariant): the LDS
-  // row of load j is (wave KPT + j) RPI + ld_row, whose uniform part is added per
+  // row of load j is (run0 + j) RPI + ld_row, whose uniform part is added per
   // load (no multiply in the loop). The K swizzle at D = 128 also depends on that row's bits 2-3,
   // a uniform XOR of bits 6-7 of the chunk offset; row_bytes is then a multiple of
   // 256, so the XOR never meets a carry from the row part.
   const uint32_t k_lane = (uint32_t)(ld_row * row_bytes + 16 * (ld_pos ^ (ld_row % CPR)));
   const uint32_t v_lane = (uint32_t)(ld_row * row_bytes + 16 * (ld_pos ^ sv(ld_row)));
-  // one block of K (or V) into `stage`: KPT wave-wide loads per wave
+  // one block of K (or V) into `stage`: KPT wave-wide loads by this wave (runs
+  // run0 .. run0 + KPT - 1 of the block)
   auto load_block = [&](const char* base, int kb, unsigned char* stage, bool is_v) MODA_INL {
     const int64_t keys_left = kend - (int64_t)kb * BN;
     int64_t nrec = keys_left > 0 ? (keys_left - 1) * row_bytes + D * 2 : 0;
     nrec = nrec < 0x7fffffff ? nrec : 0x7fffffff;
     const i32x4 rs = make_rsrc(base + (int64_t)kb * BN * row_bytes, (uint32_t)nrec);
-    const uint32_t lds0 = (uint32_t)(uintptr_t)stage + (uint32_t)(wave_u * KPT) * 1024u;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)stage + (uint32_t)run0 * 1024u;
     if (keys_left >= BN) {  // full block: every row in range, no clamp
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        const uint32_t rg = (uint32_t)(wave_u * KPT + j);  // uniform: which RPI-row run
+        const uint32_t rg = (uint32_t)(run0 + j);  // uniform: which RPI-row run
         uint32_t voff = is_v ? v_lane : k_lane;
         if (D == 128 && !is_v) voff ^= 64u * (rg & 3u);
         load_to_lds16(lds0 + 1024u * j, voff + rg * (uint32_t)RPI * row_bytes32, rs);
@@ -508,31 +551,34 @@ moda_fwd_bf16_kernel(const Params p) {
       const int last = keys_left > 0 ? (int)keys_left - 1 : 0;
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        const int row = (wave_u * KPT + j) * RPI + ld_row;  // key within the block = LDS row
+        const int row = (run0 + j) * RPI + ld_row;  // key within the block = LDS row
         const int src = row < last ? row : last;            // key whose row is loaded there
         const int chunk = ld_pos ^ (is_v ? sv(row) : (row % CPR));
         load_to_lds16(lds0 + 1024u * j, (uint32_t)(src * row_bytes + 16 * chunk), rs);
       }
     }
   };
-  unsigned char* const kst = smem + SM::K_OFF;
-  unsigned char* const vst = smem + SM::V_OFF;
-  // Load group j: K of block j + 1 and V of block j, both read in the step of
-  // block j (the scores run one block ahead). Group j + P is issued at the top of
-  // step j, into the stages of K(j) and V(j - 1), which step j - 1 released.
-  auto issue_group = [&](int j) MODA_INL {
-    load_block(kbase, j + 1, kst + stage_of(j + 1) * SM::STAGE, false);
-    load_block(vbase, j, vst + stage_of(j) * SM::STAGE, true);
+  unsigned char* const kst = smem + SM::K_OFF + (SPLIT ? wave_u * NST * SM::STAGE : 0);
+  unsigned char* const vst = smem + SM::V_OFF + (SPLIT ? wave_u * NST * SM::STAGE : 0);
+  // This wave's key blocks: bid(i), i = 0 .. nbw - 1 (all blocks, or every NW-th).
+  const int nbw = SPLIT ? (nkb > wave_u ? (nkb - wave_u + NW - 1) / NW : 0) : nkb;
+  auto bid = [&](int i) MODA_INL { return SPLIT ? wave_u + i * NW : i; };
+  // Load group i: K of block bid(i + 1) and V of block bid(i), both read in step i
+  // (the scores run one block ahead). Group i + P is issued at the top of step i,
+  // into the stages of K(bid(i)) and V(bid(i - 1)), which step i - 1 released.
+  auto issue_group = [&](int i) MODA_INL {
+    load_block(kbase, bid(i + 1), kst + stage_of(i + 1) * SM::STAGE, false);
+    load_block(vbase, bid(i), vst + stage_of(i) * SM::STAGE, true);
   };
-  // the end of a block: load group kb + 1 has landed (only later groups may still
-  // be in flight), and every wave is done with block kb's stages
+  // the end of a step: load group i + 1 has landed (only later groups may still be
+  // in flight); shared tiles: every wave is done with step i's stages
   auto block_end = [&]() MODA_INL {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAIT_N));
-    __syncthreads();
+    if constexpr (!SPLIT) __syncthreads();
   };
 
-  const int64_t wave_tmin = t0 + (wave * WROWS) / GB;
-  const int64_t wave_tmax = t0 + (wave * WROWS + WROWS - 1) / GB;
+  const int64_t wave_tmin = t0 + wrow0 / GB;
+  const int64_t wave_tmax = t0 + (wrow0 + WROWS - 1) / GB;
   // a wave's rows see key block kb at all (monotone in kb)
   auto active = [&](int kb) MODA_INL { return !p.causal || (int64_t)kb * BN <= wave_tmax; };
 
@@ -636,16 +682,20 @@ moda_fwd_bf16_kernel(const Params p) {
   constexpr int NQK = 2 * KC;  // score MFMAs per block
   constexpr int NPV = 4 * DT;  // P.V MFMAs per block
 
-  // Prologue: K(0) and load groups 0 .. P - 1, then the scores of block 0. The
-  // barrier after them keeps step 0 from reloading K(0)'s stage under a wave that
-  // is still reading it.
-  load_block(kbase, 0, kst, false);
-#pragma unroll
-  for (int j = 0; j < P; ++j) issue_group(j);
-  block_end();
+  // Prologue: K(bid(0)) and load groups 0 .. P - 1, then the scores of block
+  // bid(0). Shared tiles: the barrier after them keeps step 0 from reloading
+  // K(0)'s stage under a wave that is still reading it (split tiles: the stages are
+  // the wave's own, read before it issues the next loads).
   f32x16 sA[2], sB[2];
-  qk(kst, sA);  // every wave sees block 0 (unconditional, so the q loads are waited for here only)
-  __syncthreads();
+  if (nbw > 0) {  // shared tiles: always (nkb >= 1); split: waves past the last block skip
+    load_block(kbase, bid(0), kst, false);
+#pragma unroll
+    for (int j = 0; j < P; ++j) issue_group(j);
+    block_end();
+    qk(kst, sA);  // every wave sees its first block (unconditional: the q loads are waited for here only)
+    if constexpr (!SPLIT) __syncthreads();
+  }
+  if constexpr (EARLY_DEPTH) depth_begin();
 
   // Blocks [0, n_full) are fully visible to every row of this wave: a
   // straight-line step (no mask, the next block's scores always issued) lets the
@@ -659,11 +709,11 @@ moda_fwd_bf16_kernel(const Params p) {
   // scores; operands are read two MFMAs ahead. sched_barrier keeps that order, so
   // the vector work runs while the matrix core is busy. When kb + 1 == nkb the
   // next scores read a stage that holds no keys and are never used.
-  auto fast_step = [&](int kb, f32x16(&scur)[2], f32x16(&snext)[2]) MODA_INL {
-    issue_group(kb + P);
+  auto fast_step = [&](int i, f32x16(&scur)[2], f32x16(&snext)[2]) MODA_INL {
+    issue_group(i + P);
     const float m_use = max_and_rescale(scur);
-    const unsigned char* ks = kst + stage_of(kb + 1) * SM::STAGE;
-    const unsigned char* vs = vst + stage_of(kb) * SM::STAGE;
+    const unsigned char* ks = kst + stage_of(i + 1) * SM::STAGE;
+    const unsigned char* vs = vst + stage_of(i) * SM::STAGE;
     uint32_t pp[2][8];
     float lsum = 0.f, rsum = 0.f;
     bf16x8 a0 = kread(ks, 0), a1 = kread(ks, 1);
@@ -704,13 +754,14 @@ moda_fwd_bf16_kernel(const Params p) {
   };
   // Generic step (the diagonal block, the segment end, blocks beyond some of the
   // wave's rows): the same loads and barriers as the fast step.
-  auto step = [&](int kb, f32x16(&scur)[2], f32x16(&snext)[2]) MODA_INL {
+  auto step = [&](int i, f32x16(&scur)[2], f32x16(&snext)[2]) MODA_INL {
+    const int kb = bid(i);
     if (kb < n_full) {
-      fast_step(kb, scur, snext);
+      fast_step(i, scur, snext);
       return;
     }
-    issue_group(kb + P);
-    if (kb + 1 < nkb && active(kb + 1)) qk(kst + stage_of(kb + 1) * SM::STAGE, snext);
+    issue_group(i + P);
+    if (i + 1 < nbw && active(bid(i + 1))) qk(kst + stage_of(i + 1) * SM::STAGE, snext);
     if (active(kb)) {
       mask_block(kb, scur);
       const float m_use = max_and_rescale(scur);
@@ -720,24 +771,68 @@ moda_fwd_bf16_kernel(const Params p) {
       for (int q = 0; q < 16; ++q) exp_pair(scur, m_use, q, pp, lsum, rsum);
       l_run += lsum;
       r_run += rsum;
-      const unsigned char* vs = vst + stage_of(kb) * SM::STAGE;
+      const unsigned char* vs = vst + stage_of(i) * SM::STAGE;
 #pragma unroll
-      for (int i = 0; i < NPV; ++i)
-        acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vs, i), pfrag(pp, i), acc[i % DT], 0, 0, 0);
+      for (int j = 0; j < NPV; ++j)
+        acc[j % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vs, j), pfrag(pp, j), acc[j % DT], 0, 0, 0);
     }
     block_end();
   };
-  for (int kb = 0; kb < nkb; kb += 2) {
-    step(kb, sA, sB);
-    if (kb + 1 < nkb) step(kb + 1, sB, sA);
+  for (int i = 0; i < nbw; i += 2) {
+    step(i, sA, sB);
+    if (i + 1 < nbw) step(i + 1, sB, sA);
   }
   // the groups issued past the last block must land before their LDS is reused
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // ---- fold in the depth state of this row ------------------------------------
-  if (MODE == kSerial && !depth_first) {
+  if constexpr (SPLIT) {
+    // finish the depth pass (its own LDS area), then merge the partial states of
+    // waves 1 .. NW - 1 into wave 0's through the (now free) stage bytes
+    if constexpr (MODE == kSerial) {
+      if constexpr (!EARLY_DEPTH) depth_begin();
+      depth_end();
+    }
+    __syncthreads();  // every wave is past its loop: the stages are free, depth rows published
+    float* mg = reinterpret_cast<float*>(smem);  // [NW - 1][64][MG]
+    if (wave > 0) {
+      float* rec = mg + ((wave - 1) * 64 + lane) * SM::MG;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(rec + 16 * dt + 4 * q4) =
+              make_float4(acc[dt][4 * q4], acc[dt][4 * q4 + 1], acc[dt][4 * q4 + 2], acc[dt][4 * q4 + 3]);
+      *reinterpret_cast<float4*>(rec + 16 * DT) = make_float4(m_run, l_run, r_run, 0.f);
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      const float* rec = mg + ((w - 1) * 64 + lane) * SM::MG;
+      const float4 st = *reinterpret_cast<const float4*>(rec + 16 * DT);
+      const float m_new = fmaxf(m_run, st.x);
+      const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+      const float f_a = fast_exp2(m_run - m_use), f_b = fast_exp2(st.x - m_use);
+      l_run = l_run * f_a + st.y * f_b;
+      r_run = r_run * f_a + st.z * f_b;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 x = *reinterpret_cast<const float4*>(rec + 16 * dt + 4 * q4);
+          acc[dt][4 * q4 + 0] = fmaf(x.x, f_b, acc[dt][4 * q4 + 0] * f_a);
+          acc[dt][4 * q4 + 1] = fmaf(x.y, f_b, acc[dt][4 * q4 + 1] * f_a);
+          acc[dt][4 * q4 + 2] = fmaf(x.z, f_b, acc[dt][4 * q4 + 2] * f_a);
+          acc[dt][4 * q4 + 3] = fmaf(x.w, f_b, acc[dt][4 * q4 + 3] * f_a);
+        }
+      m_run = m_new;
+    }
+    if constexpr (MODE == kSerial) depth_fold();
+  } else if (MODE == kSerial && !depth_first) {
     __syncthreads();  // every wave's loads have landed: the K/V area is free
-    depth_pass(wave);
+    depth_begin();
+    depth_end();
     __syncthreads();
     depth_fold();
   }
@@ -775,48 +870,52 @@ moda_fwd_bf16_kernel(const Params p) {
   }
 }
 
-template <int D, int GB, int NW, int MODE>
+template <int D, int GB, int NW, int MODE, bool SPLIT>
 hipError_t launch_t(const Params& p, bool out_f32, hipStream_t stream) {
   const dim3 grid((unsigned)p.n_tiles), block(64 * NW);
   if (out_f32)
-    hipLaunchKernelGGL((moda_fwd_bf16_kernel<D, GB, NW, MODE, true>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((moda_fwd_bf16_kernel<D, GB, NW, MODE, true, SPLIT>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((moda_fwd_bf16_kernel<D, GB, NW, MODE, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((moda_fwd_bf16_kernel<D, GB, NW, MODE, false, SPLIT>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int GB, int NW>
+template <int D, int GB, int NW, bool SPLIT>
 hipError_t launch_d(const Params& p, bool out_f32, hipStream_t stream) {
-  if (p.n_depth == 0) return launch_t<D, GB, NW, kNoDepth>(p, out_f32, stream);
-  return launch_t<D, GB, NW, kSerial>(p, out_f32, stream);
+  if (p.n_depth == 0) return launch_t<D, GB, NW, kNoDepth, SPLIT>(p, out_f32, stream);
+  return launch_t<D, GB, NW, kSerial, SPLIT>(p, out_f32, stream);
 }
 
 template <int D, int GB>
-hipError_t launch_w(const Params& p, int waves, bool out_f32, hipStream_t stream) {
+hipError_t launch_w(const Params& p, int waves, bool split, bool out_f32, hipStream_t stream) {
+  if (split) {
+    if (waves == kSplitWaves<D>) return launch_d<D, GB, kSplitWaves<D>, true>(p, out_f32, stream);
+    return hipErrorInvalidValue;
+  }
   switch (waves) {
-    case 1: return launch_d<D, GB, 1>(p, out_f32, stream);
-    case 2: return launch_d<D, GB, 2>(p, out_f32, stream);
-    case 4: return launch_d<D, GB, 4>(p, out_f32, stream);
+    case 1: return launch_d<D, GB, 1, false>(p, out_f32, stream);
+    case 2: return launch_d<D, GB, 2, false>(p, out_f32, stream);
+    case 4: return launch_d<D, GB, 4, false>(p, out_f32, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t launch_g(const Params& p, int heads_per_block, int waves, bool out_f32, hipStream_t stream) {
+hipError_t launch_g(const Params& p, int heads_per_block, int waves, bool split, bool out_f32, hipStream_t stream) {
   switch (heads_per_block) {
-    case 1: return launch_w<D, 1>(p, waves, out_f32, stream);
-    case 2: return launch_w<D, 2>(p, waves, out_f32, stream);
-    case 4: return launch_w<D, 4>(p, waves, out_f32, stream);
+    case 1: return launch_w<D, 1>(p, waves, split, out_f32, stream);
+    case 2: return launch_w<D, 2>(p, waves, split, out_f32, stream);
+    case 4: return launch_w<D, 4>(p, waves, split, out_f32, stream);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const Params& p, int head_dim, int heads_per_block, int waves, bool out_f32,
+hipError_t launch_fwd_bf16(const Params& p, int head_dim, int heads_per_block, int waves, bool split, bool out_f32,
                            hipStream_t stream) {
-  if (head_dim == 128) return launch_g<128>(p, heads_per_block, waves, out_f32, stream);
-  if (head_dim == 64) return launch_g<64>(p, heads_per_block, waves, out_f32, stream);
+  if (head_dim == 128) return launch_g<128>(p, heads_per_block, waves, split, out_f32, stream);
+  if (head_dim == 64) return launch_g<64>(p, heads_per_block, waves, split, out_f32, stream);
   return hipErrorInvalidValue;
 }
 

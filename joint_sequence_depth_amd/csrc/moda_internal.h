@@ -37,19 +37,26 @@ struct Params {
   int64_t lse_head_stride;    // T (batch layout) or N (packed layout)
   int32_t lse_batch_layout;   // 1: base = s * Hq * T; 0: base = seg_start
   int32_t xcd_interleave;     // 1: (segment, KV head) pairs go round-robin to the 8 XCDs
+  int32_t qb_major;           // 1: tiles ordered by query block across all pairs (heaviest first)
   int32_t serial_order;       // bf16 with depth slots: 0 = depth pass first and last in turn
                               // (by workgroup round), 1 = depth pass first, 2 = last
   int64_t n_tiles;
 };
 
 // Launchers (return the hipError_t of the launch).
-hipError_t launch_fwd_bf16(const Params& p, int head_dim, int heads_per_block, int waves, bool out_f32,
+hipError_t launch_fwd_bf16(const Params& p, int head_dim, int heads_per_block, int waves, bool split, bool out_f32,
                            hipStream_t stream);
 hipError_t launch_fwd_f32(const Params& p, int head_dim, hipStream_t stream);
 
 // Expanded query rows (tokens x grouped heads) per bf16 wave; a workgroup has 1,
 // 2 or 4 waves.
 constexpr int kWaveRows = 32;
+// Waves per workgroup of the split bf16 kernel (they share one 32-row tile and
+// split its key blocks). Their K/V stages take 2 x 2 x 16 KB per wave at D = 128
+// and 2 x 2 x 8 KB at D = 64; two waves keep two workgroups per CU at D = 64, so
+// the small grids run in one round.
+template <int D>
+constexpr int kSplitWaves = 2;
 constexpr int kF32BlockRows = 64;
 
 }  // namespace moda

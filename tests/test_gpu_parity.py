@@ -164,7 +164,35 @@ def test_workload_full_output(name):
 @pytest.mark.parametrize("name", configs.ORDER)
 def test_workload_sampled_rows(name):
     """Full-size workload, launched as the benchmark launches it (bf16 output)."""
-    w = configs.WORKLOADS[name]
+    _sampled_compare(configs.WORKLOADS[name])
+
+
+# Mid-size shapes that reach every tile schedule of the bf16 kernel (the host picks
+# it from the tile count): shared tiles of 4 and 2 waves at both head dims and all
+# head-group widths, and split tiles (waves dividing one tile's key blocks).
+SCHEDULE_CASES = {
+    "shared4_d64": dict(head_dim=64, batch=4, seqlen=2048, n_heads_q=16, n_heads_kv=16, n_depth=8),
+    "shared2_d64": dict(head_dim=64, batch=1, seqlen=2048, n_heads_q=16, n_heads_kv=16, n_depth=8),
+    "split_d64_g2": dict(head_dim=64, batch=1, seqlen=1024, n_heads_q=8, n_heads_kv=4, n_depth=11),
+    "shared2_d128_g4": dict(head_dim=128, batch=1, seqlen=2048, n_heads_q=16, n_heads_kv=4, n_depth=9),
+    "shared4_d128_g2": dict(head_dim=128, batch=2, seqlen=2048, n_heads_q=16, n_heads_kv=8, n_depth=6),
+    "split_d128": dict(head_dim=128, batch=1, seqlen=1500, n_heads_q=4, n_heads_kv=4, n_depth=13),
+}
+
+
+@pytest.mark.parametrize("case", list(SCHEDULE_CASES))
+def test_tile_schedules(case):
+    import bench
+
+    w = workload(dtype="bf16", seed=40 + list(SCHEDULE_CASES).index(case), **SCHEDULE_CASES[case])
+    kern = bench.kernel_name(w)
+    _say(f"{case}: {kern}")
+    assert ("true>" in kern) == case.startswith("split")
+    _sampled_compare(w)
+
+
+def _sampled_compare(w):
+    name = w.name
     _say(f"workload {name}: generating inputs on the device")
     x, out, lse = run_hip(w)
     _, out32, _ = run_hip(w, inputs=x, out_f32=True) if w.bf16 else (None, None, None)
