@@ -37,6 +37,11 @@ def compile_flags():
         "-target-feature",
         "-Xclang",
         "-packed-fp32-ops",
+        # MFMA accumulators in VGPRs: where LDS caps a kernel at one wave per SIMD
+        # the compiler would otherwise place MFMA results in AGPRs and copy every
+        # score back to VGPRs for the softmax
+        "-mllvm",
+        "-amdgpu-mfma-vgpr-form",
         "-Wall",
         "-Wno-unused-function",
         f"-I{INCLUDE}",

@@ -756,7 +756,7 @@ moda_fwd_bf16_kernel(const Params p) {
   // wave's rows): the same loads and barriers as the fast step.
   auto step = [&](int i, f32x16(&scur)[2], f32x16(&snext)[2]) MODA_INL {
     const int kb = bid(i);
-    if (kb < n_full) {
+    if (!SPLIT && kb < n_full) {
       fast_step(i, scur, snext);
       return;
     }
@@ -778,7 +778,25 @@ moda_fwd_bf16_kernel(const Params p) {
     }
     block_end();
   };
-  for (int i = 0; i < nbw; i += 2) {
+  // Split tiles: the fully visible blocks are a prefix of this wave's blocks, so a
+  // loop of fast steps runs first and one of generic steps after it (no path merge
+  // inside either loop: at one wave per SIMD the register allocator otherwise
+  // copies the score vectors at every merge). Shared tiles choose per step (their
+  // register budget is tighter and one loop spills less).
+  const int nfw = SPLIT ? (n_full > wave_u ? (n_full - wave_u + NW - 1) / NW : 0) : 0;
+  const int n_fast = nfw < nbw ? nfw : nbw;
+  int i = 0;
+  for (; i + 1 < n_fast; i += 2) {
+    fast_step(i, sA, sB);
+    fast_step(i + 1, sB, sA);
+  }
+  if (i < n_fast) {  // odd count: one more fast step, then the generic loop starts from sB
+    fast_step(i, sA, sB);
+    ++i;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) sA[st] = sB[st];
+  }
+  for (; i < nbw; i += 2) {
     step(i, sA, sB);
     if (i + 1 < nbw) step(i + 1, sB, sA);
   }
