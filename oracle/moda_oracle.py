@@ -308,3 +308,50 @@ def sequence_only(q, k, v, causal=True, scale=None, cu_seqlens=None):
 def depth_only(q, k, v, k_depth, v_depth, n_depth, scale=None, cu_seqlens=None):
     """Softmax over the row's own depth slots alone (the partial state of the depth blocks)."""
     return joint_attention(q, k, v, k_depth, v_depth, n_depth, True, scale, cu_seqlens, mode="depth")
+
+def decode(q, k_cache, v_cache, cache_seqlens, k_depth, v_depth, n_depth, scale=None):
+    """One new token per sequence (a decode step) in float64. Returns (out, lse).
+
+    The same joint operator as ``joint_attention`` (deck slide "One denominator
+    allocates probability across both memories"), for the one query row of each
+    sequence: the paper's Table 1, as the deck quotes it, names the decode-time
+    sequence cache and depth cache this reads.
+
+    q [B, Hq, d]: the new token's queries. k_cache, v_cache [B, T_max, Hkv, d]:
+    sequence b sees keys/values 0 .. cache_seqlens[b] - 1, the last of them being
+    the new token's own. k_depth, v_depth [B, S_cap, Hkv, d]: the new token's depth
+    slots, of which [0, n_depth) are read. Query head h reads KV head h // G.
+    out [B, Hq, d]; lse [B, Hq] = natural log of the joint denominator.
+
+    Per row the closed form: the maximum over every visible logit, natural
+    exponentials, one sum, one division.
+    """
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    B, Hq, d = q.shape
+    Hkv = kc.shape[2]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kd = _f64(k_depth) if n_depth > 0 else None
+    vd = _f64(v_depth) if n_depth > 0 else None
+    out = np.zeros((B, Hq, d))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        L = int(cache_seqlens[b])
+        for h in range(Hq):
+            hk = h // G
+            a = scale * (kc[b, :L, hk] @ q[b, h])
+            logits = [a]
+            if n_depth > 0:
+                logits.append(scale * (kd[b, :n_depth, hk] @ q[b, h]))
+            M = np.max(np.concatenate(logits))
+            w = np.exp(a - M)
+            num = w @ vc[b, :L, hk]
+            Z = w.sum()
+            if n_depth > 0:
+                u = np.exp(logits[1] - M)
+                num = num + u @ vd[b, :n_depth, hk]
+                Z = Z + u.sum()
+            out[b, h] = num / Z
+            lse[b, h] = M + math.log(Z)
+    return out, lse

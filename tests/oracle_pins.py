@@ -292,6 +292,54 @@ def pin_utilization(orc):
     assert abs(orc.depth_utilization("group", T=0, C=16, G=4, L=2) - 4 / 16) < 1e-15
 
 
+# ---------------------------------------------------------------- decode (one new token per sequence)
+
+
+def _decode_case(seed, B=3, T=11, Hq=4, Hkv=2, d=8, S=3):
+    q, k, v, kd, vd = rand_case(seed, B=B, T=T, Hq=Hq, Hkv=Hkv, d=d, S=S)
+    ts = np.array([T - 1, 0, T // 2])[:B]  # the decoded token of each sequence
+    b = np.arange(B)
+    return q, k, v, kd, vd, ts, q[b, ts], kd[b, ts], vd[b, ts]
+
+
+def pin_decode_is_last_row(orc):
+    """A decode step at position t equals row t of the full causal forward (the
+    cache prefix 0..t holds the token's own key)."""
+    q, k, v, kd, vd, ts, qt, kdt, vdt = _decode_case(21)
+    o_full, l_full = orc.joint_attention(q, k, v, kd, vd, 3, causal=True)
+    o, l = orc.decode(qt, k, v, ts + 1, kdt, vdt, 3)
+    for b, t in enumerate(ts):
+        assert np.abs(o[b] - o_full[b, t]).max() < 1e-12
+        assert np.abs(l[b] - l_full[b, :, t]).max() < 1e-12
+
+
+def pin_decode_empty_depth_is_sdpa(orc):
+    """No depth slots: ordinary attention of one query row over the cache prefix
+    (torch's scaled_dot_product_attention, float64)."""
+    q, k, v, kd, vd, ts, qt, kdt, vdt = _decode_case(22)
+    o, _ = orc.decode(qt, k, v, ts + 1, kdt, vdt, 0)
+    G = qt.shape[1] // k.shape[2]
+    for b, t in enumerate(ts):
+        L = int(t) + 1
+        qq = torch.from_numpy(qt[b][:, None, :].copy())                       # [Hq, 1, d]
+        kk = torch.from_numpy(np.repeat(k[b, :L].transpose(1, 0, 2), G, axis=0).copy())  # [Hq, L, d]
+        vv = torch.from_numpy(np.repeat(v[b, :L].transpose(1, 0, 2), G, axis=0).copy())
+        ref = F.scaled_dot_product_attention(qq, kk, vv).numpy()[:, 0]
+        assert np.abs(o[b] - ref).max() < 1e-12
+
+
+def pin_decode_single_key(orc):
+    """One cached key and no slots: the output is that key's value and lse its
+    logit (closed form)."""
+    q, k, v, kd, vd, ts, qt, kdt, vdt = _decode_case(23, Hq=2, Hkv=1, d=5)
+    o, l = orc.decode(qt, k, v, np.ones(3, dtype=np.int32), kdt, vdt, 0)
+    scale = 1.0 / math.sqrt(5)
+    for b in range(3):
+        for h in range(2):
+            assert np.abs(o[b, h] - v[b, 0, 0]).max() < 1e-14
+            assert abs(l[b, h] - scale * float(q[b, ts[b], h] @ k[b, 0, 0])) < 1e-12
+
+
 ALL_PINS = [
     pin_empty_depth_is_sdpa,
     pin_equal_logits_plain_mean,
@@ -309,4 +357,7 @@ ALL_PINS = [
     pin_index_map_example,
     pin_expanded_rows_equal,
     pin_utilization,
+    pin_decode_is_last_row,
+    pin_decode_empty_depth_is_sdpa,
+    pin_decode_single_key,
 ]

@@ -30,6 +30,10 @@ MUTANTS = {
         "M = np.max(parts_logit[0], axis=1)",
     ),
     "depth_value_of_other_head": ("Vd = vdp[st:en, :n_depth, hk]", "Vd = vdp[st:en, :n_depth, (hk + 1) % Hkv]"),
+    "decode_prefix_off_by_one": ("L = int(cache_seqlens[b])", "L = int(cache_seqlens[b]) - 1"),
+    "decode_group_map": ("hk = h // G\n            a = scale", "hk = h % Hkv\n            a = scale"),
+    "decode_depth_logit_unscaled": ("logits.append(scale * (kd[b", "logits.append((kd[b"),
+    "decode_depth_keys_as_values": ("num = num + u @ vd[b, :n_depth, hk]", "num = num + u @ kd[b, :n_depth, hk]"),
 }
 
 
