@@ -17,6 +17,7 @@ workload (HBM bytes or bf16 MFMA FLOPs, whichever takes longer at peak).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -34,12 +35,14 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector
 CACHE_DEFEAT_BYTES = 768 << 20  # > 256 MB Infinity Cache + 8 x 4 MB L2
-KERNEL_SOURCES = ["moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_attn.hip", "moda_internal.h"]
+KERNEL_SOURCES = ["moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_attn.hip", "moda_internal.h"]  # the forward path
+DECODE_SOURCES = ["moda_decode.hip", "moda_attn.hip", "moda_internal.h"]
+DECODE_METRIC = "MoDA decode step (joint seq+depth softmax, one token per sequence) HBM GB/s"
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(sources=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "joint_sequence_depth_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -49,6 +52,10 @@ def kernel_name(w) -> str:
     """The kernel instance the library launches for this workload (mirrors the
     host dispatch: heads per workgroup, waves per workgroup, depth schedule,
     shared or split tiles)."""
+    if _is_decode(w):
+        G = w.group
+        gd = next(g for g in (8, 4, 2, 1) if G % g == 0)
+        return f"moda_decode_partial_kernel<{w.head_dim}, {gd}, {str(w.bf16).lower()}>"
     if not w.bf16:
         return f"moda_fwd_f32_kernel<{w.head_dim}>"
     G = w.group
@@ -66,6 +73,20 @@ def kernel_name(w) -> str:
         waves, split = 2, True
     mode = 0 if w.n_depth == 0 else 1
     return f"moda_fwd_bf16_kernel<{w.head_dim}, {gb}, {waves}, {mode}, false, {str(split).lower()}>"
+
+
+def _is_decode(w) -> bool:
+    from workloads import configs
+
+    return isinstance(w, configs.DecodeWorkload)
+
+
+def _sources(w):
+    return DECODE_SOURCES if _is_decode(w) else KERNEL_SOURCES
+
+
+def _summary_prefix(w) -> str:
+    return "moda_decode" if _is_decode(w) else "moda_fwd"
 
 
 def roofline(w, sec_per_launch: float) -> dict:
@@ -91,7 +112,7 @@ def traffic_from_profile(w, algorithmic_bytes):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha") != kernel_source_sha():
+    if rec.get("kernel_source_sha") != kernel_source_sha(_sources(w)):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -130,9 +151,14 @@ def write_traffic(w, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cmds)
     scale_w = copy_bytes / (w_c * 1024.0)
     rd = f_k * 1024.0 * scale_f
     wr = w_k * 1024.0 * scale_w
-    alg_rd = w.total_bytes() - w.n_tokens * w.n_heads_q * (w.head_dim * w.elem_bytes() + 4)
-    alg_wr = w.total_bytes() - alg_rd
-    rec = {"workload": w.name, "kernel": kernel_name(w), "kernel_source_sha": kernel_source_sha(),
+    if _is_decode(w):  # the partial kernel: reads q, the visible cache rows and the depth slots once
+        alg_rd = w.cache_bytes() + w.depth_bytes() + w.batch * w.n_heads_q * w.head_dim * w.elem_bytes()
+        alg_wr = 0.0  # its writes are the chunk states in the workspace, not part of the operator's output
+    else:
+        alg_rd = w.total_bytes() - w.n_tokens * w.n_heads_q * (w.head_dim * w.elem_bytes() + 4)
+        alg_wr = w.total_bytes() - alg_rd
+    sha = kernel_source_sha(_sources(w))
+    rec = {"workload": w.name, "kernel": kernel_name(w), "kernel_source_sha": sha,
            "hbm_bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
            "algorithmic_read_bytes": alg_rd, "algorithmic_write_bytes": alg_wr,
            "fetch_size_kib": f_k, "write_size_kib": w_k, "dispatches": [n_fk, n_wk],
@@ -149,11 +175,17 @@ def write_traffic(w, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cmds)
               f"{scale_f:.4f} (reads) and {scale_w:.4f} (writes) turn counter KiB into bytes.", "",
               "| per launch | counter (KiB) | scaled bytes | algorithmic bytes | ratio |", "|---|---|---|---|---|",
               f"| read | {f_k:.1f} | {rd / 1e6:.2f} MB | {alg_rd / 1e6:.2f} MB | {rd / alg_rd:.3f} |",
-              f"| write | {w_k:.1f} | {wr / 1e6:.2f} MB | {alg_wr / 1e6:.2f} MB | {wr / alg_wr:.3f} |",
-              f"| total | | {(rd + wr) / 1e6:.2f} MB | {w.total_bytes() / 1e6:.2f} MB | {(rd + wr) / w.total_bytes():.3f} |",
-              "", f"Means over {n_fk} and {n_wk} dispatches; kernel sources sha {kernel_source_sha()}.",
-              "Algorithmic reads: q, k, v and the depth K/V rows once; writes: out and lse once."]
-    with open(os.path.join(ROOT, "profiles", f"moda_fwd_{w.name}_hbm_counters.txt"), "w") as f:
+              f"| write | {w_k:.1f} | {wr / 1e6:.2f} MB | {alg_wr / 1e6:.2f} MB | "
+              f"{(wr / alg_wr if alg_wr else float('nan')):.3f} |",
+              f"| total | | {(rd + wr) / 1e6:.2f} MB | {(alg_rd + alg_wr) / 1e6:.2f} MB | "
+              f"{(rd + wr) / (alg_rd + alg_wr):.3f} |",
+              "", f"Means over {n_fk} and {n_wk} dispatches; kernel sources sha {sha}."]
+    if _is_decode(w):
+        lines.append("Algorithmic reads: q, the visible cache K/V rows and the depth K/V slots once; the kernel's "
+                     "writes are the per-chunk fp32 states that the merge kernel reads.")
+    else:
+        lines.append("Algorithmic reads: q, k, v and the depth K/V rows once; writes: out and lse once.")
+    with open(os.path.join(ROOT, "profiles", f"{_summary_prefix(w)}_{w.name}_hbm_counters.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
@@ -171,6 +203,12 @@ def write_trace_summary(w, trace_dir, log_path, cmd) -> None:
         raise SystemExit(f"kernel {kname} or the bench line missing in {trace_dir}")
     avg_us = float(row["AverageNs"]) / 1e3
     bench_us = bench_line["ms_per_step"] * 1e3
+    step_us = avg_us
+    if _is_decode(w):  # a decode step is the partial kernel and the merge kernel
+        merge = next((r for r in stats if "moda_decode_merge_kernel" in r["Name"]), None)
+        if merge is None:
+            raise SystemExit(f"merge kernel missing in {trace_dir}")
+        step_us += float(merge["AverageNs"]) / 1e3
     lines = [f"# rocprofv3 kernel trace: {kname} on {w.name} ({w.desc})", "",
              "Command (on the GPU host; R = repository root):", f"    {cmd}", "",
              "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
@@ -180,12 +218,13 @@ def write_trace_summary(w, trace_dir, log_path, cmd) -> None:
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} "
                      f"| {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} % |")
     lines += ["", f"bench.py (same run, HIP events over {bench_line['steps']} graph-replayed steps): "
-                  f"{bench_us:.2f} us per step; trace average {avg_us:.2f} us "
-                  f"({100 * (bench_us / avg_us - 1):+.1f} %).",
+                  f"{bench_us:.2f} us per step; trace average {step_us:.2f} us "
+                  + ("(partial + merge kernels) " if _is_decode(w) else "")
+                  + f"({100 * (bench_us / step_us - 1):+.1f} %).",
               f"value {bench_line['value']} {bench_line['unit']}; roofline {bench_line['roofline']['bound']} "
               f"{bench_line['roofline']['achieved']:.1f} {bench_line['roofline']['unit']} "
               f"(frac {bench_line['roofline']['frac']:.3f}); kernel sources sha {bench_line['kernel_source_sha']}."]
-    with open(os.path.join(ROOT, "profiles", f"moda_fwd_{w.name}_kernel_trace.txt"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"{_summary_prefix(w)}_{w.name}_kernel_trace.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
@@ -245,6 +284,185 @@ def cpu_baseline(w, budget_s: float) -> dict:
                       "generation not timed)"}
 
 
+def cpu_baseline_decode(w, budget_s: float) -> dict:
+    """The fp64 oracle's decode on whole sequences of the workload (operands
+    regenerated on the host, not timed), cycled until about ``budget_s`` seconds."""
+    import numpy as np
+
+    import oracle
+    from workloads import configs
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [cores])
+    except Exception:
+        pass
+    d, S, Hkv = w.head_dim, w.n_depth, w.n_heads_kv
+    c = np.arange(d)
+    prepared = []
+    t_start = time.perf_counter()
+    for b in range(w.batch):
+        L = w.cache_lengths[b]
+        q = configs.decode_host_slice(w, "q", np.ix_([b], np.arange(w.n_heads_q), c))
+        kidx = np.ix_([b], np.arange(L), np.arange(Hkv), c)
+        k = configs.decode_host_slice(w, "k", kidx)
+        v = configs.decode_host_slice(w, "v", kidx)
+        if S > 0:
+            didx = np.ix_([b], np.arange(S), np.arange(Hkv), c)
+            kd, vd = configs.decode_host_slice(w, "kd", didx), configs.decode_host_slice(w, "vd", didx)
+        else:
+            kd = vd = None
+        nbytes = 2.0 * (L + S) * Hkv * d * w.elem_bytes() + w.n_heads_q * d * (w.elem_bytes() + 2) + 4 * w.n_heads_q
+        prepared.append((q, k, v, kd, vd, np.array([L]), nbytes))
+        if time.perf_counter() - t_start > budget_s:
+            break
+    done, nbytes_total, compute_s, calls = 0, 0.0, 0.0, 0
+    while compute_s < budget_s:
+        q, k, v, kd, vd, lens, nbytes = prepared[calls % len(prepared)]
+        t0 = time.perf_counter()
+        oracle.decode(q, k, v, lens, kd, vd, S, w.scale)
+        compute_s += time.perf_counter() - t0
+        nbytes_total += nbytes
+        calls += 1
+    done = len(prepared)
+    return {"value": nbytes_total / compute_s / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{calls} oracle decode calls over {done} of the {w.batch} sequences of {w.name} "
+                      f"({nbytes_total / 1e9:.2f} GB of operand bytes in {compute_s:.1f} s; operands regenerated "
+                      "on the host, generation not timed)"}
+
+
+def bench_decode(args, w, dev) -> int:
+    """One step = one decode call (partial + merge kernels) for every sequence of
+    the workload, inputs resident in HBM, cycling through enough input batches to
+    defeat the Infinity Cache, replayed as a HIP graph."""
+    import torch
+
+    from joint_sequence_depth_amd import attn_decode, decode_workspace_size
+    from workloads import configs
+
+    batch_bytes = w.total_bytes()
+    n_batches = max(1, min(32, math.ceil(CACHE_DEFEAT_BYTES / batch_bytes)))
+    print(f"# workload {w.name}: {w.desc}; {n_batches} input batch(es) of {batch_bytes / 1e6:.1f} MB", file=sys.stderr,
+          flush=True)
+    inputs = []
+    for i in range(n_batches):
+        wi = dataclasses.replace(w, seed=w.seed + 1000 * i)
+        inputs.append(configs.make_decode_device(wi, dev))
+    odt = torch.bfloat16 if w.bf16 else torch.float32
+    outs = [torch.empty(w.shape_q(), dtype=odt, device=dev) for _ in range(n_batches)]
+    lses = [torch.empty((w.batch, w.n_heads_q), dtype=torch.float32, device=dev) for _ in range(n_batches)]
+    ws = torch.empty(decode_workspace_size(w.batch, w.n_heads_q, w.n_heads_kv, w.head_dim, w.max_cache_len),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        x = inputs[i % n_batches]
+        attn_decode(x["q"], x["k"], x["v"], x["seqlens"], x["kd"], x["vd"], n_depth=w.n_depth, scale=w.scale,
+                    out=outs[i % n_batches], lse=lses[i % n_batches], workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_batches):
+        step(i)
+    torch.cuda.synchronize()
+    rough = (time.perf_counter() - t0) / n_batches
+    steps = args.steps or max(n_batches, int(1.0 / max(rough, 1e-6)))
+    steps = max(n_batches, (steps // n_batches) * n_batches)
+
+    stream = torch.cuda.current_stream(dev)
+    use_graph = not args.no_graph
+    graph = None
+    if use_graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n_batches):
+                step(i)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    if use_graph:
+        for _ in range(steps // n_batches):
+            graph.replay()
+    else:
+        for i in range(steps):
+            step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    sec = ms / 1e3
+
+    # the last replayed batch's results must equal an eager call (bitwise)
+    last = (steps - 1) % n_batches
+    ref_out, ref_lse = torch.empty_like(outs[0]), torch.empty_like(lses[0])
+    x = inputs[last]
+    attn_decode(x["q"], x["k"], x["v"], x["seqlens"], x["kd"], x["vd"], n_depth=w.n_depth, scale=w.scale,
+                out=ref_out, lse=ref_lse, workspace=ws)
+    torch.cuda.synchronize()
+    replay_ok = bool(torch.equal(ref_out, outs[last]) and torch.equal(ref_lse, lses[last]))
+    if not replay_ok:
+        print("error: timed replays differ from an eager call", file=sys.stderr)
+
+    nbytes = w.total_bytes(out_bytes=w.elem_bytes())
+    gbs = nbytes / sec / 1e9
+    rec = {
+        "metric": DECODE_METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.bf16 else "f32",
+        "data": "synthetic (seeded counter-based N(0,1) quantile grid)",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "cache_lengths": list(w.cache_lengths),
+            "max_cache_len": w.max_cache_len,
+            "n_heads_q": w.n_heads_q,
+            "n_heads_kv": w.n_heads_kv,
+            "head_dim": w.head_dim,
+            "n_depth": w.n_depth,
+            "input_batches": n_batches,
+            "graph": use_graph,
+        },
+        "parts": {
+            "tflops": round(w.flops() / sec / 1e12, 3),
+            "cache_kv_gbs": round(w.cache_bytes() / sec / 1e9, 1),
+            "depth_kv_gbs": round(w.depth_bytes() / sec / 1e9, 1),
+        },
+        "kernel": kernel_name(w),
+        "kernel_source_sha": kernel_source_sha(DECODE_SOURCES),
+        "replay_matches_eager": replay_ok,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": traffic_from_profile(w, nbytes)},
+        "cpu_baseline": None,
+    }
+    del inputs, outs, lses, graph, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_decode(w, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0 if replay_ok else 1
+
+
 def _lead_index(w, s, L):
     import numpy as np
 
@@ -284,7 +502,7 @@ def main(argv=None) -> int:
     if args.summarize_trace or args.write_traffic:
         from workloads import configs
 
-        w = configs.WORKLOADS[args.workload]
+        w = configs.WORKLOADS.get(args.workload) or configs.DECODE_WORKLOADS[args.workload]
         if args.summarize_trace:
             write_trace_summary(w, args.summarize_trace[0], args.summarize_trace[1], " ".join(args.profile_cmd))
         if args.write_traffic:
@@ -320,6 +538,8 @@ def main(argv=None) -> int:
     from workloads import configs
 
     lib()  # fail loudly before any work if the HIP library is missing
+    if args.workload in configs.DECODE_WORKLOADS:
+        return bench_decode(args, configs.DECODE_WORKLOADS[args.workload], dev)
     w = configs.WORKLOADS[args.workload]
     batch_bytes = w.total_bytes()
     n_batches = max(1, min(32, math.ceil(CACHE_DEFEAT_BYTES / batch_bytes)))

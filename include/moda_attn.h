@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MODA_ABI_VERSION 1
+#define MODA_ABI_VERSION 2
 
 /* status codes */
 #define MODA_OK 0
@@ -97,6 +97,42 @@ int moda_attn_fwd_varlen(const void* q, const void* k, const void* v, const void
                          const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen,
                          int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
                          int32_t n_depth, int32_t causal, float scale, void* stream);
+
+/*
+ * One decode step: a single new token per sequence attends, through the same
+ * joint softmax, to its sequence-cache prefix and to its own depth slots (the
+ * decode-time sequence and depth caches of the paper's Table 1, as the MoDA deck
+ * quotes it on slide "Depth compute still accumulates quadratically in depth").
+ *
+ *   q          [B, Hq, d]              the new tokens' queries
+ *   k_cache,
+ *   v_cache    [B, T_max, Hkv, d]      sequence b reads rows 0 .. cache_seqlens[b] - 1;
+ *                                      the last of them is the new token's own key/value
+ *   k_depth,
+ *   v_depth    [B, S_cap, Hkv, d]      the new token's depth slots; [0, n_depth) are read
+ *   out        [B, Hq, d] (out_dtype)  lse [B, Hq] float32 (may be NULL)
+ *   cache_seqlens: DEVICE pointer to B int32 lengths in [1, T_max] (T_max =
+ *   max_cache_len); values outside are clamped to that range on the device.
+ *
+ * dtype pairs, head_dim, grouping and scale as for moda_attn_fwd. The causal
+ * mask is implied (the cache prefix is the visible set).
+ *
+ * workspace: DEVICE memory of at least moda_attn_decode_workspace_size(...)
+ * bytes, 16-byte aligned, owned by the caller; it holds fp32 partial states of
+ * the key chunks between the two kernels of the step, its contents on entry do
+ * not matter, and calls that share one workspace must not overlap. The call
+ * launches both kernels on `stream` and returns without waiting.
+ * Returns MODA_OK or an error code (MODA_ERR_SHAPE also for a too small workspace).
+ */
+int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, const void* k_depth,
+                     const void* v_depth, void* out, float* lse, int32_t dtype, int32_t out_dtype,
+                     const int32_t* cache_seqlens, int64_t batch, int32_t max_cache_len, int32_t n_heads_q,
+                     int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t n_depth, float scale,
+                     void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes moda_attn_decode needs for these sizes, or -1 for invalid sizes. */
+int64_t moda_attn_decode_workspace_size(int64_t batch, int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                                        int32_t max_cache_len);
 
 /* Description of the last non-OK status returned on the calling thread ("" if none). */
 const char* moda_last_error(void);

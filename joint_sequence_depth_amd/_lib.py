@@ -29,7 +29,8 @@ STATUS_NAMES = {
 }
 
 # every symbol include/moda_attn.h declares
-EXPORTS = ("moda_attn_fwd", "moda_attn_fwd_varlen", "moda_last_error", "moda_abi_version")
+EXPORTS = ("moda_attn_fwd", "moda_attn_fwd_varlen", "moda_attn_decode", "moda_attn_decode_workspace_size",
+           "moda_last_error", "moda_abi_version")
 
 _lib = None
 
@@ -55,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.moda_attn_fwd.restype = ctypes.c_int
         L.moda_attn_fwd_varlen.argtypes = [vp] * 7 + [i32, i32, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32, f32, vp]
         L.moda_attn_fwd_varlen.restype = ctypes.c_int
+        L.moda_attn_decode.argtypes = [vp] * 7 + [i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp, i64, vp]
+        L.moda_attn_decode.restype = ctypes.c_int
+        L.moda_attn_decode_workspace_size.argtypes = [i64, i32, i32, i32, i32]
+        L.moda_attn_decode_workspace_size.restype = ctypes.c_int64
         L.moda_last_error.argtypes = []
         L.moda_last_error.restype = ctypes.c_char_p
         L.moda_abi_version.argtypes = []
@@ -180,5 +185,92 @@ def attn_fwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(k_depth), _ptr(v_depth), _ptr(out), _ptr(lse),
             code, out_code, q.shape[0], q.shape[1], Hq, Hkv, d, s_cap, int(n_depth), int(bool(causal)), float(scale), stream,
         )
+    _check(status)
+    return out, lse
+
+
+def decode_workspace_size(batch: int, n_heads_q: int, n_heads_kv: int, head_dim: int, max_cache_len: int) -> int:
+    """Bytes of device workspace one decode call with these sizes needs."""
+    n = lib().moda_attn_decode_workspace_size(batch, n_heads_q, n_heads_kv, head_dim, max_cache_len)
+    if n < 0:
+        raise ValueError("invalid decode sizes")
+    return int(n)
+
+
+def attn_decode(
+    q,
+    k_cache,
+    v_cache,
+    cache_seqlens,
+    k_depth=None,
+    v_depth=None,
+    n_depth: Optional[int] = None,
+    scale: Optional[float] = None,
+    out=None,
+    lse=None,
+    workspace=None,
+    stream=None,
+    out_dtype=None,
+    return_lse: bool = True,
+):
+    """One decode step through the C ABI: q [B,Hq,d] (one new token per sequence),
+    k_cache/v_cache [B,T_max,Hkv,d] with cache_seqlens (int32 [B] on the device)
+    valid rows each (the last being the new token's own), k_depth/v_depth
+    [B,S_cap,Hkv,d] the new token's depth slots. Returns (out [B,Hq,d], lse
+    float32 [B,Hq]). ``workspace`` (a uint8 device tensor) is allocated here when
+    not given; pass one to keep the call allocation-free."""
+    import torch
+
+    for t in (q, k_cache, v_cache, cache_seqlens, k_depth, v_depth, out, lse, workspace):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if t is not None and t.device.type != "cuda":
+            raise ValueError("all tensors must be on the GPU")
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B,Hq,d] and the caches [B,T_max,Hkv,d]")
+    B, Hq, d = q.shape
+    T_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} cache{tuple(k_cache.shape)}")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    if cache_seqlens.dtype != torch.int32 or tuple(cache_seqlens.shape) != (B,):
+        raise ValueError("cache_seqlens must be int32 [B] on the device")
+    if k_depth is not None:
+        if v_depth is None or k_depth.shape != v_depth.shape or k_depth.dim() != 4:
+            raise ValueError("k_depth and v_depth must both be [B,S_cap,Hkv,d]")
+        if k_depth.shape[0] != B or k_depth.shape[2:] != (Hkv, d):
+            raise ValueError(f"depth tensors must be [B,S_cap,Hkv,d], got {tuple(k_depth.shape)}")
+        if k_depth.dtype != q.dtype or v_depth.dtype != q.dtype:
+            raise TypeError("depth tensors must share q's dtype")
+        s_cap = k_depth.shape[1]
+    else:
+        s_cap = 0
+    if n_depth is None:
+        n_depth = s_cap
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else q.dtype
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype:
+        raise ValueError("out must have q's shape and out_dtype")
+    if not return_lse:
+        lse = None
+    elif lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    elif tuple(lse.shape) != (B, Hq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq]")
+    if workspace is None:
+        n = decode_workspace_size(B, Hq, Hkv, d, T_max) if B > 0 else 0
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    status = lib().moda_attn_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_depth), _ptr(v_depth), _ptr(out), _ptr(lse),
+        _dtype_code(q), _dtype_code(out), _ptr(cache_seqlens), B, T_max, Hq, Hkv, d, s_cap, int(n_depth),
+        float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), stream,
+    )
     _check(status)
     return out, lse

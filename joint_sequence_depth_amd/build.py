@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmoda_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["moda_attn.hip", "moda_fwd_bf16.hip", "moda_fwd_f32.hip"]
+SOURCES = ["moda_attn.hip", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_decode.hip"]
 ARCH = "gfx950"
 
 

@@ -131,6 +131,33 @@ int dispatch(moda::Params& p, const Common& c, int64_t n_seg, int64_t max_len, h
   return MODA_OK;
 }
 
+// ---- decode ---------------------------------------------------------------------
+// Query heads per decode workgroup: the largest of 8, 4, 2, 1 dividing G.
+int decode_heads_per_block(int G) {
+  for (int g = 8; g > 1; g /= 2)
+    if (G % g == 0) return g;
+  return 1;
+}
+
+// Cache rows per chunk: enough chunks for about 1024 workgroups, each a whole
+// number of the partial kernel's load rounds. Shared by the call and the
+// workspace-size query, so both see the same chunk count.
+int64_t decode_chunk(int64_t batch, int Hq, int Hkv, int d, int64_t T_max) {
+  const int64_t unit = moda::decode_rows_per_chunk_unit(d);
+  int64_t units = batch * Hkv * (int64_t)((Hq / Hkv) / decode_heads_per_block(Hq / Hkv));
+  if (units < 1) units = 1;
+  int64_t want = units >= 1024 ? 1 : (1024 + units - 1) / units;
+  int64_t chunk = (T_max + want - 1) / want;
+  chunk = (chunk + unit - 1) / unit * unit;
+  return chunk < unit ? unit : chunk;
+}
+
+int64_t decode_workspace_bytes(int64_t batch, int Hq, int Hkv, int d, int64_t T_max) {
+  const int64_t chunk = decode_chunk(batch, Hq, Hkv, d, T_max);
+  const int64_t n_chunks = (T_max + chunk - 1) / chunk + 1;
+  return batch * Hq * n_chunks * (int64_t)(d + 4) * 4;
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,6 +212,71 @@ int moda_attn_fwd_varlen(const void* q, const void* k, const void* v, const void
   p.lse_head_stride = total_tokens;
   p.lse_batch_layout = 0;
   return dispatch(p, c, n_seqs, max_seqlen, static_cast<hipStream_t>(stream));
+}
+
+int64_t moda_attn_decode_workspace_size(int64_t batch, int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                                        int32_t max_cache_len) {
+  if (batch < 0 || n_heads_q < 1 || n_heads_kv < 1 || n_heads_q % n_heads_kv != 0 || max_cache_len < 1 ||
+      (head_dim != 64 && head_dim != 128))
+    return -1;
+  return decode_workspace_bytes(batch, n_heads_q, n_heads_kv, head_dim, max_cache_len);
+}
+
+int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, const void* k_depth,
+                     const void* v_depth, void* out, float* lse, int32_t dtype, int32_t out_dtype,
+                     const int32_t* cache_seqlens, int64_t batch, int32_t max_cache_len, int32_t n_heads_q,
+                     int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t n_depth, float scale,
+                     void* workspace, int64_t workspace_bytes, void* stream) {
+  if (batch < 0) return fail(MODA_ERR_SHAPE, "batch must be >= 0");
+  const Common c{q,        k_cache,    v_cache,  k_depth,        v_depth, out,     lse,   dtype,
+                 out_dtype, n_heads_q, n_heads_kv, head_dim, depth_capacity, n_depth, 1,     scale};
+  if (batch == 0) {
+    g_err[0] = '\0';
+    return MODA_OK;
+  }
+  const int rc = check_common(c);
+  if (rc != MODA_OK) return rc;
+  if (max_cache_len < 1) return fail(MODA_ERR_SHAPE, "max_cache_len must be >= 1");
+  if (!cache_seqlens) return fail(MODA_ERR_NULL, "cache_seqlens must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(cache_seqlens) & 3u) return fail(MODA_ERR_ALIGN, "cache_seqlens must be 4-byte aligned");
+  if (batch > 0x7fffffffLL) return fail(MODA_ERR_SHAPE, "batch too large");
+  const int64_t need = decode_workspace_bytes(batch, n_heads_q, n_heads_kv, head_dim, max_cache_len);
+  if (!workspace) return fail(MODA_ERR_NULL, "workspace must be non-NULL");
+  if (!aligned16(workspace)) return fail(MODA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(MODA_ERR_SHAPE, "workspace too small: %lld bytes given, %lld needed", (long long)workspace_bytes,
+                (long long)need);
+  moda::DecodeParams p{};
+  p.q = q;
+  p.kc = k_cache;
+  p.vc = v_cache;
+  p.kd = n_depth > 0 ? k_depth : nullptr;
+  p.vd = n_depth > 0 ? v_depth : nullptr;
+  p.out = out;
+  p.lse = lse;
+  p.cache_seqlens = cache_seqlens;
+  p.workspace = static_cast<float*>(workspace);
+  p.B = batch;
+  p.T_max = max_cache_len;
+  p.Hq = n_heads_q;
+  p.Hkv = n_heads_kv;
+  p.G = n_heads_q / n_heads_kv;
+  const int gd = decode_heads_per_block(p.G);
+  p.n_hgroups = p.G / gd;
+  p.S_cap = depth_capacity;
+  p.n_depth = n_depth;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.chunk = decode_chunk(batch, n_heads_q, n_heads_kv, head_dim, max_cache_len);
+  p.n_seq_chunks = (int32_t)((max_cache_len + p.chunk - 1) / p.chunk);
+  p.n_chunks = p.n_seq_chunks + 1;
+  p.n_partial_blocks = batch * n_heads_kv * p.n_hgroups * p.n_chunks;
+  if (p.n_partial_blocks > 0x7fffffffLL || batch * n_heads_q > 0x7fffffffLL)
+    return fail(MODA_ERR_SHAPE, "problem too large for one launch");
+  const hipError_t err = moda::launch_decode(p, head_dim, gd, dtype == MODA_DTYPE_BF16, out_dtype == MODA_DTYPE_F32,
+                                             static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(MODA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  g_err[0] = '\0';
+  return MODA_OK;
 }
 
 const char* moda_last_error(void) { return g_err; }

@@ -1,0 +1,359 @@
+// MoDA joint sequence/depth attention for a decode step: one new token per
+// sequence attends to its sequence-cache prefix and to its own depth slots
+// through ONE softmax (MoDA, arXiv 2603.15619; deck slide "One denominator
+// allocates probability across both memories"; the decode caches are those of the
+// paper's Table 1 as the deck quotes it).
+//
+// With one query row per (sequence, head) there is no matrix product to feed the
+// matrix cores: each key row is read once and dotted with the GD query heads that
+// share its KV head, so the step is bound by HBM (G flops per byte). Two kernels:
+//
+//  * partial: a workgroup of DW waves per (sequence, KV head, head group, key
+//    chunk). LPR = D / 8 lanes hold one 8-element slice of a key row, so one
+//    wave-wide load covers NGRP = 64 / LPR rows; each lane group keeps, per head,
+//    the running max (base 2), the running sum and its slice of the weighted value
+//    sum, loads U rows ahead of the arithmetic in registers, and the lane groups
+//    and waves merge by the online-softmax update at the end. The depth slots of
+//    the token have the same row stride as the cache (H_kv d elements), so they are
+//    one more chunk. Partial states go to the caller's workspace.
+//  * merge: per (sequence, query head) the chunks' states merge into the output
+//    and the natural-log lse, normalised once.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moda_internal.h"
+
+namespace moda {
+namespace {
+
+typedef __bf16 dbf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr int kDecWaves = 4;  // waves per partial workgroup
+constexpr int kDecU = 4;      // key rows per lane group per load batch
+
+__device__ __forceinline__ float d_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float d_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float d_dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dbf16x2, a), __builtin_bit_cast(dbf16x2, b), c, false);
+}
+
+// 8 consecutive elements of a row, as stored (bf16: one 16-byte word; fp32: two).
+template <bool BF16>
+struct Slice {
+  uint4 w[BF16 ? 1 : 2];
+};
+template <bool BF16>
+__device__ __forceinline__ Slice<BF16> load_slice(const void* base, int64_t elem) {
+  Slice<BF16> s;
+  if constexpr (BF16) {
+    s.w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem);
+    s.w[0] = p[0];
+    s.w[1] = p[1];
+  }
+  return s;
+}
+template <bool BF16>
+__device__ __forceinline__ float elem(const Slice<BF16>& s, int i) {
+  if constexpr (BF16) {
+    const uint32_t w = i < 2 ? s.w[0].x : i < 4 ? s.w[0].y : i < 6 ? s.w[0].z : s.w[0].w;
+    return (i & 1) ? d_hi(w) : d_lo(w);
+  } else {
+    const uint4 q = s.w[i >> 2];
+    const uint32_t w = (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
+    return __uint_as_float(w);
+  }
+}
+// <q slice, k slice> in fp32
+template <bool BF16>
+__device__ __forceinline__ float dot8(const Slice<BF16>& q, const Slice<BF16>& k) {
+  if constexpr (BF16) {
+    float s = d_dot2(q.w[0].x, k.w[0].x, 0.f);
+    s = d_dot2(q.w[0].y, k.w[0].y, s);
+    s = d_dot2(q.w[0].z, k.w[0].z, s);
+    return d_dot2(q.w[0].w, k.w[0].w, s);
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = fmaf(elem<false>(q, i), elem<false>(k, i), s);
+    return s;
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float d_dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// sum over aligned groups of LPR lanes; every lane of a group ends with the same bits
+template <int LPR>
+__device__ __forceinline__ float d_group_sum(float s) {
+  s += d_dpp<0xB1>(s);
+  s += d_dpp<0x4E>(s);
+  s += d_dpp<0x141>(s);
+  if constexpr (LPR == 16) s += d_dpp<0x140>(s);
+  return s;
+}
+
+// Merges running state (mb, lb, ob) into (ma, la, oa), base-2 units.
+__device__ __forceinline__ void merge_state(float& ma, float& la, float (&oa)[8], float mb, float lb,
+                                            const float (&ob)[8]) {
+  const float m = fmaxf(ma, mb);
+  const float mu = m == kNegInf ? 0.f : m;
+  const float fa = __builtin_amdgcn_exp2f(ma - mu), fb = __builtin_amdgcn_exp2f(mb - mu);
+  la = la * fa + lb * fb;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) oa[j] = oa[j] * fa + ob[j] * fb;
+  ma = m;
+}
+
+template <int D, int GD, bool BF16>
+__global__ __launch_bounds__(64 * kDecWaves) void moda_decode_partial_kernel(const DecodeParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int NGRP = 64 / LPR;
+  constexpr int U = kDecU;
+  constexpr int NBUF = 2;
+  constexpr int ROWS_PER_BATCH = NGRP * U;  // key rows one wave consumes per batch
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane / LPR, cl = lane % LPR;
+
+  // workgroup -> (sequence b, KV head hk, head group hg, chunk s)
+  int64_t id = blockIdx.x;
+  const int s = (int)(id % p.n_chunks);
+  id /= p.n_chunks;
+  const int hg = (int)(id % p.n_hgroups);
+  id /= p.n_hgroups;
+  const int hk = (int)(id % p.Hkv);
+  const int b = (int)(id / p.Hkv);
+
+  int64_t L = p.cache_seqlens[b];
+  L = L < 1 ? 1 : (L > p.T_max ? p.T_max : L);  // the token's own key is always there
+  const bool depth_chunk = s == p.n_seq_chunks;
+  const int64_t r0 = depth_chunk ? 0 : (int64_t)s * p.chunk;
+  const int64_t r1 = depth_chunk ? p.n_depth : (r0 + p.chunk < L ? r0 + p.chunk : L);
+  if (r0 >= r1) return;  // chunk past this sequence's cache (the merge does not read it)
+
+  const int64_t row_stride = (int64_t)p.Hkv * D;  // cache and depth rows alike
+  const int64_t base_row = depth_chunk ? ((int64_t)b * p.S_cap) * p.Hkv + hk : ((int64_t)b * p.T_max) * p.Hkv + hk;
+  const void* KB = depth_chunk ? p.kd : p.kc;
+  const void* VB = depth_chunk ? p.vd : p.vc;
+  const int h0 = hk * p.G + hg * GD;  // first query head of the group
+  const float c2 = p.scale_log2;
+
+  Slice<BF16> qs[GD];
+#pragma unroll
+  for (int g = 0; g < GD; ++g) qs[g] = load_slice<BF16>(p.q, ((int64_t)b * p.Hq + h0 + g) * D + 8 * cl);
+
+  float m[GD], l[GD], o[GD][8];
+#pragma unroll
+  for (int g = 0; g < GD; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
+  }
+
+  // this wave's batches: rows r0 + (wave + k DW) ROWS_PER_BATCH + u NGRP + grp
+  const int64_t n_rows = r1 - r0;
+  const int n_batches = (int)((n_rows + ROWS_PER_BATCH - 1) / ROWS_PER_BATCH);
+  const int my_batches = n_batches > wave ? (n_batches - wave + kDecWaves - 1) / kDecWaves : 0;
+  auto row_of = [&](int k, int u) { return r0 + (int64_t)(wave + k * kDecWaves) * ROWS_PER_BATCH + u * NGRP + grp; };
+  // Loads are unconditional (a fixed count per batch keeps the compiler's waits
+  // exact): rows past the chunk re-read its last row and are masked.
+  auto issue = [&](int k, Slice<BF16>(&kw)[U], Slice<BF16>(&vw)[U]) {
+    k = k < my_batches ? k : my_batches - 1;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t r = row_of(k, u);
+      r = r < r1 ? r : r1 - 1;
+      const int64_t e = (base_row + r * p.Hkv) * D + 8 * cl;
+      kw[u] = load_slice<BF16>(KB, e);
+      vw[u] = load_slice<BF16>(VB, e);
+    }
+  };
+  auto process = [&](int k, const Slice<BF16>(&kw)[U], const Slice<BF16>(&vw)[U]) {
+#pragma unroll
+    for (int g = 0; g < GD; ++g) {
+      float sc[U];
+      float mx = kNegInf;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float t = d_group_sum<LPR>(dot8<BF16>(qs[g], kw[u])) * c2;
+        t = row_of(k, u) < r1 ? t : kNegInf;
+        sc[u] = t;
+        mx = fmaxf(mx, t);
+      }
+      const float mn = fmaxf(m[g], mx);
+      const float mu = mn == kNegInf ? 0.f : mn;
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - mu);
+      l[g] *= alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[g][j] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float pu = __builtin_amdgcn_exp2f(sc[u] - mu);
+        l[g] += pu;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pu, elem<BF16>(vw[u], j), o[g][j]);
+      }
+      m[g] = mn;
+    }
+  };
+  if (my_batches > 0) {
+    Slice<BF16> kb[NBUF][U], vb[NBUF][U];
+    issue(0, kb[0], vb[0]);
+    for (int k = 0; k < my_batches; k += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        issue(k + j + 1, kb[(j + 1) % NBUF], vb[(j + 1) % NBUF]);
+        if (k + j < my_batches) process(k + j, kb[j], vb[j]);
+      }
+    }
+  }
+
+  // merge the NGRP lane groups (lanes with the same slice cl), then the waves
+#pragma unroll
+  for (int g = 0; g < GD; ++g) {
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+      const float mb = __shfl_xor(m[g], off), lb = __shfl_xor(l[g], off);
+      float ob[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ob[j] = __shfl_xor(o[g][j], off);
+      merge_state(m[g], l[g], o[g], mb, lb, ob);
+    }
+  }
+  __shared__ float red[kDecWaves][GD][D + 4];  // per wave: o slices, then m and l
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 0; g < GD; ++g) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) red[wave][g][8 * cl + j] = o[g][j];
+      if (cl == 0) {
+        red[wave][g][D] = m[g];
+        red[wave][g][D + 1] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+  // one thread per (head, 8-element slice) writes the chunk's state
+  float* ws = p.workspace;
+  for (int t = tid; t < GD * LPR; t += 64 * kDecWaves) {
+    const int g = t / LPR, c = t % LPR;
+    float ma = kNegInf, la = 0.f, oa[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oa[j] = 0.f;
+    for (int w = 0; w < kDecWaves; ++w) {
+      float ob[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ob[j] = red[w][g][8 * c + j];
+      merge_state(ma, la, oa, red[w][g][D], red[w][g][D + 1], ob);
+    }
+    // record [b][h][chunk]: o[D], m, l (stride D + 4 floats)
+    float* rec = ws + (((int64_t)b * p.Hq + h0 + g) * p.n_chunks + s) * (D + 4);
+    *reinterpret_cast<float4*>(rec + 8 * c) = make_float4(oa[0], oa[1], oa[2], oa[3]);
+    *reinterpret_cast<float4*>(rec + 8 * c + 4) = make_float4(oa[4], oa[5], oa[6], oa[7]);
+    if (c == 0) {
+      rec[D] = ma;
+      rec[D + 1] = la;
+    }
+  }
+}
+
+// One workgroup of 64 lanes per (sequence, query head): lane c < D / 8 handles an
+// 8-element slice (64 lanes cover D <= 512).
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(64) void moda_decode_merge_kernel(const DecodeParams p) {
+  constexpr int LPR = D / 8;
+  const int lane = threadIdx.x;
+  const int64_t bh = blockIdx.x;  // b * Hq + h
+  const int b = (int)(bh / p.Hq);
+  int64_t L = p.cache_seqlens[b];
+  L = L < 1 ? 1 : (L > p.T_max ? p.T_max : L);
+  const int n_used = (int)((L + p.chunk - 1) / p.chunk);
+  const float* recs = p.workspace + bh * p.n_chunks * (D + 4);
+  float M = kNegInf;
+  for (int s = 0; s < n_used; ++s) M = fmaxf(M, recs[s * (D + 4) + D]);
+  if (p.n_depth > 0) M = fmaxf(M, recs[p.n_seq_chunks * (D + 4) + D]);
+  const float mu = M == kNegInf ? 0.f : M;
+  float Z = 0.f, acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  const int c = lane < LPR ? lane : 0;
+  auto add = [&](int s) {
+    const float* rec = recs + s * (D + 4);
+    const float f = __builtin_amdgcn_exp2f(rec[D] - mu);
+    Z = fmaf(rec[D + 1], f, Z);
+    const float4 a = *reinterpret_cast<const float4*>(rec + 8 * c);
+    const float4 bb = *reinterpret_cast<const float4*>(rec + 8 * c + 4);
+    acc[0] = fmaf(a.x, f, acc[0]);
+    acc[1] = fmaf(a.y, f, acc[1]);
+    acc[2] = fmaf(a.z, f, acc[2]);
+    acc[3] = fmaf(a.w, f, acc[3]);
+    acc[4] = fmaf(bb.x, f, acc[4]);
+    acc[5] = fmaf(bb.y, f, acc[5]);
+    acc[6] = fmaf(bb.z, f, acc[6]);
+    acc[7] = fmaf(bb.w, f, acc[7]);
+  };
+  for (int s = 0; s < n_used; ++s) add(s);
+  if (p.n_depth > 0) add(p.n_seq_chunks);
+  const float inv = Z > 0.f ? 1.f / Z : 0.f;
+  if (lane < LPR) {
+    const int64_t e = bh * D + 8 * lane;
+    if constexpr (OUT_F32) {
+      float* out = static_cast<float*>(p.out) + e;
+      *reinterpret_cast<float4*>(out) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+      *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        const f2 v = {acc[2 * j] * inv, acc[2 * j + 1] * inv};
+        w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, dbf16x2));
+      }
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + e) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    if (lane == 0 && p.lse) p.lse[bh] = (M + __log2f(Z)) * kLn2;
+  }
+}
+
+template <int D, bool BF16>
+hipError_t launch_partial(const DecodeParams& p, int gd, hipStream_t stream) {
+  const dim3 grid((unsigned)p.n_partial_blocks), block(64 * kDecWaves);
+  switch (gd) {
+    case 1: hipLaunchKernelGGL((moda_decode_partial_kernel<D, 1, BF16>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((moda_decode_partial_kernel<D, 2, BF16>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((moda_decode_partial_kernel<D, 4, BF16>), grid, block, 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((moda_decode_partial_kernel<D, 8, BF16>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dec(const DecodeParams& p, int gd, bool bf16, bool out_f32, hipStream_t stream) {
+  hipError_t e = bf16 ? launch_partial<D, true>(p, gd, stream) : launch_partial<D, false>(p, gd, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(p.B * p.Hq)), block(64);
+  if (out_f32)
+    hipLaunchKernelGGL((moda_decode_merge_kernel<D, true>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((moda_decode_merge_kernel<D, false>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_rows_per_chunk_unit(int head_dim) { return 64 / (head_dim / 8) * kDecU * kDecWaves; }
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int heads_per_block, bool bf16, bool out_f32,
+                         hipStream_t stream) {
+  if (head_dim == 128) return launch_dec<128>(p, heads_per_block, bf16, out_f32, stream);
+  if (head_dim == 64) return launch_dec<64>(p, heads_per_block, bf16, out_f32, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moda

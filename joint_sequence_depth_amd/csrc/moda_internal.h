@@ -59,4 +59,33 @@ template <int D>
 constexpr int kSplitWaves = 2;
 constexpr int kF32BlockRows = 64;
 
+// One decode step (one new token per sequence); see moda_decode.hip.
+// Element offsets: q, out: (b * Hq + h) * D + c; caches: ((b * T_max + j) * Hkv + hk) * D + c;
+// depth: ((b * S_cap + i) * Hkv + hk) * D + c; lse: b * Hq + h.
+struct DecodeParams {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const void* kd;
+  const void* vd;
+  void* out;
+  float* lse;                  // may be null
+  const int32_t* cache_seqlens;  // device, B entries
+  float* workspace;            // [B][Hq][n_chunks][D + 4] fp32 partial states
+  int64_t B;
+  int64_t T_max;
+  int32_t Hq, Hkv, G, n_hgroups;
+  int32_t S_cap, n_depth;
+  float scale_log2;
+  int64_t chunk;               // cache rows per chunk (a multiple of the partial kernel's rows per batch round)
+  int32_t n_seq_chunks;        // ceil(T_max / chunk)
+  int32_t n_chunks;            // n_seq_chunks + 1 (the last one holds the depth slots)
+  int64_t n_partial_blocks;    // B * Hkv * n_hgroups * n_chunks
+};
+
+// Rows a decode chunk is a multiple of (one round of load batches of all waves).
+int decode_rows_per_chunk_unit(int head_dim);
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int heads_per_block, bool bf16, bool out_f32,
+                         hipStream_t stream);
+
 }  // namespace moda

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moda_abi_version() == 1
+    assert L.moda_abi_version() == 2
 
 
 def test_status_codes_match_header():
@@ -149,4 +149,65 @@ def test_ctypes_signatures():
     L = _lib.lib()
     assert len(L.moda_attn_fwd.argtypes) == 19
     assert len(L.moda_attn_fwd_varlen.argtypes) == 21
+    assert len(L.moda_attn_decode.argtypes) == 21
+    assert len(L.moda_attn_decode_workspace_size.argtypes) == 5
+    assert L.moda_attn_decode_workspace_size.restype is ctypes.c_int64
     assert L.moda_last_error.restype is ctypes.c_char_p
+
+
+def calld(seqlens=P, Tmax=32, ws=P, ws_bytes=1 << 30, **kw):
+    a = dict(A)
+    a.update(kw)
+    L = _lib.lib()
+    return L.moda_attn_decode(a["q"], a["k"], a["v"], a["kd"], a["vd"], a["out"], a["lse"], a["dtype"], a["odt"],
+                              seqlens, a["B"], Tmax, a["Hq"], a["Hkv"], a["d"], a["Scap"], a["S"], a["scale"], ws,
+                              ws_bytes, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(seqlens=None), 1),
+        (dict(seqlens=P + 2), 4),
+        (dict(ws=None), 1),
+        (dict(ws=P + 8), 4),
+        (dict(ws_bytes=16), 2),
+        (dict(Tmax=0), 2),
+        (dict(Tmax=-4), 2),
+        (dict(B=-1), 2),
+        (dict(q=None), 1),
+        (dict(kd=None), 1),
+        (dict(Hq=6, Hkv=4), 2),
+        (dict(d=32), 5),
+        (dict(dtype=0, odt=1), 3),
+        (dict(scale=0.0), 7),
+        (dict(S=5, Scap=4), 2),
+    ],
+)
+def test_decode_validation_rejects(kw, code):
+    assert calld(**kw) == code
+    assert err()
+
+
+def test_decode_empty_batch_is_ok_without_launch():
+    assert calld(B=0, ws=None, seqlens=None) == 0
+    assert err() == ""
+
+
+def test_decode_workspace_size():
+    L = _lib.lib()
+    assert L.moda_attn_decode_workspace_size(1, 4, 2, 96, 16) == -1
+    assert L.moda_attn_decode_workspace_size(1, 3, 2, 64, 16) == -1
+    assert L.moda_attn_decode_workspace_size(1, 4, 2, 64, 0) == -1
+    assert L.moda_attn_decode_workspace_size(0, 4, 2, 64, 16) == 0
+    for B, Hq, Hkv, d, T in [(1, 4, 2, 64, 16), (16, 32, 8, 128, 8192), (3, 8, 8, 128, 100000)]:
+        n = L.moda_attn_decode_workspace_size(B, Hq, Hkv, d, T)
+        # one fp32 record (d accumulators, max, sum, 2 pad) per (row, head, chunk),
+        # with at least one sequence chunk and the depth chunk
+        rec = (d + 4) * 4
+        assert n > 0 and n % (B * Hq * rec) == 0
+        assert n // (B * Hq * rec) >= 2
+    # a workspace one byte short is refused
+    need = L.moda_attn_decode_workspace_size(1, 4, 2, 64, 32)
+    assert calld(ws_bytes=need - 1) == 2
+    assert "workspace" in err()

@@ -218,3 +218,161 @@ def host_slice(w: Workload, name: str, index_arrays, batch_index: int = 0) -> np
     mult = w.key_mult if name in ("k", "kd") else 1.0
     idx = np.ravel_multi_index(tuple(np.asarray(a, dtype=np.int64) for a in index_arrays), shape)
     return gen.values_np(w.seed, tids(batch_index)[name], idx, mult, w.bf16)
+
+
+# ------------------------------------------------------------------------------ decode
+#
+# One decode step: one new token per sequence reads its sequence-cache prefix and
+# its own depth slots (the decode-time caches of the MoDA paper's Table 1 as the
+# deck quotes it on slide "Depth compute still accumulates quadratically in depth").
+#
+#   q                 [B, H_q, d]
+#   k_cache, v_cache  [B, T_max, H_kv, d]   rows 0 .. cache_seqlens[b] - 1 are valid
+#   k_depth, v_depth  [B, S_cap, H_kv, d]   the new token's depth slots
+#   out [B, H_q, d]; lse [B, H_q] float32
+
+
+def draw_cache_lengths(seed: int, batch: int, lo: int, hi: int) -> tuple:
+    """``batch`` cache lengths uniform on [lo, hi]; the first is hi and the second lo
+    (when batch allows), so every draw holds both extremes."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 77])))
+    lens = [int(x) for x in rng.integers(lo, hi + 1, size=batch)]
+    if batch >= 1:
+        lens[0] = hi
+    if batch >= 2:
+        lens[1] = lo
+    return tuple(lens)
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    desc: str
+    dtype: str  # "f32" | "bf16"
+    cache_lengths: tuple  # cache_seqlens, one per sequence (B = len)
+    max_cache_len: int  # T_max (>= every length)
+    n_heads_q: int
+    n_heads_kv: int
+    head_dim: int
+    n_depth: int
+    seed: int
+    key_mult: float = 1.0
+    depth_capacity: Optional[int] = None
+
+    @property
+    def batch(self) -> int:
+        return len(self.cache_lengths)
+
+    @property
+    def group(self) -> int:
+        return self.n_heads_q // self.n_heads_kv
+
+    @property
+    def s_cap(self) -> int:
+        return self.depth_capacity if self.depth_capacity is not None else self.n_depth
+
+    @property
+    def bf16(self) -> bool:
+        return self.dtype == "bf16"
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.head_dim))
+
+    def elem_bytes(self) -> int:
+        return 2 if self.bf16 else 4
+
+    def shape_q(self):
+        return (self.batch, self.n_heads_q, self.head_dim)
+
+    def shape_cache(self):
+        return (self.batch, self.max_cache_len, self.n_heads_kv, self.head_dim)
+
+    def shape_depth(self):
+        return (self.batch, self.s_cap, self.n_heads_kv, self.head_dim)
+
+    # algorithmic bytes: each visible cache row and depth slot read once (K and V),
+    # q read once, out and lse written once
+    def cache_bytes(self) -> float:
+        return 2.0 * sum(self.cache_lengths) * self.n_heads_kv * self.head_dim * self.elem_bytes()
+
+    def depth_bytes(self) -> float:
+        return 2.0 * self.batch * self.n_depth * self.n_heads_kv * self.head_dim * self.elem_bytes()
+
+    def other_bytes(self, out_bytes: int = 2) -> float:
+        n = self.batch * self.n_heads_q
+        return n * self.head_dim * (self.elem_bytes() + out_bytes) + 4.0 * n
+
+    def total_bytes(self, out_bytes: int = 2) -> float:
+        return self.cache_bytes() + self.depth_bytes() + self.other_bytes(out_bytes)
+
+    def flops(self) -> float:
+        """QK and PV over every visible key: 4 d H_q (sum L + B n_depth)."""
+        return 4.0 * self.head_dim * self.n_heads_q * (sum(self.cache_lengths) + self.batch * self.n_depth)
+
+
+DECODE_WORKLOADS = {
+    "decode_gqa_bf16": DecodeWorkload(
+        "decode_gqa_bf16",
+        "bf16 decode GQA B=16 Hq=32 Hkv=8 d=128 S=46, cache lengths 1024..8192",
+        "bf16",
+        draw_cache_lengths(5, 16, 1024, 8192),
+        8192,
+        32,
+        8,
+        128,
+        46,
+        seed=5,
+    ),
+    "decode_mha_bf16": DecodeWorkload(
+        "decode_mha_bf16",
+        "bf16 decode B=32 H=16 d=128 S=24, cache lengths 512..4096",
+        "bf16",
+        draw_cache_lengths(6, 32, 512, 4096),
+        4096,
+        16,
+        16,
+        128,
+        24,
+        seed=6,
+    ),
+}
+
+
+def make_decode_host(w: DecodeWorkload) -> dict:
+    """Every decode input as float32 numpy arrays of the stored values (small cases)."""
+    b = w.bf16
+    out = dict(
+        q=gen.tensor_np(w.seed, TID_Q, w.shape_q(), 1.0, b),
+        k=gen.tensor_np(w.seed, TID_K, w.shape_cache(), w.key_mult, b),
+        v=gen.tensor_np(w.seed, TID_V, w.shape_cache(), 1.0, b),
+        kd=gen.tensor_np(w.seed, TID_KD, w.shape_depth(), w.key_mult, b) if w.s_cap > 0 else None,
+        vd=gen.tensor_np(w.seed, TID_VD, w.shape_depth(), 1.0, b) if w.s_cap > 0 else None,
+        seqlens=np.asarray(w.cache_lengths, dtype=np.int32),
+    )
+    return out
+
+
+def make_decode_device(w: DecodeWorkload, device) -> dict:
+    import torch
+
+    dt = torch.bfloat16 if w.bf16 else torch.float32
+    out = dict(
+        q=gen.tensor_t(w.seed, TID_Q, w.shape_q(), dt, device),
+        k=gen.tensor_t(w.seed, TID_K, w.shape_cache(), dt, device, w.key_mult),
+        v=gen.tensor_t(w.seed, TID_V, w.shape_cache(), dt, device),
+        kd=gen.tensor_t(w.seed, TID_KD, w.shape_depth(), dt, device, w.key_mult) if w.s_cap > 0 else None,
+        vd=gen.tensor_t(w.seed, TID_VD, w.shape_depth(), dt, device) if w.s_cap > 0 else None,
+        seqlens=torch.tensor(w.cache_lengths, dtype=torch.int32, device=device),
+    )
+    return out
+
+
+def decode_host_slice(w: DecodeWorkload, name: str, index_arrays) -> np.ndarray:
+    """Regenerate selected elements of one decode input on the host."""
+    shape = {"q": w.shape_q(), "k": w.shape_cache(), "v": w.shape_cache(), "kd": w.shape_depth(),
+             "vd": w.shape_depth()}[name]
+    tid = {"q": TID_Q, "k": TID_K, "v": TID_V, "kd": TID_KD, "vd": TID_VD}[name]
+    mult = w.key_mult if name in ("k", "kd") else 1.0
+    idx = np.ravel_multi_index(tuple(np.asarray(a, dtype=np.int64) for a in index_arrays), shape)
+    return gen.values_np(w.seed, tid, idx, mult, w.bf16)
