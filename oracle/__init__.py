@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the MoDA joint sequence/depth attention forward.
+"""fp64 CPU oracle of the MoDA joint sequence/depth attention (forward, decode, backward).
 
 Test infrastructure: only the tests, the smoke check and the benchmark's CPU
 baseline leg may import it. It shares no code with the HIP library."""
@@ -9,6 +9,7 @@ from .moda_oracle import (  # noqa: F401
     depth_visible,
     expanded_rows_attention,
     joint_attention,
+    joint_attention_backward,
     joint_rows,
     scalar_ref,
     separate_then_add,

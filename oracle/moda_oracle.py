@@ -355,3 +355,101 @@ def decode(q, k_cache, v_cache, cache_seqlens, k_depth, v_depth, n_depth, scale=
             out[b, h] = num / Z
             lse[b, h] = M + math.log(Z)
     return out, lse
+
+
+def joint_attention_backward(
+    q,
+    k,
+    v,
+    k_depth,
+    v_depth,
+    n_depth: int,
+    dout,
+    causal: bool = True,
+    scale: Optional[float] = None,
+    cu_seqlens=None,
+    row_block: int = 256,
+):
+    """Gradients of the MoDA forward in float64: returns (dq, dk, dv, dk_depth, dv_depth).
+
+    The pages define the forward only (deck slide "One denominator allocates
+    probability across both memories"); the backward here is its exact derivative
+    for an upstream gradient ``dout`` of ``out``, written from the chain rule:
+
+        P_j   = e^{a_j - lse}, P_i = e^{b_i - lse}   (one softmax over both key sets)
+        dP_x  = <dout_t, value_x>                     x over every visible key
+        dS_x  = P_x (dP_x - sum_y P_y dP_y)            (softmax Jacobian, the sum over
+                                                        the row's whole visible set)
+        dq_t  = scale (sum_j dS_j k_j + sum_i dS_i k^depth_{t,i})
+        dk_j  += scale dS_j q_t,  dv_j += P_j dout_t   (over rows t that see key j)
+        dk^depth_{t,i} += scale dS_i q_t,  dv^depth_{t,i} += P_i dout_t
+
+    Grouped heads accumulate the gradients of all G query heads into their KV head.
+    Layouts as for ``joint_attention``; dk_depth / dv_depth have the full slot axis
+    S_cap, with zeros in slots [n_depth, S_cap), which the operator never reads.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    kd, vd = _f64(k_depth), _f64(v_depth)
+    d = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    use_depth = n_depth > 0
+    qp, kp, vp, kdp, vdp, cu, batch_shape = _as_packed(q, k, v, kd, vd, cu_seqlens)
+    dop = do.reshape(qp.shape)
+    N, Hq, _ = qp.shape
+    Hkv = kp.shape[1]
+    G = Hq // Hkv
+    dq = np.zeros_like(qp)
+    dk = np.zeros_like(kp)
+    dv = np.zeros_like(vp)
+    dkd = None if kdp is None else np.zeros_like(kdp)
+    dvd = None if vdp is None else np.zeros_like(vdp)
+    for s in range(len(cu) - 1):
+        st, en = int(cu[s]), int(cu[s + 1])
+        L = en - st
+        if L == 0:
+            continue
+        for h in range(Hq):
+            hk = h // G
+            Q, dO = qp[st:en, h], dop[st:en, h]
+            K, V = kp[st:en, hk], vp[st:en, hk]
+            if use_depth:
+                KD = kdp[st:en, :n_depth, hk]  # [L, S, d]: each token's own slots
+                VD = vdp[st:en, :n_depth, hk]
+            for r0 in range(0, L, row_block):
+                r1 = min(L, r0 + row_block)
+                rows = np.arange(r0, r1)
+                kend = r1 if causal else L
+                a = scale * (Q[r0:r1] @ K[:kend].T)
+                if causal:  # key j visible to row t iff j <= t
+                    a = np.where(rows[:, None] >= np.arange(kend)[None, :], a, -np.inf)
+                logits = [a]
+                if use_depth:
+                    logits.append(scale * np.sum(Q[r0:r1][:, None, :] * KD[r0:r1], axis=2))
+                M = np.max(np.concatenate(logits, axis=1), axis=1)
+                Z = sum(np.exp(lg - M[:, None]).sum(axis=1) for lg in logits)
+                Pa = np.exp(a - M[:, None]) / Z[:, None]  # [R, kend], zero where masked
+                dPa = dO[r0:r1] @ V[:kend].T
+                rowdot = np.sum(Pa * dPa, axis=1)
+                if use_depth:
+                    Pb = np.exp(logits[1] - M[:, None]) / Z[:, None]  # [R, S]
+                    dPb = np.sum(dO[r0:r1][:, None, :] * VD[r0:r1], axis=2)
+                    rowdot = rowdot + np.sum(Pb * dPb, axis=1)
+                dSa = Pa * (dPa - rowdot[:, None])
+                dq[st + r0 : st + r1, h] += scale * (dSa @ K[:kend])
+                dk[st : st + kend, hk] += scale * (dSa.T @ Q[r0:r1])
+                dv[st : st + kend, hk] += Pa.T @ dO[r0:r1]
+                if use_depth:
+                    dSb = Pb * (dPb - rowdot[:, None])
+                    dq[st + r0 : st + r1, h] += scale * np.sum(dSb[:, :, None] * KD[r0:r1], axis=1)
+                    dkd[st + r0 : st + r1, :n_depth, hk] += scale * dSb[:, :, None] * Q[r0:r1][:, None, :]
+                    dvd[st + r0 : st + r1, :n_depth, hk] += Pb[:, :, None] * dO[r0:r1][:, None, :]
+    if batch_shape is not None:
+        B, T = batch_shape
+        dq = dq.reshape(B, T, Hq, d)
+        dk = dk.reshape(B, T, Hkv, d)
+        dv = dv.reshape(B, T, Hkv, d)
+        if dkd is not None:
+            dkd = dkd.reshape((B, T) + dkd.shape[1:])
+            dvd = dvd.reshape((B, T) + dvd.shape[1:])
+    return dq, dk, dv, dkd, dvd

@@ -340,6 +340,97 @@ def pin_decode_single_key(orc):
             assert abs(l[b, h] - scale * float(q[b, ts[b], h] @ k[b, 0, 0])) < 1e-12
 
 
+# backward ----------------------------------------------------------------------
+# The pages give the forward only; the backward is its exact derivative. These pins
+# tie the oracle's gradients to the forward (finite differences), to identities
+# that any derivative of a softmax-weighted average obeys, and to torch's autograd
+# of its SDPA routine where the depth set is empty.
+
+
+def _bwd_cases():
+    # (seed, B, T, Hq, Hkv, d, S, Scap, causal, cu_seqlens or None)
+    return [
+        (11, 2, 5, 4, 2, 4, 2, 3, True, None),
+        (12, 1, 6, 2, 2, 4, 3, 3, False, None),
+        (13, 1, 7, 2, 1, 4, 1, 2, True, np.array([0, 3, 7])),
+        (14, 2, 4, 3, 3, 4, 0, 2, True, None),
+    ]
+
+
+def _bwd_inputs(seed, B, T, Hq, Hkv, d, S, Scap, cu):
+    q, k, v, kd, vd = rand_case(seed, B=B, T=T, Hq=Hq, Hkv=Hkv, d=d, S=S, Scap=Scap)
+    w = np.random.default_rng(seed + 100).standard_normal(q.shape)
+    if cu is not None:  # packed layout: drop the batch axis
+        q, k, v, w = (x.reshape((-1,) + x.shape[2:]) for x in (q, k, v, w))
+        kd, vd = (x.reshape((-1,) + x.shape[2:]) for x in (kd, vd))
+    return [q, k, v, kd, vd], w
+
+
+def pin_backward_finite_differences(orc):
+    """Every gradient element equals the central difference of sum(out * W) under
+    the forward oracle (itself pinned above), including zeros for unread slots."""
+    for seed, B, T, Hq, Hkv, d, S, Scap, causal, cu in _bwd_cases():
+        xs, w = _bwd_inputs(seed, B, T, Hq, Hkv, d, S, Scap, cu)
+        scale = 0.61
+        grads = orc.joint_attention_backward(*xs[:5], S, w, causal, scale, cu_seqlens=cu)
+
+        def loss(ys):
+            o, _ = orc.joint_attention(*ys, S, causal, scale, cu_seqlens=cu)
+            return float(np.sum(o * w))
+
+        eps = 1e-6
+        for which in range(5):
+            g = grads[which]
+            for idx in np.ndindex(xs[which].shape):
+                up = [x.copy() for x in xs]
+                dn = [x.copy() for x in xs]
+                up[which][idx] += eps
+                dn[which][idx] -= eps
+                fd = (loss(up) - loss(dn)) / (2 * eps)
+                assert abs(g[idx] - fd) < 1e-6 * (1 + abs(fd)), (seed, which, idx, g[idx], fd)
+
+
+def pin_backward_sums(orc):
+    """Per segment and KV head: the value gradients sum to the summed upstream
+    gradient of the head group (each row's weights sum to one), and the key
+    gradients sum to zero (a common shift of all keys moves every logit of a row
+    by the same amount, which leaves the softmax unchanged)."""
+    q, k, v, kd, vd = rand_case(21, B=2, T=13, Hq=4, Hkv=2, d=8, S=4, Scap=5)
+    w = np.random.default_rng(22).standard_normal(q.shape)
+    for causal in (True, False):
+        dq, dk, dv, dkd, dvd = orc.joint_attention_backward(q, k, v, kd, vd, 4, w, causal, 0.4)
+        G = 2
+        for b in range(2):
+            for hk in range(2):
+                vsum = dv[b, :, hk].sum(axis=0) + dvd[b, :, :, hk].sum(axis=(0, 1))
+                osum = w[b, :, hk * G : (hk + 1) * G].sum(axis=(0, 1))
+                assert np.max(np.abs(vsum - osum)) < 1e-10
+                ksum = dk[b, :, hk].sum(axis=0) + dkd[b, :, :, hk].sum(axis=(0, 1))
+                assert np.max(np.abs(ksum)) < 1e-10
+        assert np.all(dkd[:, :, 4:] == 0) and np.all(dvd[:, :, 4:] == 0)
+
+
+def pin_backward_empty_depth_is_sdpa_autograd(orc):
+    """With no depth slots the gradients are those of ordinary softmax attention:
+    torch's autograd through its SDPA routine in float64 (grouped heads by repeating
+    KV heads, whose gradients then sum over the group)."""
+    for seed, (Hq, Hkv), causal in [(31, (2, 2), True), (32, (4, 2), True), (33, (3, 1), False)]:
+        q, k, v, kd, vd = rand_case(seed, B=2, T=9, Hq=Hq, Hkv=Hkv, d=8, S=2)
+        w = np.random.default_rng(seed).standard_normal(q.shape)
+        scale = 0.29
+        dq, dk, dv, _, _ = orc.joint_attention_backward(q, k, v, kd, vd, 0, w, causal, scale)
+        G = Hq // Hkv
+        qt = torch.tensor(q.transpose(0, 2, 1, 3), requires_grad=True)
+        kt = torch.tensor(k.transpose(0, 2, 1, 3), requires_grad=True)
+        vt = torch.tensor(v.transpose(0, 2, 1, 3), requires_grad=True)
+        o = F.scaled_dot_product_attention(qt, kt.repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1),
+                                           is_causal=causal, scale=scale)
+        (o * torch.from_numpy(np.ascontiguousarray(w.transpose(0, 2, 1, 3)))).sum().backward()
+        for mine, ref in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+            ref = ref.numpy().transpose(0, 2, 1, 3)
+            assert np.max(np.abs(mine - ref)) < 1e-12, np.max(np.abs(mine - ref))
+
+
 ALL_PINS = [
     pin_empty_depth_is_sdpa,
     pin_equal_logits_plain_mean,
@@ -360,4 +451,7 @@ ALL_PINS = [
     pin_decode_is_last_row,
     pin_decode_empty_depth_is_sdpa,
     pin_decode_single_key,
+    pin_backward_finite_differences,
+    pin_backward_sums,
+    pin_backward_empty_depth_is_sdpa_autograd,
 ]

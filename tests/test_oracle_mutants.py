@@ -34,6 +34,17 @@ MUTANTS = {
     "decode_group_map": ("hk = h // G\n            a = scale", "hk = h % Hkv\n            a = scale"),
     "decode_depth_logit_unscaled": ("logits.append(scale * (kd[b", "logits.append((kd[b"),
     "decode_depth_keys_as_values": ("num = num + u @ vd[b, :n_depth, hk]", "num = num + u @ kd[b, :n_depth, hk]"),
+    "bwd_rowdot_without_depth": ("rowdot = rowdot + np.sum(Pb * dPb, axis=1)", "rowdot = rowdot + 0.0"),
+    "bwd_dq_without_depth": ("dq[st + r0 : st + r1, h] += scale * np.sum(dSb", "dq[st + r0 : st + r1, h] += 0.0 * np.sum(dSb"),
+    "bwd_dk_unscaled": ("dk[st : st + kend, hk] += scale * (dSa.T", "dk[st : st + kend, hk] += (dSa.T"),
+    "bwd_dvd_from_dS": ("dvd[st + r0 : st + r1, :n_depth, hk] += Pb[", "dvd[st + r0 : st + r1, :n_depth, hk] += dSb["),
+    "bwd_jacobian_sign": ("dSa = Pa * (dPa - rowdot[:, None])", "dSa = Pa * (dPa + rowdot[:, None])"),
+    "bwd_group_map": ("hk = h // G\n            Q, dO", "hk = h % Hkv\n            Q, dO"),
+    "bwd_dkd_of_previous_token": ("scale * dSb[:, :, None] * Q[r0:r1][:, None, :]",
+                                  "scale * dSb[:, :, None] * np.roll(Q, 1, axis=0)[r0:r1][:, None, :]"),
+    "bwd_dv_from_dS": ("dv[st : st + kend, hk] += Pa.T @ dO[r0:r1]", "dv[st : st + kend, hk] += dSa.T @ dO[r0:r1]"),
+    "bwd_diagonal_dropped": ("rows[:, None] >= np.arange(kend)", "rows[:, None] > np.arange(kend)"),
+    "bwd_depth_values_as_keys": ("VD = vdp[st:en, :n_depth, hk]", "VD = kdp[st:en, :n_depth, hk]"),
 }
 
 
