@@ -1,6 +1,6 @@
 /*
- * moda_attn.h - C ABI of the MoDA joint sequence/depth attention forward on
- * AMD Instinct MI355X (gfx950).
+ * moda_attn.h - C ABI of the MoDA joint sequence/depth attention (forward,
+ * backward and decode step) on AMD Instinct MI355X (gfx950).
  *
  * Operator: "Mixture-of-Depths Attention" (arXiv 2603.15619), MoDA deck slide
  * "One denominator allocates probability across both memories" (teaching form of
@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MODA_ABI_VERSION 2
+#define MODA_ABI_VERSION 3
 
 /* status codes */
 #define MODA_OK 0
@@ -133,6 +133,54 @@ int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, co
 /* Workspace bytes moda_attn_decode needs for these sizes, or -1 for invalid sizes. */
 int64_t moda_attn_decode_workspace_size(int64_t batch, int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
                                         int32_t max_cache_len);
+
+/*
+ * Backward of moda_attn_fwd: the gradients of the joint operator for an upstream
+ * gradient dout of out. The pages (MoDA deck, slide "One denominator allocates
+ * probability across both memories") define the forward; this is its exact
+ * derivative. With P the joint softmax of row (t, h) over its visible sequence
+ * keys and its own depth slots (recomputed from lse), delta_t = <dout_t, out_t>
+ * and dS_x = P_x (<dout_t, value_x> - delta_t):
+ *   dq_t = scale (sum_j dS_j k_j + sum_i dS_i k_depth_{t,i})
+ *   dk_j = scale sum_t dS_tj q_t,  dv_j = sum_t P_tj dout_t
+ *   dk_depth_{t,i} = scale dS_ti q_t,  dv_depth_{t,i} = P_ti dout_t
+ * with the sums of the G query heads of a KV head added into it.
+ *
+ * q, k, v, k_depth, v_depth: the forward's inputs, in `dtype`. out, dout and
+ * every gradient (dq, dk, dv, dk_depth, dv_depth) are in `grad_dtype`, laid out
+ * like the tensor they belong to; lse is the forward's float32 lse (required).
+ * dtype pairs as for the forward: (F32, F32), (BF16, BF16), (BF16, F32). For bf16
+ * inputs the matrix products take bf16 operands (dout and the softmax gradient
+ * rounded to bf16) with fp32 accumulation.
+ * dq, dk, dv are fully overwritten. dk_depth / dv_depth: slots [0, n_depth) are
+ * overwritten, slots [n_depth, S_cap) are not written; both may be NULL when
+ * n_depth == 0. n_heads_q / n_heads_kv <= 16.
+ *
+ * workspace: DEVICE memory of at least moda_attn_bwd_workspace_size(...) bytes,
+ * 256-byte aligned, owned by the caller (fp32 delta and the depth share of dq);
+ * contents on entry do not matter; calls sharing one workspace must not overlap.
+ * Launches on `stream` and returns without waiting. Other arguments, checks and
+ * errors as for moda_attn_fwd; MODA_ERR_SHAPE also for a too small workspace.
+ */
+int moda_attn_bwd(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
+                  const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                  void* dk_depth, void* dv_depth, int32_t dtype, int32_t grad_dtype, int64_t batch, int64_t seqlen,
+                  int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t n_depth,
+                  int32_t causal, float scale, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* The backward over packed variable-length sequences (layouts and cu_seqlens as
+ * for moda_attn_fwd_varlen, lse [Hq, N]). */
+int moda_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
+                         const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         void* dk_depth, void* dv_depth, int32_t dtype, int32_t grad_dtype,
+                         const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen,
+                         int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
+                         int32_t n_depth, int32_t causal, float scale, void* workspace, int64_t workspace_bytes,
+                         void* stream);
+
+/* Workspace bytes the backward needs for N = total tokens (B * T), or -1 for
+ * invalid sizes. */
+int64_t moda_attn_bwd_workspace_size(int64_t total_tokens, int32_t n_heads_q, int32_t head_dim, int32_t n_depth);
 
 /* Description of the last non-OK status returned on the calling thread ("" if none). */
 const char* moda_last_error(void);

@@ -1,8 +1,19 @@
-"""MoDA joint sequence/depth attention forward (and decode step) on MI355X (gfx950).
+"""MoDA joint sequence/depth attention on MI355X (gfx950): forward, backward and
+decode step.
 
 The computation lives in libmoda_attn.so (hand-written HIP kernels behind the C
 ABI declared in include/moda_attn.h); this package only marshals torch tensors.
 """
-from ._lib import EXPORTS, ModaError, attn_decode, attn_fwd, decode_workspace_size, lib  # noqa: F401
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    ModaError,
+    attn_bwd,
+    attn_decode,
+    attn_fwd,
+    bwd_workspace_size,
+    decode_workspace_size,
+    lib,
+)
 
-__all__ = ["attn_fwd", "attn_decode", "decode_workspace_size", "lib", "ModaError", "EXPORTS"]
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "bwd_workspace_size", "decode_workspace_size", "lib", "ModaError",
+           "EXPORTS"]

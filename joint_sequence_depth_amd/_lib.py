@@ -30,7 +30,8 @@ STATUS_NAMES = {
 
 # every symbol include/moda_attn.h declares
 EXPORTS = ("moda_attn_fwd", "moda_attn_fwd_varlen", "moda_attn_decode", "moda_attn_decode_workspace_size",
-           "moda_last_error", "moda_abi_version")
+           "moda_attn_bwd", "moda_attn_bwd_varlen", "moda_attn_bwd_workspace_size", "moda_last_error",
+           "moda_abi_version")
 
 _lib = None
 
@@ -60,6 +61,13 @@ def lib() -> ctypes.CDLL:
         L.moda_attn_decode.restype = ctypes.c_int
         L.moda_attn_decode_workspace_size.argtypes = [i64, i32, i32, i32, i32]
         L.moda_attn_decode_workspace_size.restype = ctypes.c_int64
+        L.moda_attn_bwd.argtypes = [vp] * 13 + [i32, i32, i64, i64, i32, i32, i32, i32, i32, i32, f32, vp, i64, vp]
+        L.moda_attn_bwd.restype = ctypes.c_int
+        L.moda_attn_bwd_varlen.argtypes = [vp] * 13 + [i32, i32, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32, f32,
+                                                        vp, i64, vp]
+        L.moda_attn_bwd_varlen.restype = ctypes.c_int
+        L.moda_attn_bwd_workspace_size.argtypes = [i64, i32, i32, i32]
+        L.moda_attn_bwd_workspace_size.restype = ctypes.c_int64
         L.moda_last_error.argtypes = []
         L.moda_last_error.restype = ctypes.c_char_p
         L.moda_abi_version.argtypes = []
@@ -274,3 +282,109 @@ def attn_decode(
     )
     _check(status)
     return out, lse
+
+
+def bwd_workspace_size(total_tokens: int, n_heads_q: int, head_dim: int, n_depth: int) -> int:
+    """Bytes of device workspace one backward call with these sizes needs."""
+    n = lib().moda_attn_bwd_workspace_size(total_tokens, n_heads_q, head_dim, n_depth)
+    if n < 0:
+        raise ValueError("invalid backward sizes")
+    return int(n)
+
+
+def attn_bwd(
+    q,
+    k,
+    v,
+    k_depth,
+    v_depth,
+    out,
+    dout,
+    lse,
+    n_depth: Optional[int] = None,
+    causal: bool = True,
+    scale: Optional[float] = None,
+    cu_seqlens=None,
+    max_seqlen: Optional[int] = None,
+    grads=None,
+    workspace=None,
+    stream=None,
+):
+    """Backward of ``attn_fwd`` through the C ABI. ``out`` and ``lse`` are the
+    forward's results, ``dout`` the gradient of ``out`` (same dtype as out: the
+    gradient dtype). Returns (dq, dk, dv, dk_depth, dv_depth) in that dtype, laid
+    out like q, k, v, k_depth, v_depth (dk_depth/dv_depth None without depth
+    tensors). Slots [n_depth, S_cap) of the depth gradients are zero when this
+    function allocates them, and left untouched in a caller's ``grads``, a
+    tuple of five preallocated tensors, and ``workspace`` (a uint8 device tensor of
+    ``bwd_workspace_size`` bytes) make the call allocation-free."""
+    import torch
+
+    varlen = cu_seqlens is not None
+    lead = 1 if varlen else 2
+    ts = (q, k, v, k_depth, v_depth, out, dout, lse, cu_seqlens, workspace) + tuple(grads or ())
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if t is not None and t.device.type != "cuda":
+            raise ValueError("all tensors must be on the GPU")
+    if q.dim() != lead + 2 or k.shape != v.shape or k.shape[:-2] != q.shape[:-2] or k.shape[-1] != q.shape[-1]:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if out.shape != q.shape or dout.shape != q.shape or out.dtype != dout.dtype:
+        raise ValueError("out and dout must have q's shape and one dtype")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    d, Hq, Hkv = q.shape[-1], q.shape[-2], k.shape[-2]
+    if k_depth is not None:
+        if v_depth is None or k_depth.shape != v_depth.shape or k_depth.dim() != lead + 3:
+            raise ValueError("k_depth and v_depth must both be [..., S_cap, Hkv, d]")
+        if k_depth.shape[:lead] != q.shape[:lead] or k_depth.shape[-2:] != (Hkv, d):
+            raise ValueError(f"depth tensors must be [..., S_cap, Hkv, d], got {tuple(k_depth.shape)}")
+        if k_depth.dtype != q.dtype or v_depth.dtype != q.dtype:
+            raise TypeError("depth tensors must share q's dtype")
+        s_cap = k_depth.shape[lead]
+    else:
+        s_cap = 0
+    if n_depth is None:
+        n_depth = s_cap
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    N = q.shape[0] if varlen else q.shape[0] * q.shape[1]
+    lse_shape = (Hq, N) if varlen else (q.shape[0], Hq, q.shape[1])
+    if lse is None or tuple(lse.shape) != lse_shape or lse.dtype != torch.float32:
+        raise ValueError(f"lse must be the forward's float32 {lse_shape}")
+    gdt = out.dtype
+    if grads is None:
+        # the library never writes slots [n_depth, S_cap): their gradient is zero
+        grads = (torch.empty_like(q, dtype=gdt), torch.empty_like(k, dtype=gdt), torch.empty_like(v, dtype=gdt),
+                 None if k_depth is None else torch.zeros_like(k_depth, dtype=gdt),
+                 None if v_depth is None else torch.zeros_like(v_depth, dtype=gdt))
+    dq, dk, dv, dkd, dvd = grads
+    for g, ref in zip(grads, (q, k, v, k_depth, v_depth)):
+        if (g is None) != (ref is None) or (g is not None and (g.shape != ref.shape or g.dtype != gdt)):
+            raise ValueError("grads must match q, k, v, k_depth, v_depth in shape, in out's dtype")
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_size(N, Hq, d, int(n_depth)), 256), dtype=torch.uint8,
+                                device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    code, gcode = _dtype_code(q), _dtype_code(out)
+    ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(k_depth), _ptr(v_depth), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(dkd), _ptr(dvd))
+    wsb = workspace.numel() * workspace.element_size()
+    L = lib()
+    if varlen:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
+        n_seqs = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            cu_host = cu_seqlens.cpu()
+            max_seqlen = int((cu_host[1:] - cu_host[:-1]).max()) if n_seqs > 0 else 0
+        status = L.moda_attn_bwd_varlen(*ptrs, code, gcode, _ptr(cu_seqlens), n_seqs, N, int(max_seqlen), Hq, Hkv, d,
+                                        s_cap, int(n_depth), int(bool(causal)), float(scale), _ptr(workspace), wsb,
+                                        stream)
+    else:
+        status = L.moda_attn_bwd(*ptrs, code, gcode, q.shape[0], q.shape[1], Hq, Hkv, d, s_cap, int(n_depth),
+                                 int(bool(causal)), float(scale), _ptr(workspace), wsb, stream)
+    _check(status)
+    return dq, dk, dv, dkd, dvd

@@ -15,7 +15,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmoda_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["moda_attn.hip", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_decode.hip"]
+SOURCES = ["moda_attn.hip", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_decode.hip", "moda_bwd.hip"]
+# Sources whose kernels keep matrix-core accumulators in AGPRs (the backward
+# holds two 128 x 32 fp32 accumulators per wave, more than the VGPRs alone)
+AGPR_ACCUMULATORS = {"moda_bwd.hip"}
 ARCH = "gfx950"
 
 
@@ -26,8 +29,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def compile_flags():
-    return [
+def compile_flags(source: str = ""):
+    flags = [
         f"--offload-arch={ARCH}",
         "-O3",
         "-std=c++17",
@@ -37,16 +40,17 @@ def compile_flags():
         "-target-feature",
         "-Xclang",
         "-packed-fp32-ops",
-        # MFMA accumulators in VGPRs: where LDS caps a kernel at one wave per SIMD
-        # the compiler would otherwise place MFMA results in AGPRs and copy every
-        # score back to VGPRs for the softmax
-        "-mllvm",
-        "-amdgpu-mfma-vgpr-form",
         "-Wall",
         "-Wno-unused-function",
         f"-I{INCLUDE}",
         f"-I{CSRC}",
     ]
+    if source not in AGPR_ACCUMULATORS:
+        # MFMA accumulators in VGPRs: where LDS caps a kernel at one wave per SIMD
+        # the compiler would otherwise place MFMA results in AGPRs and copy every
+        # score back to VGPRs for the softmax
+        flags += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    return flags
 
 
 def build(verbose: bool = False) -> str:
@@ -57,7 +61,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *compile_flags(src), "-c", os.path.join(CSRC, src), "-o", obj]
         _run(cmd, verbose)
         objs.append(obj)
     tmp = LIB_PATH + ".tmp"

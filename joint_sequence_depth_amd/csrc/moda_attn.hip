@@ -132,6 +132,11 @@ int dispatch(moda::Params& p, const Common& c, int64_t n_seg, int64_t max_len, h
 }
 
 // ---- decode ---------------------------------------------------------------------
+#ifndef MODA_DEC_TARGET_WGS
+#define MODA_DEC_TARGET_WGS 1024
+#endif
+constexpr int64_t kDecodeTargetBlocks = MODA_DEC_TARGET_WGS;
+
 // Query heads per decode workgroup: the largest of 8, 4, 2, 1 dividing G.
 int decode_heads_per_block(int G) {
   for (int g = 8; g > 1; g /= 2)
@@ -146,7 +151,7 @@ int64_t decode_chunk(int64_t batch, int Hq, int Hkv, int d, int64_t T_max) {
   const int64_t unit = moda::decode_rows_per_chunk_unit(d);
   int64_t units = batch * Hkv * (int64_t)((Hq / Hkv) / decode_heads_per_block(Hq / Hkv));
   if (units < 1) units = 1;
-  int64_t want = units >= 1024 ? 1 : (1024 + units - 1) / units;
+  int64_t want = units >= kDecodeTargetBlocks ? 1 : (kDecodeTargetBlocks + units - 1) / units;
   int64_t chunk = (T_max + want - 1) / want;
   chunk = (chunk + unit - 1) / unit * unit;
   return chunk < unit ? unit : chunk;
@@ -156,6 +161,92 @@ int64_t decode_workspace_bytes(int64_t batch, int Hq, int Hkv, int d, int64_t T_
   const int64_t chunk = decode_chunk(batch, Hq, Hkv, d, T_max);
   const int64_t n_chunks = (T_max + chunk - 1) / chunk + 1;
   return batch * Hq * n_chunks * (int64_t)(d + 4) * 4;
+}
+
+// ---- backward --------------------------------------------------------------------
+constexpr int kBwdMaxGroup = 16;  // query heads per KV head the backward supports
+
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+int64_t bwd_workspace_bytes(int64_t N, int Hq, int d, int n_depth) {
+  const int64_t delta = round256(4 * N * (int64_t)Hq);
+  return delta + (n_depth > 0 ? round256(4 * N * (int64_t)Hq * d) : 0);
+}
+
+struct BwdArgs {
+  const void *q, *k, *v, *kd, *vd, *out, *dout;
+  const float* lse;
+  void *dq, *dk, *dv, *dkd, *dvd;
+  int32_t dtype, grad_dtype, Hq, Hkv, d, S_cap, n_depth, causal;
+  float scale;
+  void* workspace;
+  int64_t workspace_bytes;
+};
+
+// Checks shared by both backward entry points; fills the fields of p they fix.
+int check_bwd(const BwdArgs& a, int64_t N, moda::BwdParams& p) {
+  const Common c{a.q,  a.k,   a.v,   a.kd,      a.vd,    a.dq,   nullptr, a.dtype, a.grad_dtype,
+                 a.Hq, a.Hkv, a.d,   a.S_cap,   a.n_depth, a.causal, a.scale};
+  const int rc = check_common(c);
+  if (rc != MODA_OK) return rc;
+  if (!a.out || !a.dout || !a.lse || !a.dk || !a.dv)
+    return fail(MODA_ERR_NULL, "out, dout, lse, dq, dk and dv must be non-NULL");
+  if (a.n_depth > 0 && (!a.dkd || !a.dvd))
+    return fail(MODA_ERR_NULL, "dk_depth and dv_depth must be non-NULL when n_depth > 0");
+  if (a.Hq / a.Hkv > kBwdMaxGroup)
+    return fail(MODA_ERR_UNSUPPORTED, "backward supports up to %d query heads per KV head (got %d)", kBwdMaxGroup,
+                a.Hq / a.Hkv);
+  if (!aligned16(a.out) || !aligned16(a.dout) || !aligned16(a.dk) || !aligned16(a.dv))
+    return fail(MODA_ERR_ALIGN, "out, dout, dq, dk and dv must be 16-byte aligned");
+  if (a.n_depth > 0 && (!aligned16(a.dkd) || !aligned16(a.dvd)))
+    return fail(MODA_ERR_ALIGN, "dk_depth and dv_depth must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(a.lse) & 3u) return fail(MODA_ERR_ALIGN, "lse must be 4-byte aligned");
+  if (!a.workspace) return fail(MODA_ERR_NULL, "workspace must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(a.workspace) & 255u) return fail(MODA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const int64_t need = bwd_workspace_bytes(N, a.Hq, a.d, a.n_depth);
+  if (a.workspace_bytes < need)
+    return fail(MODA_ERR_SHAPE, "workspace too small: %lld bytes given, %lld needed", (long long)a.workspace_bytes,
+                (long long)need);
+  p = moda::BwdParams{};
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.kd = a.n_depth > 0 ? a.kd : nullptr;
+  p.vd = a.n_depth > 0 ? a.vd : nullptr;
+  p.out = a.out;
+  p.dout = a.dout;
+  p.lse = a.lse;
+  p.dq = a.dq;
+  p.dk = a.dk;
+  p.dv = a.dv;
+  p.dkd = a.n_depth > 0 ? a.dkd : nullptr;
+  p.dvd = a.n_depth > 0 ? a.dvd : nullptr;
+  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  p.delta = reinterpret_cast<float*>(ws);
+  p.dq_depth = a.n_depth > 0 ? reinterpret_cast<float*>(ws + round256(4 * N * (int64_t)a.Hq)) : nullptr;
+  p.total_tokens = N;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.G = a.Hq / a.Hkv;
+  p.S_cap = a.S_cap;
+  p.n_depth = a.n_depth;
+  p.causal = a.causal;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  return MODA_OK;
+}
+
+int launch_bwd_checked(moda::BwdParams& p, const BwdArgs& a, int64_t n_seg, int64_t max_len, hipStream_t stream) {
+  const int64_t nb = (max_len + 127) / 128;
+  p.n_qblocks = (int32_t)nb;
+  p.n_kblocks = (int32_t)nb;
+  if (n_seg * a.Hq * nb > 0x7fffffffLL || p.total_tokens * a.Hq > 0x7fffffffLL * 4)
+    return fail(MODA_ERR_SHAPE, "problem too large for one launch");
+  const hipError_t err =
+      moda::launch_bwd(p, a.d, a.dtype == MODA_DTYPE_BF16, a.grad_dtype == MODA_DTYPE_F32, stream);
+  if (err != hipSuccess) return fail(MODA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  g_err[0] = '\0';
+  return MODA_OK;
 }
 
 }  // namespace
@@ -277,6 +368,66 @@ int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, co
   if (err != hipSuccess) return fail(MODA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
   g_err[0] = '\0';
   return MODA_OK;
+}
+
+int64_t moda_attn_bwd_workspace_size(int64_t total_tokens, int32_t n_heads_q, int32_t head_dim, int32_t n_depth) {
+  if (total_tokens < 0 || n_heads_q < 1 || n_depth < 0 || (head_dim != 64 && head_dim != 128)) return -1;
+  return bwd_workspace_bytes(total_tokens, n_heads_q, head_dim, n_depth);
+}
+
+int moda_attn_bwd(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
+                  const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                  void* dk_depth, void* dv_depth, int32_t dtype, int32_t grad_dtype, int64_t batch, int64_t seqlen,
+                  int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t n_depth,
+                  int32_t causal, float scale, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (batch < 0 || seqlen < 0) return fail(MODA_ERR_SHAPE, "batch and seqlen must be >= 0");
+  if (batch == 0 || seqlen == 0) {
+    g_err[0] = '\0';
+    return MODA_OK;
+  }
+  if (batch > 0x7fffffffLL) return fail(MODA_ERR_SHAPE, "batch too large");
+  const BwdArgs a{q,  k,  v,  k_depth, v_depth,    out,       dout,       lse,          dq,
+                  dk, dv, dk_depth, dv_depth, dtype, grad_dtype, n_heads_q, n_heads_kv, head_dim,
+                  depth_capacity, n_depth, causal, scale, workspace, workspace_bytes};
+  moda::BwdParams p;
+  const int rc = check_bwd(a, batch * seqlen, p);
+  if (rc != MODA_OK) return rc;
+  p.cu_seqlens = nullptr;
+  p.uniform_len = seqlen;
+  p.n_seg = (int32_t)batch;
+  p.lse_head_stride = seqlen;
+  p.lse_batch_layout = 1;
+  return launch_bwd_checked(p, a, batch, seqlen, static_cast<hipStream_t>(stream));
+}
+
+int moda_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
+                         const void* out, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         void* dk_depth, void* dv_depth, int32_t dtype, int32_t grad_dtype,
+                         const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen,
+                         int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
+                         int32_t n_depth, int32_t causal, float scale, void* workspace, int64_t workspace_bytes,
+                         void* stream) {
+  if (n_seqs < 0 || total_tokens < 0 || max_seqlen < 0)
+    return fail(MODA_ERR_SHAPE, "n_seqs, total_tokens and max_seqlen must be >= 0");
+  if (n_seqs == 0 || total_tokens == 0 || max_seqlen == 0) {
+    g_err[0] = '\0';
+    return MODA_OK;
+  }
+  if (!cu_seqlens) return fail(MODA_ERR_NULL, "cu_seqlens must be non-NULL");
+  if ((int64_t)max_seqlen > total_tokens) return fail(MODA_ERR_SHAPE, "max_seqlen exceeds total_tokens");
+  const BwdArgs a{q,  k,  v,  k_depth, v_depth,    out,       dout,       lse,          dq,
+                  dk, dv, dk_depth, dv_depth, dtype, grad_dtype, n_heads_q, n_heads_kv, head_dim,
+                  depth_capacity, n_depth, causal, scale, workspace, workspace_bytes};
+  moda::BwdParams p;
+  const int rc = check_bwd(a, total_tokens, p);
+  if (rc != MODA_OK) return rc;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return fail(MODA_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+  p.cu_seqlens = cu_seqlens;
+  p.uniform_len = 0;
+  p.n_seg = n_seqs;
+  p.lse_head_stride = total_tokens;
+  p.lse_batch_layout = 0;
+  return launch_bwd_checked(p, a, n_seqs, max_seqlen, static_cast<hipStream_t>(stream));
 }
 
 const char* moda_last_error(void) { return g_err; }

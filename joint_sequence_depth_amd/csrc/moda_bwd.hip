@@ -1,0 +1,685 @@
+// Backward of the MoDA joint sequence/depth attention (MoDA, arXiv 2603.15619;
+// forward on deck slide "One denominator allocates probability across both
+// memories"). The pages give the forward only; this is its exact derivative.
+// With P the joint softmax of a row (over its visible sequence keys and its own
+// depth slots, recomputed from the forward's lse), dout the upstream gradient:
+//
+//   delta_t = <dout_t, out_t>        (= sum over the row's keys of P dP)
+//   dS_x    = P_x (<dout_t, value_x> - delta_t)
+//   dq_t    = scale (sum_j dS_j k_j + sum_i dS_i k_depth_{t,i})
+//   dk_j    = scale sum_t dS_tj q_t,     dv_j = sum_t P_tj dout_t
+//   dk_depth_{t,i} = scale dS_ti q_t,    dv_depth_{t,i} = P_ti dout_t
+//
+// summed over the G query heads of a KV head. Three launches on one stream:
+//
+//  * prep (any dtype): one wave per (token, KV head). Computes delta for the G
+//    heads, then the depth part, which is row-local (a depth slot belongs to one
+//    token): lanes hold 8-element slices of a slot row (LPR = D / 8 lanes per
+//    row), so dk_depth / dv_depth are summed over the heads in registers and
+//    written once, and the depth share of dq (summed over slots in LDS) goes to an
+//    fp32 workspace.
+//  * dq (bf16, matrix cores): a workgroup of 4 waves per (segment, query head,
+//    128 tokens), 32 tokens per wave, K/V blocks of 64 keys staged in LDS.
+//    S^T = K Q^T and dP^T = V dO^T put one token per lane; dS^T feeds
+//    dQ^T += K^T dS^T through transposing LDS reads of K, with the keys of the
+//    dS^T registers and of the K^T operand in the same order. The epilogue adds
+//    the depth share.
+//  * dk/dv (bf16, matrix cores): a workgroup of 4 waves per (segment, KV head,
+//    128 keys), 32 keys per wave, looping over the G query heads and the query
+//    blocks of 64 tokens that can see them (Q, dO, lse and delta staged in LDS).
+//    S = Q K^T and dP = dO V^T put one key per lane; dV^T += dO^T P and
+//    dK^T += Q^T dS read dO^T and Q^T transposed from LDS.
+//  * fp32 inputs take row-wise vector kernels for dq and dk/dv instead (lanes over
+//    8-element slices, as in prep): the full-precision path.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moda_internal.h"
+#include "moda_rowops.h"
+
+namespace moda {
+namespace {
+
+using rowops::group_sum;
+using rowops::load8;
+using rowops::store_n;
+
+typedef __bf16 bbf16x8 __attribute__((ext_vector_type(8)));
+typedef float bf32x16 __attribute__((ext_vector_type(16)));
+typedef short bi16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBwdWaves = 4;   // waves per workgroup, all kernels
+constexpr int kBlk = 128;      // tokens (dq) or keys (dk/dv) per workgroup
+constexpr int kTile = 64;      // keys (dq) or tokens (dk/dv) staged per step
+
+#define MODA_BWD_TR_READ(a) __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bi16x4*)(a))
+
+struct Seg {
+  int64_t start, len;
+};
+
+__device__ __forceinline__ Seg segment(const BwdParams& p, int seg) {
+  if (p.cu_seqlens) {
+    int64_t a = p.cu_seqlens[seg], b = p.cu_seqlens[seg + 1];
+    a = a < 0 ? 0 : (a > p.total_tokens ? p.total_tokens : a);
+    b = b < a ? a : (b > p.total_tokens ? p.total_tokens : b);
+    return {a, b - a};
+  }
+  return {(int64_t)seg * p.uniform_len, p.uniform_len};
+}
+
+// Segment holding packed token n (the segment whose range contains it).
+__device__ __forceinline__ Seg segment_of(const BwdParams& p, int64_t n) {
+  if (!p.cu_seqlens) {
+    const int64_t s = n / p.uniform_len;
+    return {s * p.uniform_len, p.uniform_len};
+  }
+  int lo = 0, hi = p.n_seg - 1;  // last segment whose clamped start <= n
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segment(p, mid).start <= n) lo = mid;
+    else hi = mid - 1;
+  }
+  return segment(p, lo);
+}
+
+// lse element of packed token n, query head h.
+__device__ __forceinline__ int64_t lse_index(const BwdParams& p, int64_t n, int h) {
+  if (p.lse_batch_layout) {
+    const int64_t b = n / p.lse_head_stride, t = n - b * p.lse_head_stride;
+    return (b * p.Hq + h) * p.lse_head_stride + t;
+  }
+  return (int64_t)h * p.lse_head_stride + n;
+}
+
+// ---------------------------------------------------------------- prep + depth
+// LDS floats per wave of the prep kernel (a multiple of 4, so each wave's block
+// stays 16-byte aligned).
+__host__ __device__ constexpr int prep_wave_floats(int G, int D) { return G * D + ((2 * G + 3) & ~3); }
+
+template <int D, bool BF16, bool GF32>
+__global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_prep_kernel(const BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int NGRP = 64 / LPR;
+  extern __shared__ float dyn[];  // per wave: dq_depth [G][D], lse2 [G], delta [G]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane / LPR, cl = lane % LPR;
+  const int64_t item = (int64_t)blockIdx.x * kBwdWaves + wave;
+  if (item >= p.total_tokens * p.Hkv) return;  // no workgroup barrier below
+  const int64_t n = item / p.Hkv;
+  const int hk = (int)(item % p.Hkv);
+  const int G = p.G;
+  float* dqd = dyn + (size_t)wave * prep_wave_floats(G, D);
+  float* lse2s = dqd + G * D;
+  float* dels = lse2s + G;
+
+  for (int g = 0; g < G; ++g) {
+    const int h = hk * G + g;
+    const int64_t e = (n * p.Hq + h) * D + 8 * cl;
+    float o8[8], d8[8];
+    load8<!GF32>(p.out, e, o8);
+    load8<!GF32>(p.dout, e, d8);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s = fmaf(o8[j], d8[j], s);
+    s = group_sum<LPR>(s);
+    if (lane == 0) {
+      p.delta[(int64_t)h * p.total_tokens + n] = s;
+      dels[g] = s;
+      lse2s[g] = p.lse[lse_index(p, n, h)] * kLog2e;
+    }
+    if (grp == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dqd[g * D + 8 * cl + j] = 0.f;
+    }
+  }
+  if (p.n_depth <= 0) return;
+  // LDS accesses of one wave complete in issue order: the values written above
+  // are visible to every lane of the wave below.
+  __builtin_amdgcn_wave_barrier();
+
+  const float c2 = p.scale_log2, sc = p.scale;
+  const int nb = (p.n_depth + NGRP - 1) / NGRP;
+  for (int ib = 0; ib < nb; ++ib) {
+    const int i = ib * NGRP + grp;
+    const bool valid = i < p.n_depth;
+    const int ic = valid ? i : p.n_depth - 1;
+    const int64_t de = ((n * p.S_cap + ic) * p.Hkv + hk) * D + 8 * cl;
+    float kd8[8], vd8[8], dk8[8], dv8[8];
+    load8<BF16>(p.kd, de, kd8);
+    load8<BF16>(p.vd, de, vd8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dk8[j] = dv8[j] = 0.f;
+    for (int g = 0; g < G; ++g) {
+      const int h = hk * G + g;
+      const int64_t e = (n * p.Hq + h) * D + 8 * cl;
+      float q8[8], do8[8];
+      load8<BF16>(p.q, e, q8);
+      load8<!GF32>(p.dout, e, do8);
+      float b = 0.f, dp = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        b = fmaf(q8[j], kd8[j], b);
+        dp = fmaf(do8[j], vd8[j], dp);
+      }
+      b = group_sum<LPR>(b);
+      dp = group_sum<LPR>(dp);
+      const float pr = valid ? __builtin_amdgcn_exp2f(b * c2 - lse2s[g]) : 0.f;
+      const float ds = pr * (dp - dels[g]) * sc;
+      float part[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        dv8[j] = fmaf(pr, do8[j], dv8[j]);
+        dk8[j] = fmaf(ds, q8[j], dk8[j]);
+        part[j] = ds * kd8[j];
+      }
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) part[j] += __shfl_xor(part[j], off);
+      if (grp == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dqd[g * D + 8 * cl + j] += part[j];
+      }
+    }
+    if (valid) {
+      store_n<GF32, 8>(p.dkd, de, dk8);
+      store_n<GF32, 8>(p.dvd, de, dv8);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  // the G heads of this KV head are contiguous in dq_depth: G * D floats
+  float* dst = p.dq_depth + (n * p.Hq + (int64_t)hk * G) * D;
+  for (int x = lane; x < G * D / 4; x += 64)
+    reinterpret_cast<float4*>(dst)[x] = reinterpret_cast<const float4*>(dqd)[x];
+}
+
+// ---------------------------------------------------------------- bf16 helpers
+// One 16-byte chunk of a row (8 bf16) from global memory, as bf16; fp32 storage is
+// rounded to bf16 (nearest even).
+template <bool F32>
+__device__ __forceinline__ uint4 load_chunk_bf16(const void* base, int64_t elem) {
+  if constexpr (F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+    const float4 a = p[0], b = p[1];
+    return make_uint4(rowops::pack_bf16x2(a.x, a.y), rowops::pack_bf16x2(a.z, a.w), rowops::pack_bf16x2(b.x, b.y),
+                      rowops::pack_bf16x2(b.z, b.w));
+  } else {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+  }
+}
+
+__device__ __forceinline__ bbf16x8 as_b8(uint4 w) { return __builtin_bit_cast(bbf16x8, w); }
+
+__device__ __forceinline__ bbf16x8 pk_b8(const uint32_t* w) {
+  return __builtin_bit_cast(bbf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// Transposed operand of rows [r0, r0 + 16) of a row-major LDS tile (pitch PITCH
+// bytes), d tile dt: lane 16 g + 4 e + q reads rows r0 + 4 (g / 2) + e and that + 8
+// at columns 32 dt + 16 (g % 2) + 4 q .. + 3; after the transpose lane (r, hh)
+// holds column 32 dt + r at rows r0 + 4 hh + {0..3, 8..11}, the row order of 8
+// consecutive accumulator registers of a 32 x 32 score tile.
+template <int PITCH>
+__device__ __forceinline__ bbf16x8 tr_operand(const unsigned char* tile, int r0, int dt, int lane) {
+  const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+  const uint32_t a = (uint32_t)(uintptr_t)tile + (uint32_t)((r0 + 4 * (g >> 1) + e) * PITCH) +
+                     (uint32_t)(2 * (32 * dt + 16 * (g & 1) + 4 * q));
+  const bi16x4 x0 = MODA_BWD_TR_READ(a);
+  const bi16x4 x1 = MODA_BWD_TR_READ(a + 8 * PITCH);
+  return __builtin_bit_cast(bbf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// ---------------------------------------------------------------- dq (bf16)
+template <int D, bool GF32>
+__global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dq_kernel(const BwdParams p) {
+  constexpr int KC = D / 16, DT = D / 32;
+  constexpr int PITCH = D * 2 + 16;
+  constexpr int CPR = D * 2 / 16;                      // 16-byte chunks per row
+  constexpr int NLD = kTile * CPR / (64 * kBwdWaves);  // chunks per thread per tile
+  __shared__ __align__(16) unsigned char ks[kTile * PITCH];
+  __shared__ __align__(16) unsigned char vs[kTile * PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 31, hh = lane >> 5;
+
+  int64_t rest = blockIdx.x;
+  const int qb = (int)(rest % p.n_qblocks);
+  rest /= p.n_qblocks;
+  const int h = (int)(rest % p.Hq);
+  const int seg = (int)(rest / p.Hq);
+  const Seg sg = segment(p, seg);
+  const int64_t t0 = (int64_t)qb * kBlk;
+  if (t0 >= sg.len) return;  // whole workgroup, before any barrier
+  const int hk = h / p.G;
+  const int64_t tw = t0 + 32 * wave;
+  const int64_t t = tw + r;
+  const bool row_ok = t < sg.len;
+  const int64_t n = sg.start + (row_ok ? t : sg.len - 1);
+
+  bbf16x8 qf[KC], dof[KC];
+  {
+    const int64_t e = (n * p.Hq + h) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      qf[kc] = as_b8(load_chunk_bf16<false>(p.q, e + 16 * kc + 8 * hh));
+      dof[kc] = as_b8(load_chunk_bf16<GF32>(p.dout, e + 16 * kc + 8 * hh));
+    }
+  }
+  const float lse2 = p.lse[lse_index(p, n, h)] * kLog2e;
+  const float dl = p.delta[(int64_t)h * p.total_tokens + n];
+  const float c2 = p.scale_log2;
+
+  bf32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+  const int64_t kend = p.causal ? (t0 + kBlk < sg.len ? t0 + kBlk : sg.len) : sg.len;
+  const int nkb = (int)((kend + kTile - 1) / kTile);
+  uint4 kreg[NLD], vreg[NLD];
+  auto gload = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = tid + 64 * kBwdWaves * u, row = idx / CPR, ch = idx % CPR;
+      int64_t key = (int64_t)kb * kTile + row;
+      key = key < sg.len ? key : sg.len - 1;  // rows past the end repeat the last key (masked)
+      const int64_t e = ((sg.start + key) * p.Hkv + hk) * D + 8 * ch;
+      kreg[u] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + e);
+      vreg[u] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + e);
+    }
+  };
+  auto sstore = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = tid + 64 * kBwdWaves * u, row = idx / CPR, ch = idx % CPR;
+      *reinterpret_cast<uint4*>(ks + row * PITCH + 16 * ch) = kreg[u];
+      *reinterpret_cast<uint4*>(vs + row * PITCH + 16 * ch) = vreg[u];
+    }
+  };
+
+  gload(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    __syncthreads();  // every wave is done reading the previous tile
+    sstore();
+    __syncthreads();
+    if (kb + 1 < nkb) gload(kb + 1);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int64_t k0 = (int64_t)kb * kTile + 32 * st;
+      if (k0 >= sg.len || (p.causal && k0 > tw + 31)) continue;  // wave-uniform
+      bf32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const unsigned char* row = ks + (32 * st + r) * PITCH + 16 * (2 * kc + hh);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(row)), qf[kc], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const unsigned char* row = vs + (32 * st + r) * PITCH + 16 * (2 * kc + hh);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(row)), dof[kc], dp, 0, 0,
+                                                     0);
+      }
+      // register i holds key k0 + 8 (i / 4) + 4 hh + i % 4 of token t
+      uint32_t dsp[8];
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        float v2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int64_t key = k0 + 8 * ((i + u) >> 2) + 4 * hh + ((i + u) & 3);
+          const bool vis = row_ok && key < sg.len && (!p.causal || key <= t);
+          const float pr = vis ? __builtin_amdgcn_exp2f(s[i + u] * c2 - lse2) : 0.f;
+          v2[u] = pr * (dp[i + u] - dl);
+        }
+        dsp[i >> 1] = rowops::pack_bf16x2(v2[0], v2[1]);
+      }
+#pragma unroll
+      for (int part = 0; part < 2; ++part)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<PITCH>(ks, 32 * st + 16 * part, dt, lane),
+                                                            pk_b8(dsp + 4 * part), acc[dt], 0, 0, 0);
+    }
+  }
+
+  if (!row_ok) return;
+  const int64_t e = (n * p.Hq + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 32 * dt + 8 * j + 4 * hh;
+      float x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = acc[dt][4 * j + u] * p.scale;
+      if (p.n_depth > 0) {
+        const float4 a = *reinterpret_cast<const float4*>(p.dq_depth + e + c);
+        x[0] += a.x;
+        x[1] += a.y;
+        x[2] += a.z;
+        x[3] += a.w;
+      }
+      store_n<GF32, 4>(p.dq, e + c, x);
+    }
+}
+
+// ---------------------------------------------------------------- dk / dv (bf16)
+template <int D, bool GF32>
+__global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdParams p) {
+  constexpr int KC = D / 16, DT = D / 32;
+  constexpr int PITCH = D * 2 + 16;
+  constexpr int CPR = D * 2 / 16;
+  constexpr int NLD = kTile * CPR / (64 * kBwdWaves);
+  __shared__ __align__(16) unsigned char qs[kTile * PITCH];
+  __shared__ __align__(16) unsigned char os[kTile * PITCH];  // dout
+  __shared__ __align__(16) float lse2s[kTile];
+  __shared__ __align__(16) float dels[kTile];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 31, hh = lane >> 5;
+
+  int64_t rest = blockIdx.x;
+  const int kbk = (int)(rest % p.n_kblocks);
+  rest /= p.n_kblocks;
+  const int hk = (int)(rest % p.Hkv);
+  const int seg = (int)(rest / p.Hkv);
+  const Seg sg = segment(p, seg);
+  const int64_t k0 = (int64_t)kbk * kBlk;
+  if (k0 >= sg.len) return;
+  const int64_t kw = k0 + 32 * wave;
+  const int64_t key = kw + r;
+  const bool key_ok = key < sg.len;
+  const int64_t nk = sg.start + (key_ok ? key : sg.len - 1);
+
+  // K^T and V^T operands: lane (r, hh) holds key r, columns 16 kc + 8 hh .. + 7
+  bbf16x8 kf[KC], vf[KC];
+  {
+    const int64_t e = (nk * p.Hkv + hk) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      kf[kc] = as_b8(load_chunk_bf16<false>(p.k, e + 16 * kc + 8 * hh));
+      vf[kc] = as_b8(load_chunk_bf16<false>(p.v, e + 16 * kc + 8 * hh));
+    }
+  }
+  bf32x16 dka[DT], dva[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dka[dt][i] = dva[dt][i] = 0.f;
+
+  const float c2 = p.scale_log2;
+  const int64_t tstart = p.causal ? k0 / kTile * kTile : 0;
+  const int ntq = (int)((sg.len - tstart + kTile - 1) / kTile);
+  const int nsteps = p.G * ntq;  // (query head, query tile) pairs
+  uint4 qreg[NLD], oreg[NLD];
+  float lreg = 0.f, dreg = 0.f;
+  auto gload = [&](int step) __attribute__((always_inline)) {
+    const int h = hk * p.G + step / ntq;
+    const int64_t tq0 = tstart + (int64_t)(step % ntq) * kTile;
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = tid + 64 * kBwdWaves * u, row = idx / CPR, ch = idx % CPR;
+      int64_t tq = tq0 + row;
+      tq = tq < sg.len ? tq : sg.len - 1;  // rows past the end repeat the last token (masked)
+      const int64_t e = ((sg.start + tq) * p.Hq + h) * D + 8 * ch;
+      qreg[u] = load_chunk_bf16<false>(p.q, e);
+      oreg[u] = load_chunk_bf16<GF32>(p.dout, e);
+    }
+    if (tid < kTile) {
+      int64_t tq = tq0 + tid;
+      tq = tq < sg.len ? tq : sg.len - 1;
+      const int64_t nq = sg.start + tq;
+      lreg = p.lse[lse_index(p, nq, h)] * kLog2e;
+      dreg = p.delta[(int64_t)h * p.total_tokens + nq];
+    }
+  };
+  auto sstore = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = tid + 64 * kBwdWaves * u, row = idx / CPR, ch = idx % CPR;
+      *reinterpret_cast<uint4*>(qs + row * PITCH + 16 * ch) = qreg[u];
+      *reinterpret_cast<uint4*>(os + row * PITCH + 16 * ch) = oreg[u];
+    }
+    if (tid < kTile) {
+      lse2s[tid] = lreg;
+      dels[tid] = dreg;
+    }
+  };
+
+  if (nsteps > 0) gload(0);
+  for (int step = 0; step < nsteps; ++step) {
+    __syncthreads();
+    sstore();
+    __syncthreads();
+    if (step + 1 < nsteps) gload(step + 1);
+    const int64_t tq0 = tstart + (int64_t)(step % ntq) * kTile;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int64_t q0 = tq0 + 32 * st;
+      if (q0 >= sg.len || (p.causal && q0 + 31 < kw)) continue;  // wave-uniform
+      bf32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int off = (32 * st + r) * PITCH + 16 * (2 * kc + hh);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(qs + off)), kf[kc], s, 0, 0,
+                                                    0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(os + off)), vf[kc], dp, 0,
+                                                     0, 0);
+      }
+      // register i holds token q0 + 8 (i / 4) + 4 hh + i % 4, key `key`
+      uint32_t pp[8], dsp[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lse2s + 32 * st + 8 * j + 4 * hh);
+        const float4 d4 = *reinterpret_cast<const float4*>(dels + 32 * st + 8 * j + 4 * hh);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * j + u;
+          const int64_t tq = q0 + 8 * j + 4 * hh + u;
+          const bool vis = key_ok && tq < sg.len && (!p.causal || key <= tq);
+          const float pr = vis ? __builtin_amdgcn_exp2f(s[i] * c2 - lv[u]) : 0.f;
+          pv[u] = pr;
+          dsv[u] = pr * (dp[i] - dv4[u]);
+        }
+        pp[2 * j] = rowops::pack_bf16x2(pv[0], pv[1]);
+        pp[2 * j + 1] = rowops::pack_bf16x2(pv[2], pv[3]);
+        dsp[2 * j] = rowops::pack_bf16x2(dsv[0], dsv[1]);
+        dsp[2 * j + 1] = rowops::pack_bf16x2(dsv[2], dsv[3]);
+      }
+#pragma unroll
+      for (int part = 0; part < 2; ++part)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<PITCH>(os, 32 * st + 16 * part, dt, lane),
+                                                            pk_b8(pp + 4 * part), dva[dt], 0, 0, 0);
+          dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<PITCH>(qs, 32 * st + 16 * part, dt, lane),
+                                                            pk_b8(dsp + 4 * part), dka[dt], 0, 0, 0);
+        }
+    }
+  }
+
+  if (!key_ok) return;
+  const int64_t e = (nk * p.Hkv + hk) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 32 * dt + 8 * j + 4 * hh;
+      float xk[4], xv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        xk[u] = dka[dt][4 * j + u] * p.scale;
+        xv[u] = dva[dt][4 * j + u];
+      }
+      store_n<GF32, 4>(p.dk, e + c, xk);
+      store_n<GF32, 4>(p.dv, e + c, xv);
+    }
+}
+
+// ---------------------------------------------------------------- fp32 (vector)
+// dq: one wave per (packed token, query head); lane groups take NGRP keys at a time.
+template <int D>
+__global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dq_f32_kernel(const BwdParams p) {
+  constexpr int LPR = D / 8, NGRP = 64 / LPR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane / LPR, cl = lane % LPR;
+  const int64_t item = (int64_t)blockIdx.x * kBwdWaves + wave;
+  if (item >= p.total_tokens * p.Hq) return;
+  const int64_t n = item / p.Hq;
+  const int h = (int)(item % p.Hq), hk = h / p.G;
+  const Seg sg = segment_of(p, n);
+  const int64_t t = n - sg.start;
+  float q8[8], do8[8], acc[8];
+  load8<false>(p.q, (n * p.Hq + h) * D + 8 * cl, q8);
+  load8<false>(p.dout, (n * p.Hq + h) * D + 8 * cl, do8);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  const float lse2 = p.lse[lse_index(p, n, h)] * kLog2e;
+  const float dl = p.delta[(int64_t)h * p.total_tokens + n];
+  const int64_t nkeys = p.causal ? t + 1 : sg.len;
+  for (int64_t j0 = 0; j0 < nkeys; j0 += NGRP) {
+    const int64_t j = j0 + grp;
+    const bool vis = j < nkeys;
+    const int64_t e = ((sg.start + (vis ? j : nkeys - 1)) * p.Hkv + hk) * D + 8 * cl;
+    float k8[8], v8[8];
+    load8<false>(p.k, e, k8);
+    load8<false>(p.v, e, v8);
+    float s = 0.f, dp = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      s = fmaf(q8[c], k8[c], s);
+      dp = fmaf(do8[c], v8[c], dp);
+    }
+    s = group_sum<LPR>(s);
+    dp = group_sum<LPR>(dp);
+    const float pr = vis ? __builtin_amdgcn_exp2f(s * p.scale_log2 - lse2) : 0.f;
+    const float ds = pr * (dp - dl);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = fmaf(ds, k8[c], acc[c]);
+  }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] += __shfl_xor(acc[c], off);
+  if (grp != 0) return;
+  const int64_t e = (n * p.Hq + h) * D + 8 * cl;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] *= p.scale;
+  if (p.n_depth > 0) {
+    const float4 a = *reinterpret_cast<const float4*>(p.dq_depth + e);
+    const float4 b = *reinterpret_cast<const float4*>(p.dq_depth + e + 4);
+    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  }
+  store_n<true, 8>(p.dq, e, acc);
+}
+
+// dk / dv: one wave per (packed key token, KV head); lane groups take NGRP query
+// tokens at a time, for each of the G query heads.
+template <int D>
+__global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_f32_kernel(const BwdParams p) {
+  constexpr int LPR = D / 8, NGRP = 64 / LPR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane / LPR, cl = lane % LPR;
+  const int64_t item = (int64_t)blockIdx.x * kBwdWaves + wave;
+  if (item >= p.total_tokens * p.Hkv) return;
+  const int64_t n = item / p.Hkv;
+  const int hk = (int)(item % p.Hkv);
+  const Seg sg = segment_of(p, n);
+  const int64_t j = n - sg.start;
+  float k8[8], v8[8], dk8[8], dv8[8];
+  load8<false>(p.k, (n * p.Hkv + hk) * D + 8 * cl, k8);
+  load8<false>(p.v, (n * p.Hkv + hk) * D + 8 * cl, v8);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dk8[c] = dv8[c] = 0.f;
+  const int64_t tbeg = p.causal ? j : 0;
+  for (int g = 0; g < p.G; ++g) {
+    const int h = hk * p.G + g;
+    for (int64_t t0 = tbeg; t0 < sg.len; t0 += NGRP) {
+      const int64_t t = t0 + grp;
+      const bool vis = t < sg.len;
+      const int64_t nq = sg.start + (vis ? t : sg.len - 1);
+      const int64_t e = (nq * p.Hq + h) * D + 8 * cl;
+      float q8[8], do8[8];
+      load8<false>(p.q, e, q8);
+      load8<false>(p.dout, e, do8);
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        s = fmaf(q8[c], k8[c], s);
+        dp = fmaf(do8[c], v8[c], dp);
+      }
+      s = group_sum<LPR>(s);
+      dp = group_sum<LPR>(dp);
+      const float lse2 = p.lse[lse_index(p, nq, h)] * kLog2e;
+      const float dl = p.delta[(int64_t)h * p.total_tokens + nq];
+      const float pr = vis ? __builtin_amdgcn_exp2f(s * p.scale_log2 - lse2) : 0.f;
+      const float ds = pr * (dp - dl);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        dv8[c] = fmaf(pr, do8[c], dv8[c]);
+        dk8[c] = fmaf(ds, q8[c], dk8[c]);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      dk8[c] += __shfl_xor(dk8[c], off);
+      dv8[c] += __shfl_xor(dv8[c], off);
+    }
+  if (grp != 0) return;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dk8[c] *= p.scale;
+  const int64_t e = (n * p.Hkv + hk) * D + 8 * cl;
+  store_n<true, 8>(p.dk, e, dk8);
+  store_n<true, 8>(p.dv, e, dv8);
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, bool bf16, bool grad_f32, hipStream_t stream) {
+  const dim3 block(64 * kBwdWaves);
+  const size_t prep_lds = (size_t)kBwdWaves * prep_wave_floats(p.G, D) * sizeof(float);
+  const dim3 prep_grid((unsigned)((p.total_tokens * p.Hkv + kBwdWaves - 1) / kBwdWaves));
+  if (bf16 && grad_f32)
+    hipLaunchKernelGGL((moda_bwd_prep_kernel<D, true, true>), prep_grid, block, prep_lds, stream, p);
+  else if (bf16)
+    hipLaunchKernelGGL((moda_bwd_prep_kernel<D, true, false>), prep_grid, block, prep_lds, stream, p);
+  else
+    hipLaunchKernelGGL((moda_bwd_prep_kernel<D, false, true>), prep_grid, block, prep_lds, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (bf16) {
+    const dim3 gq((unsigned)((int64_t)p.n_seg * p.Hq * p.n_qblocks));
+    const dim3 gk((unsigned)((int64_t)p.n_seg * p.Hkv * p.n_kblocks));
+    if (grad_f32) {
+      hipLaunchKernelGGL((moda_bwd_dq_kernel<D, true>), gq, block, 0, stream, p);
+      hipLaunchKernelGGL((moda_bwd_dkv_kernel<D, true>), gk, block, 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((moda_bwd_dq_kernel<D, false>), gq, block, 0, stream, p);
+      hipLaunchKernelGGL((moda_bwd_dkv_kernel<D, false>), gk, block, 0, stream, p);
+    }
+  } else {
+    const dim3 gq((unsigned)((p.total_tokens * p.Hq + kBwdWaves - 1) / kBwdWaves));
+    const dim3 gk((unsigned)((p.total_tokens * p.Hkv + kBwdWaves - 1) / kBwdWaves));
+    hipLaunchKernelGGL((moda_bwd_dq_f32_kernel<D>), gq, block, 0, stream, p);
+    hipLaunchKernelGGL((moda_bwd_dkv_f32_kernel<D>), gk, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, int head_dim, bool bf16, bool grad_f32, hipStream_t stream) {
+  if (head_dim == 128) return launch_bwd_d<128>(p, bf16, grad_f32, stream);
+  if (head_dim == 64) return launch_bwd_d<64>(p, bf16, grad_f32, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moda

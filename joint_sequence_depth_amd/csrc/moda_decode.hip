@@ -22,6 +22,7 @@
 #include <stdint.h>
 
 #include "moda_internal.h"
+#include "moda_rowops.h"
 
 namespace moda {
 namespace {
@@ -30,8 +31,14 @@ typedef __bf16 dbf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309417f;
-constexpr int kDecWaves = 4;  // waves per partial workgroup
-constexpr int kDecU = 4;      // key rows per lane group per load batch
+#ifndef MODA_DEC_WAVES
+#define MODA_DEC_WAVES 4
+#endif
+#ifndef MODA_DEC_U
+#define MODA_DEC_U 4
+#endif
+constexpr int kDecWaves = MODA_DEC_WAVES;  // waves per partial workgroup
+constexpr int kDecU = MODA_DEC_U;          // key rows per lane group per load batch
 
 __device__ __forceinline__ float d_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float d_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -81,20 +88,6 @@ __device__ __forceinline__ float dot8(const Slice<BF16>& q, const Slice<BF16>& k
     for (int i = 0; i < 8; ++i) s = fmaf(elem<false>(q, i), elem<false>(k, i), s);
     return s;
   }
-}
-
-template <int CTRL>
-__device__ __forceinline__ float d_dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-// sum over aligned groups of LPR lanes; every lane of a group ends with the same bits
-template <int LPR>
-__device__ __forceinline__ float d_group_sum(float s) {
-  s += d_dpp<0xB1>(s);
-  s += d_dpp<0x4E>(s);
-  s += d_dpp<0x141>(s);
-  if constexpr (LPR == 16) s += d_dpp<0x140>(s);
-  return s;
 }
 
 // Merges running state (mb, lb, ob) into (ma, la, oa), base-2 units.
@@ -180,7 +173,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void moda_decode_partial_kernel(con
       float mx = kNegInf;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        float t = d_group_sum<LPR>(dot8<BF16>(qs[g], kw[u])) * c2;
+        float t = rowops::group_sum<LPR>(dot8<BF16>(qs[g], kw[u])) * c2;
         t = row_of(k, u) < r1 ? t : kNegInf;
         sc[u] = t;
         mx = fmaxf(mx, t);

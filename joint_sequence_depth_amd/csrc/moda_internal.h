@@ -59,6 +59,44 @@ template <int D>
 constexpr int kSplitWaves = 2;
 constexpr int kF32BlockRows = 64;
 
+// Backward of the joint forward (see moda_bwd.hip). Offsets as in Params; out,
+// dout and every gradient are in the gradient dtype; delta and dq_depth are fp32
+// workspace: delta[h * N + n] = <dout, out> of row (n, h); dq_depth[(n * Hq + h) * D + c]
+// is the depth slots' share of dq (written only when n_depth > 0).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* kd;
+  const void* vd;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dkd;
+  void* dvd;
+  float* delta;
+  float* dq_depth;
+
+  const int32_t* cu_seqlens;  // null = uniform segments of uniform_len tokens
+  int64_t uniform_len;
+  int64_t total_tokens;       // N
+  int32_t n_seg;
+  int32_t n_qblocks;          // 128-token blocks per segment (bf16 dq kernel)
+  int32_t n_kblocks;          // 128-key blocks per segment (bf16 dk/dv kernel)
+  int32_t Hq, Hkv, G;
+  int32_t S_cap, n_depth;
+  int32_t causal;
+  float scale;
+  float scale_log2;
+  int64_t lse_head_stride;    // as in Params
+  int32_t lse_batch_layout;
+};
+
+hipError_t launch_bwd(const BwdParams& p, int head_dim, bool bf16, bool grad_f32, hipStream_t stream);
+
 // One decode step (one new token per sequence); see moda_decode.hip.
 // Element offsets: q, out: (b * Hq + h) * D + c; caches: ((b * T_max + j) * Hkv + hk) * D + c;
 // depth: ((b * S_cap + i) * Hkv + hk) * D + c; lse: b * Hq + h.

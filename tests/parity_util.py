@@ -172,3 +172,155 @@ def gpu_row(w, out, lse, s, t, h):
 
 def with_(w, **kw):
     return dataclasses.replace(w, **kw)
+
+
+# --------------------------------------------------------------------------- backward
+
+
+def bwd_tolerance(w, ref, grad_bf16):
+    """Per-element bound for a gradient compared with the fp64 reference: the
+    forward's rule (1e-5 absolute for fp32 inputs; 2e-2 RMS(ref) for bf16 inputs,
+    plus half a bf16 ulp for bf16 gradients), RMS over the whole compared tensor."""
+    return tolerance(w, ref, out_bf16=grad_bf16)
+
+
+def check_grad(w, got, ref, what, grad_bf16):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    if not got.size:
+        return 0.0, 0.0
+    diff = np.abs(got - ref)
+    ratio = float(np.max(diff / bwd_tolerance(w, ref, grad_bf16)))
+    err = float(np.max(diff))
+    assert ratio <= 1.0, f"{what}: max|got-ref| = {err:.3e}, worst error/bound = {ratio:.3f}"
+    return err, ratio
+
+
+def unit_operands(w, s, hk, grad_bf16, batch_index=0):
+    """Operands of one (segment, KV head) unit regenerated on the host: the G query
+    heads of hk over the segment's tokens, as a batch-layout problem with B = 1:
+    q, dout [1, L, G, d]; k, v [1, L, 1, d]; depth [1, L, S_cap, 1, d] (or None)."""
+    d, G = w.head_dim, w.group
+    L = w.lengths[s]
+    if w.varlen:
+        lead = (np.arange(int(w.cu_seqlens()[s]), int(w.cu_seqlens()[s]) + L),)
+    else:
+        lead = (np.array([s]), np.arange(L))
+
+    def ix(*rest):
+        if len(lead) == 2:
+            idx = np.ix_(lead[0], lead[1], *rest)
+            return tuple(a[0] for a in idx)
+        return np.ix_(lead[0], *rest)
+
+    hq = np.arange(hk * G, (hk + 1) * G)
+    c = np.arange(d)
+    q = configs.host_slice(w, "q", ix(hq, c), batch_index)[None]
+    do = configs.host_slice(w, "do", ix(hq, c), batch_index, bf16=grad_bf16)[None]
+    k = configs.host_slice(w, "k", ix(np.array([hk]), c), batch_index)[None]
+    v = configs.host_slice(w, "v", ix(np.array([hk]), c), batch_index)[None]
+    if w.s_cap > 0:
+        i = np.arange(w.s_cap)
+        kd = configs.host_slice(w, "kd", ix(i, np.array([hk]), c), batch_index)[None]
+        vd = configs.host_slice(w, "vd", ix(i, np.array([hk]), c), batch_index)[None]
+    else:
+        kd = vd = None
+    return q, k, v, kd, vd, do
+
+
+BF16_U = 2.0**-8  # unit roundoff of bfloat16 (8 significant bits, nearest-even)
+
+
+def bwd_rounding_magnitudes(q, k, v, kd, vd, n_depth, dout, causal, scale, cu_seqlens=None, row_block=256):
+    """First-order rounding-error magnitudes of every gradient element of the bf16
+    backward path, in float64, from the inputs alone (no kernel output).
+
+    The bf16 path rounds to bf16 (unit roundoff u) where the exact derivative has
+    none: the probabilities P in dv = P^T dout, the softmax gradient dS in
+    dq = scale dS K and dk = scale dS^T Q, and dout where it enters the matrix
+    products. Through the forward it also consumes out, itself computed with P in
+    bf16 and stored in bf16: |delta error| <= 2 u D_t, D_t = sum_c |dout_tc| (P |V|)_tc.
+    A sum sum_x a_x b_x whose a_x carry relative error u is off by at most
+    u sum_x |a_x| |b_x|; so, with E_tx = u <|dout_t|, |value_x|> the error of dP:
+        dq_tc  <- scale sum_x (u |dS_x| + P_x (2 u D_t + E_tx)) |key_xc|
+        dk_jc  <- scale sum_t (u |dS_tj| + P_tj (2 u D_t + E_tj)) |q_tc|
+        dv_jc  <- 2 u sum_t P_tj |dout_tc|
+        dk_depth_{t,i,c} <- scale P_ti (2 u D_t + E_ti) |q_tc|,  dv_depth: 0
+    Returns arrays shaped like (dq, dk, dv, dk_depth, dv_depth)."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    kd = None if kd is None else np.asarray(kd, dtype=np.float64)
+    vd = None if vd is None else np.asarray(vd, dtype=np.float64)
+    u = BF16_U
+    batch = cu_seqlens is None
+    if batch:
+        B, T = q.shape[:2]
+        flat = lambda x: None if x is None else x.reshape((B * T,) + x.shape[2:])  # noqa: E731
+        q, k, v, do, kd, vd = map(flat, (q, k, v, do, kd, vd))
+        cu = np.arange(B + 1) * T
+    else:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+    N, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    mq, mk, mv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    mkd = None if kd is None else np.zeros_like(kd)
+    S = n_depth
+    for s in range(len(cu) - 1):
+        st, en = int(cu[s]), int(cu[s + 1])
+        L = en - st
+        for h in range(Hq):
+            hk = h // G
+            Q, dO, K, V = q[st:en, h], do[st:en, h], k[st:en, hk], v[st:en, hk]
+            for r0 in range(0, L, row_block):
+                r1 = min(L, r0 + row_block)
+                rows = np.arange(r0, r1)
+                kend = r1 if causal else L
+                a = scale * (Q[r0:r1] @ K[:kend].T)
+                if causal:
+                    a = np.where(rows[:, None] >= np.arange(kend)[None, :], a, -np.inf)
+                lg = [a]
+                if S > 0:
+                    KD, VD = kd[st + r0 : st + r1, :S, hk], vd[st + r0 : st + r1, :S, hk]
+                    lg.append(scale * np.sum(Q[r0:r1][:, None, :] * KD, axis=2))
+                M = np.max(np.concatenate(lg, axis=1), axis=1)
+                Z = sum(np.exp(x - M[:, None]).sum(axis=1) for x in lg)
+                Pa = np.exp(a - M[:, None]) / Z[:, None]
+                dPa = dO[r0:r1] @ V[:kend].T
+                Ea = u * (np.abs(dO[r0:r1]) @ np.abs(V[:kend]).T)
+                PV = Pa @ np.abs(V[:kend])
+                rowdot = np.sum(Pa * dPa, axis=1)
+                if S > 0:
+                    Pb = np.exp(lg[1] - M[:, None]) / Z[:, None]
+                    dPb = np.sum(dO[r0:r1][:, None, :] * VD, axis=2)
+                    Eb = u * np.sum(np.abs(dO[r0:r1])[:, None, :] * np.abs(VD), axis=2)
+                    PV = PV + np.sum(Pb[:, :, None] * np.abs(VD), axis=1)
+                    rowdot = rowdot + np.sum(Pb * dPb, axis=1)
+                Dt = np.sum(np.abs(dO[r0:r1]) * PV, axis=1)
+                wa = u * np.abs(Pa * (dPa - rowdot[:, None])) + Pa * (2 * u * Dt[:, None] + Ea)
+                mq[st + r0 : st + r1, h] += scale * (wa @ np.abs(K[:kend]))
+                mk[st : st + kend, hk] += scale * (wa.T @ np.abs(Q[r0:r1]))
+                mv[st : st + kend, hk] += 2 * u * (Pa.T @ np.abs(dO[r0:r1]))
+                if S > 0:
+                    wb = u * np.abs(Pb * (dPb - rowdot[:, None])) + Pb * (2 * u * Dt[:, None] + Eb)
+                    mq[st + r0 : st + r1, h] += scale * np.sum(wb[:, :, None] * np.abs(KD), axis=1)
+                    mkd[st + r0 : st + r1, :S, hk] += scale * (Pb * (2 * u * Dt[:, None] + Eb))[:, :, None] * np.abs(
+                        Q[r0:r1])[:, None, :]
+    mvd = None if vd is None else np.zeros_like(vd)
+    if batch:
+        unflat = lambda x: None if x is None else x.reshape((B, T) + x.shape[1:])  # noqa: E731
+        mq, mk, mv, mkd, mvd = map(unflat, (mq, mk, mv, mkd, mvd))
+    return mq, mk, mv, mkd, mvd
+
+
+def check_grad_bf16(w, got, ref, mag, what, grad_bf16):
+    """bf16-input gradients: per element |got - ref| <= 2e-2 RMS(ref) + mag (the
+    first-order rounding magnitude), plus half a bf16 ulp for bf16 storage."""
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    if not got.size:
+        return 0.0, 0.0
+    rms = float(np.sqrt(np.mean(ref**2)))
+    e = TOL_BF16_REL_RMS * rms + mag
+    tol = e + (half_ulp_bf16(np.abs(ref) + e) if grad_bf16 else 0.0)
+    diff = np.abs(got - ref)
+    ratio = float(np.max(diff / tol))
+    assert ratio <= 1.0, f"{what}: max|got-ref| = {float(diff.max()):.3e}, worst error/bound = {ratio:.3f}"
+    return float(diff.max()), ratio

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moda_abi_version() == 2
+    assert L.moda_abi_version() == 3
 
 
 def test_status_codes_match_header():
@@ -152,6 +152,9 @@ def test_ctypes_signatures():
     assert len(L.moda_attn_decode.argtypes) == 21
     assert len(L.moda_attn_decode_workspace_size.argtypes) == 5
     assert L.moda_attn_decode_workspace_size.restype is ctypes.c_int64
+    assert len(L.moda_attn_bwd.argtypes) == 27
+    assert len(L.moda_attn_bwd_varlen.argtypes) == 29
+    assert len(L.moda_attn_bwd_workspace_size.argtypes) == 4
     assert L.moda_last_error.restype is ctypes.c_char_p
 
 
@@ -211,3 +214,87 @@ def test_decode_workspace_size():
     need = L.moda_attn_decode_workspace_size(1, 4, 2, 64, 32)
     assert calld(ws_bytes=need - 1) == 2
     assert "workspace" in err()
+
+
+BIG_WS = 1 << 40
+WS = 0x100000  # 256-byte aligned fake address
+
+
+def callb(ws=WS, ws_bytes=BIG_WS, dout=P, lse=P, dq=P, dk=P, dv=P, dkd=P, dvd=P, gdt=1, **kw):
+    a = dict(A)
+    a.update(kw)
+    L = _lib.lib()
+    return L.moda_attn_bwd(a["q"], a["k"], a["v"], a["kd"], a["vd"], a["out"], dout, lse, dq, dk, dv, dkd, dvd,
+                           a["dtype"], gdt, a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["Scap"], a["S"], a["causal"],
+                           a["scale"], ws, ws_bytes, None)
+
+
+def callbv(cu=P, n_seqs=2, N=16, max_len=8, ws=WS, ws_bytes=BIG_WS, **kw):
+    a = dict(A)
+    a.update(kw)
+    L = _lib.lib()
+    return L.moda_attn_bwd_varlen(a["q"], a["k"], a["v"], a["kd"], a["vd"], a["out"], P, P, P, P, P, P, P,
+                                  a["dtype"], 1, cu, n_seqs, N, max_len, a["Hq"], a["Hkv"], a["d"], a["Scap"], a["S"],
+                                  a["causal"], a["scale"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(dout=None), 1),
+        (dict(lse=None), 1),
+        (dict(dq=None), 1),
+        (dict(dk=None), 1),
+        (dict(dvd=None), 1),
+        (dict(out=None), 1),
+        (dict(ws=None), 1),
+        (dict(ws=WS + 16), 4),
+        (dict(ws_bytes=100), 2),
+        (dict(dv=P + 8), 4),
+        (dict(dkd=P + 4), 4),
+        (dict(lse=P + 2), 4),
+        (dict(gdt=5), 3),
+        (dict(dtype=0, gdt=1), 3),
+        (dict(Hq=34, Hkv=2), 5),
+        (dict(Hq=3, Hkv=2), 2),
+        (dict(d=96), 5),
+        (dict(S=5, Scap=4), 2),
+        (dict(scale=0.0), 7),
+        (dict(causal=3), 7),
+        (dict(B=-1), 2),
+    ],
+)
+def test_bwd_validation_rejects(kw, code):
+    assert callb(**kw) == code
+    assert err()
+
+
+def test_bwd_depth_grads_optional_without_slots():
+    # n_depth == 0 accepts NULL depth gradients; fail later on purpose (bad head_dim)
+    assert callb(kd=None, vd=None, dkd=None, dvd=None, S=0, Scap=0, d=96) == 5
+
+
+def test_bwd_empty_problems_are_ok_without_launch():
+    assert callb(B=0) == 0
+    assert callb(T=0, q=None) == 0
+    assert callbv(n_seqs=0) == 0
+    assert err() == ""
+
+
+@pytest.mark.parametrize("kw,code", [(dict(cu=None), 1), (dict(cu=P + 2), 4), (dict(max_len=17), 2),
+                                     (dict(n_seqs=-1), 2), (dict(d=32), 5)])
+def test_bwd_varlen_validation_rejects(kw, code):
+    assert callbv(**kw) == code
+    assert err()
+
+
+def test_bwd_workspace_size():
+    L = _lib.lib()
+    assert L.moda_attn_bwd_workspace_size(16, 4, 96, 2) == -1
+    assert L.moda_attn_bwd_workspace_size(-1, 4, 64, 2) == -1
+    assert L.moda_attn_bwd_workspace_size(0, 4, 64, 2) == 0
+    # fp32 delta [Hq, N], then the depth share of dq [N, Hq, d] when there are slots
+    assert L.moda_attn_bwd_workspace_size(64, 4, 64, 0) == 1024
+    assert L.moda_attn_bwd_workspace_size(64, 4, 64, 3) == 1024 + 64 * 4 * 64 * 4
+    need = L.moda_attn_bwd_workspace_size(16, 4, 64, 4)
+    assert callb(ws_bytes=need - 1) == 2 and "workspace" in err()

@@ -22,6 +22,7 @@ from . import gen
 
 # tensor ids used by the generator
 TID_Q, TID_K, TID_V, TID_KD, TID_VD = 1, 2, 3, 4, 5
+TID_DO = 6  # upstream gradient of out (backward)
 BATCH_TID_STRIDE = 16  # the i-th extra input batch uses tid + 16 * i
 
 
@@ -169,7 +170,7 @@ ORDER = ["tiny_f32", "small_bf16", "mha_bf16", "gqa_bf16", "packed_bf16"]
 
 def tids(batch_index: int = 0):
     o = BATCH_TID_STRIDE * batch_index
-    return dict(q=TID_Q + o, k=TID_K + o, v=TID_V + o, kd=TID_KD + o, vd=TID_VD + o)
+    return dict(q=TID_Q + o, k=TID_K + o, v=TID_V + o, kd=TID_KD + o, vd=TID_VD + o, do=TID_DO + o)
 
 
 def make_host(w: Workload, batch_index: int = 0) -> dict:
@@ -208,16 +209,29 @@ def make_device(w: Workload, device, batch_index: int = 0) -> dict:
     return out
 
 
-def host_slice(w: Workload, name: str, index_arrays, batch_index: int = 0) -> np.ndarray:
+def host_slice(w: Workload, name: str, index_arrays, batch_index: int = 0, bf16: bool = False) -> np.ndarray:
     """Regenerate selected elements of one input tensor on the host.
 
     ``index_arrays`` is a tuple of integer arrays (numpy fancy indexing over the
-    tensor's shape); the result has their broadcast shape.
+    tensor's shape); the result has their broadcast shape. The upstream gradient
+    "do" is stored in the gradient dtype: ``bf16`` says whether it is bfloat16.
     """
-    shape = {"q": w.shape_q(), "k": w.shape_kv(), "v": w.shape_kv(), "kd": w.shape_depth(), "vd": w.shape_depth()}[name]
+    shape = {"q": w.shape_q(), "k": w.shape_kv(), "v": w.shape_kv(), "kd": w.shape_depth(), "vd": w.shape_depth(),
+             "do": w.shape_q()}[name]
     mult = w.key_mult if name in ("k", "kd") else 1.0
     idx = np.ravel_multi_index(tuple(np.asarray(a, dtype=np.int64) for a in index_arrays), shape)
-    return gen.values_np(w.seed, tids(batch_index)[name], idx, mult, w.bf16)
+    rounded = bf16 if name == "do" else w.bf16
+    return gen.values_np(w.seed, tids(batch_index)[name], idx, mult, rounded)
+
+
+def make_dout_device(w: Workload, device, dtype, batch_index: int = 0):
+    """Upstream gradient of out (shape of q) for the backward, N(0, 1), in ``dtype``
+    (bfloat16 values are the float32 values rounded to nearest-even)."""
+    return gen.tensor_t(w.seed, tids(batch_index)["do"], w.shape_q(), dtype, device)
+
+
+def make_dout_host(w: Workload, bf16: bool, batch_index: int = 0) -> np.ndarray:
+    return gen.tensor_np(w.seed, tids(batch_index)["do"], w.shape_q(), 1.0, bf16)
 
 
 # ------------------------------------------------------------------------------ decode
