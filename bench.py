@@ -36,7 +36,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector
 CACHE_DEFEAT_BYTES = 768 << 20  # > 256 MB Infinity Cache + 8 x 4 MB L2
 KERNEL_SOURCES = ["moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_attn.hip", "moda_internal.h"]  # the forward path
-DECODE_SOURCES = ["moda_decode.hip", "moda_attn.hip", "moda_internal.h"]
+DECODE_SOURCES = ["moda_decode.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h"]
+BWD_SOURCES = ["moda_bwd.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h"]
+BWD_METRIC = "fused seq+depth attention bwd TFLOP/s (dq, dk, dv, dk_depth, dv_depth)"
 DECODE_METRIC = "MoDA decode step (joint seq+depth softmax, one token per sequence) HBM GB/s"
 
 
@@ -189,7 +191,7 @@ def write_traffic(w, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cmds)
         f.write("\n".join(lines) + "\n")
 
 
-def write_trace_summary(w, trace_dir, log_path, cmd) -> None:
+def write_trace_summary(w, trace_dir, log_path, cmd, backward=False) -> None:
     """Text summary of a rocprofv3 --kernel-trace --stats run of bench.py."""
     stats = _read_csv(os.path.join(trace_dir, "run_kernel_stats.csv"))
     bench_line = None
@@ -197,18 +199,20 @@ def write_trace_summary(w, trace_dir, log_path, cmd) -> None:
         for line in f:
             if line.startswith("{") and '"metric"' in line:
                 bench_line = json.loads(line)
-    kname = kernel_name(w)
-    row = next((r for r in stats if kname in r["Name"]), None)
-    if row is None or bench_line is None:
-        raise SystemExit(f"kernel {kname} or the bench line missing in {trace_dir}")
-    avg_us = float(row["AverageNs"]) / 1e3
+    if backward:  # a backward step is three kernels
+        parts = ["moda_bwd_prep_kernel", "moda_bwd_dq", "moda_bwd_dkv"]
+        kname = "backward (prep + dq + dk/dv kernels)"
+    elif _is_decode(w):  # a decode step is the partial kernel and the merge kernel
+        parts = [kernel_name(w), "moda_decode_merge_kernel"]
+        kname = kernel_name(w)
+    else:
+        parts = [kernel_name(w)]
+        kname = kernel_name(w)
+    rows = [next((r for r in stats if part in r["Name"]), None) for part in parts]
+    if any(r is None for r in rows) or bench_line is None:
+        raise SystemExit(f"kernels {parts} or the bench line missing in {trace_dir}")
     bench_us = bench_line["ms_per_step"] * 1e3
-    step_us = avg_us
-    if _is_decode(w):  # a decode step is the partial kernel and the merge kernel
-        merge = next((r for r in stats if "moda_decode_merge_kernel" in r["Name"]), None)
-        if merge is None:
-            raise SystemExit(f"merge kernel missing in {trace_dir}")
-        step_us += float(merge["AverageNs"]) / 1e3
+    step_us = sum(float(r["AverageNs"]) / 1e3 for r in rows)
     lines = [f"# rocprofv3 kernel trace: {kname} on {w.name} ({w.desc})", "",
              "Command (on the GPU host; R = repository root):", f"    {cmd}", "",
              "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
@@ -219,12 +223,13 @@ def write_trace_summary(w, trace_dir, log_path, cmd) -> None:
                      f"| {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} % |")
     lines += ["", f"bench.py (same run, HIP events over {bench_line['steps']} graph-replayed steps): "
                   f"{bench_us:.2f} us per step; trace average {step_us:.2f} us "
-                  + ("(partial + merge kernels) " if _is_decode(w) else "")
+                  + (f"(sum over {len(parts)} kernels) " if len(parts) > 1 else "")
                   + f"({100 * (bench_us / step_us - 1):+.1f} %).",
               f"value {bench_line['value']} {bench_line['unit']}; roofline {bench_line['roofline']['bound']} "
               f"{bench_line['roofline']['achieved']:.1f} {bench_line['roofline']['unit']} "
               f"(frac {bench_line['roofline']['frac']:.3f}); kernel sources sha {bench_line['kernel_source_sha']}."]
-    with open(os.path.join(ROOT, "profiles", f"{_summary_prefix(w)}_{w.name}_kernel_trace.txt"), "w") as f:
+    prefix = "moda_bwd" if backward else _summary_prefix(w)
+    with open(os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_kernel_trace.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
@@ -463,6 +468,164 @@ def bench_decode(args, w, dev) -> int:
     return 0 if replay_ok else 1
 
 
+def bench_backward(args, w, dev) -> int:
+    """One step = one backward call (prep/depth, dq and dk/dv kernels) over the
+    whole workload, with q, k, v, the depth slots, out, dout and lse resident in
+    HBM (out and lse from the library's forward), replayed as a HIP graph."""
+    import torch
+
+    from joint_sequence_depth_amd import attn_bwd, attn_fwd, bwd_workspace_size
+    from workloads import configs
+
+    gdt = torch.bfloat16 if w.bf16 else torch.float32
+    per_batch = 2 * w.total_bytes() + 2 * w.n_tokens * w.n_heads_q * w.head_dim * w.elem_bytes()
+    n_batches = max(1, min(8, math.ceil(CACHE_DEFEAT_BYTES / per_batch)))
+    print(f"# backward of {w.name}: {w.desc}; {n_batches} input batch(es)", file=sys.stderr, flush=True)
+    cu = torch.from_numpy(w.cu_seqlens()).to(dev) if w.varlen else None
+    max_len = max(w.lengths)
+    sets = []
+    for i in range(n_batches):
+        x = configs.make_device(w, dev, i)
+        out, lse = attn_fwd(x["q"], x["k"], x["v"], x["kd"], x["vd"], n_depth=w.n_depth, causal=w.causal,
+                            scale=w.scale, cu_seqlens=cu, max_seqlen=max_len, out_dtype=gdt)
+        dout = configs.make_dout_device(w, dev, gdt, i)
+        grads = (torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"]),
+                 None if x["kd"] is None else torch.zeros_like(x["kd"]),
+                 None if x["vd"] is None else torch.zeros_like(x["vd"]))
+        sets.append((x, out, dout, lse, grads))
+    ws = torch.empty(max(256, bwd_workspace_size(w.n_tokens, w.n_heads_q, w.head_dim, w.n_depth)), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, grads=None):
+        x, out, dout, lse, g = sets[i % n_batches]
+        return attn_bwd(x["q"], x["k"], x["v"], x["kd"], x["vd"], out, dout, lse, n_depth=w.n_depth, causal=w.causal,
+                        scale=w.scale, cu_seqlens=cu, max_seqlen=max_len, grads=grads or g, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_batches):
+        step(i)
+    torch.cuda.synchronize()
+    rough = (time.perf_counter() - t0) / n_batches
+    steps = args.steps or max(n_batches, int(2.0 / max(rough, 1e-6)))
+    steps = max(n_batches, (steps // n_batches) * n_batches)
+    stream = torch.cuda.current_stream(dev)
+    use_graph = not args.no_graph
+    graph = None
+    if use_graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n_batches):
+                step(i)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    if use_graph:
+        for _ in range(steps // n_batches):
+            graph.replay()
+    else:
+        for i in range(steps):
+            step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    sec = ms / 1e3
+
+    # the last replayed batch's gradients must equal an eager call's (bitwise)
+    last = (steps - 1) % n_batches
+    g_ref = tuple(None if t is None else torch.zeros_like(t) for t in sets[last][4])
+    step(last, grads=g_ref)
+    torch.cuda.synchronize()
+    replay_ok = all(a is None or torch.equal(a, b) for a, b in zip(sets[last][4], g_ref))
+    if not replay_ok:
+        print("error: timed replays differ from an eager call", file=sys.stderr)
+
+    # algorithmic work: dP, dS-weighted dQ and dK, and P-weighted dV over the same
+    # visible pairs and slots as the forward: twice the forward's products
+    flops = 2.0 * (w.seq_flops() + w.depth_flops())
+    tflops = flops / sec / 1e12
+    peak = PEAK_BF16_TFLOPS if w.bf16 else PEAK_F32_TFLOPS
+    rec = {
+        "metric": BWD_METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.bf16 else "f32",
+        "data": "synthetic (seeded counter-based N(0,1) quantile grid)",
+        "config": {"workload": w.name, "pass": "backward", "batch": w.batch, "seq_len": w.seqlen,
+                   "seqlens": list(w.seqlens) if w.varlen else None, "n_heads_q": w.n_heads_q,
+                   "n_heads_kv": w.n_heads_kv, "head_dim": w.head_dim, "n_depth": w.n_depth, "causal": w.causal,
+                   "input_batches": n_batches, "graph": use_graph},
+        "kernel": "moda_bwd_prep_kernel + moda_bwd_dq_kernel + moda_bwd_dkv_kernel" if w.bf16 else
+                  "moda_bwd_prep_kernel + moda_bwd_dq_f32_kernel + moda_bwd_dkv_f32_kernel",
+        "kernel_source_sha": kernel_source_sha(BWD_SOURCES),
+        "replay_matches_eager": replay_ok,
+        "roofline": {"bound": "mfma" if w.bf16 else "alu", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": tflops / peak, "traffic": None},
+        "cpu_baseline": None,
+    }
+    del sets, graph, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_backward(w, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0 if replay_ok else 1
+
+
+def cpu_baseline_backward(w, budget_s: float) -> dict:
+    """The fp64 oracle's backward on (segment, KV head) units of the workload."""
+    import numpy as np
+
+    import oracle
+    from parity_util import unit_operands
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [cores])
+    except Exception:
+        pass
+    units = [(s, hk) for s in range(len(w.lengths)) for hk in range(w.n_heads_kv)]
+    np.random.default_rng(0).shuffle(units)
+    flops = compute_s = 0.0
+    calls = 0
+    for s, hk in units:
+        ops = unit_operands(w, s, hk, w.bf16)
+        L = w.lengths[s]
+        pairs = L * (L + 1) / 2 if w.causal else L * L
+        unit_flops = 2.0 * (4.0 * w.head_dim * w.group * pairs + 4.0 * L * w.group * w.n_depth * w.head_dim)
+        t0 = time.perf_counter()
+        oracle.joint_attention_backward(*ops[:5], w.n_depth, ops[5], w.causal, w.scale)
+        compute_s += time.perf_counter() - t0
+        flops += unit_flops
+        calls += 1
+        if compute_s > budget_s:
+            break
+    return {"value": flops / compute_s / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{calls} of the {len(units)} (sequence, KV head) units of {w.name}, backward "
+                      f"({flops / 1e9:.2f} GFLOP in {compute_s:.1f} s; operands regenerated on the host, not timed)"}
+
+
 def _lead_index(w, s, L):
     import numpy as np
 
@@ -487,6 +650,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: about 2 s of GPU time)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="small_bf16")
+    ap.add_argument("--backward", action="store_true", help="time the backward pass of the workload instead")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
@@ -504,7 +668,8 @@ def main(argv=None) -> int:
 
         w = configs.WORKLOADS.get(args.workload) or configs.DECODE_WORKLOADS[args.workload]
         if args.summarize_trace:
-            write_trace_summary(w, args.summarize_trace[0], args.summarize_trace[1], " ".join(args.profile_cmd))
+            write_trace_summary(w, args.summarize_trace[0], args.summarize_trace[1], " ".join(args.profile_cmd),
+                                backward=args.backward)
         if args.write_traffic:
             write_traffic(w, *args.write_traffic, args.profile_cmd)
         return 0
@@ -541,6 +706,8 @@ def main(argv=None) -> int:
     if args.workload in configs.DECODE_WORKLOADS:
         return bench_decode(args, configs.DECODE_WORKLOADS[args.workload], dev)
     w = configs.WORKLOADS[args.workload]
+    if args.backward:
+        return bench_backward(args, w, dev)
     batch_bytes = w.total_bytes()
     n_batches = max(1, min(32, math.ceil(CACHE_DEFEAT_BYTES / batch_bytes)))
     print(f"# workload {w.name}: {w.desc}; {n_batches} input batch(es) of {batch_bytes / 1e6:.1f} MB", file=sys.stderr,
