@@ -52,6 +52,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBwdWaves = 4;   // waves per workgroup, all kernels
 constexpr int kBlk = 128;      // tokens (dq) or keys (dk/dv) per workgroup
 constexpr int kTile = 64;      // keys (dq) or tokens (dk/dv) staged per step
+#ifndef MODA_BWD_PAD
+#define MODA_BWD_PAD 16
+#endif
+constexpr int kPad = MODA_BWD_PAD;  // bytes of padding per staged LDS row
 
 #define MODA_BWD_TR_READ(a) __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bi16x4*)(a))
 
@@ -98,7 +102,46 @@ __device__ __forceinline__ int64_t lse_index(const BwdParams& p, int64_t n, int 
 // stays 16-byte aligned).
 __host__ __device__ constexpr int prep_wave_floats(int G, int D) { return G * D + ((2 * G + 3) & ~3); }
 
-template <int D, bool BF16, bool GF32>
+// 8 consecutive elements of a row as stored (bf16: one 16-byte word, fp32: two);
+// kept raw while the load is in flight and widened where it is used.
+template <bool BF16>
+struct Raw8 {
+  uint4 w[BF16 ? 1 : 2];
+};
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> load_raw8(const void* base, int64_t elem) {
+  Raw8<BF16> r;
+  if constexpr (BF16) {
+    r.w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem);
+    r.w[0] = p[0];
+    r.w[1] = p[1];
+  }
+  return r;
+}
+template <bool BF16>
+__device__ __forceinline__ void widen8(const Raw8<BF16>& r, float (&x)[8]) {
+  if constexpr (BF16) {
+    const uint32_t u[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(u[j] << 16);
+      x[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      x[4 * j] = __uint_as_float(r.w[j].x);
+      x[4 * j + 1] = __uint_as_float(r.w[j].y);
+      x[4 * j + 2] = __uint_as_float(r.w[j].z);
+      x[4 * j + 3] = __uint_as_float(r.w[j].w);
+    }
+  }
+}
+
+// G1: one query head per KV head, whose q and dout slices stay in registers.
+template <int D, bool BF16, bool GF32, bool G1>
 __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_prep_kernel(const BwdParams p) {
   constexpr int LPR = D / 8;
   constexpr int NGRP = 64 / LPR;
@@ -109,17 +152,38 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_prep_kernel(const Bwd
   if (item >= p.total_tokens * p.Hkv) return;  // no workgroup barrier below
   const int64_t n = item / p.Hkv;
   const int hk = (int)(item % p.Hkv);
-  const int G = p.G;
+  const int G = G1 ? 1 : p.G;
   float* dqd = dyn + (size_t)wave * prep_wave_floats(G, D);
   float* lse2s = dqd + G * D;
   float* dels = lse2s + G;
+  const int nb = p.n_depth > 0 ? (p.n_depth + NGRP - 1) / NGRP : 0;
 
+  // slot batch ib: slot ib * NGRP + grp (the last slot repeated past n_depth)
+  auto slot_elem = [&](int ib) __attribute__((always_inline)) {
+    int i = ib * NGRP + grp;
+    i = i < p.n_depth ? i : p.n_depth - 1;
+    return ((n * p.S_cap + i) * p.Hkv + hk) * D + 8 * cl;
+  };
+  Raw8<BF16> kdr[2], vdr[2];
+  if (nb > 0) {  // the first slot batch is in flight while delta is computed
+    kdr[0] = load_raw8<BF16>(p.kd, slot_elem(0));
+    vdr[0] = load_raw8<BF16>(p.vd, slot_elem(0));
+  }
+
+  float q1[8], do1[8], dq1[8];  // G1: the head's slices and its depth share of dq
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dq1[j] = 0.f;
   for (int g = 0; g < G; ++g) {
     const int h = hk * G + g;
     const int64_t e = (n * p.Hq + h) * D + 8 * cl;
     float o8[8], d8[8];
     load8<!GF32>(p.out, e, o8);
     load8<!GF32>(p.dout, e, d8);
+    if constexpr (G1) {
+      load8<BF16>(p.q, e, q1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) do1[j] = d8[j];
+    }
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) s = fmaf(o8[j], d8[j], s);
@@ -134,29 +198,32 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_prep_kernel(const Bwd
       for (int j = 0; j < 8; ++j) dqd[g * D + 8 * cl + j] = 0.f;
     }
   }
-  if (p.n_depth <= 0) return;
+  if (nb == 0) return;
   // LDS accesses of one wave complete in issue order: the values written above
   // are visible to every lane of the wave below.
   __builtin_amdgcn_wave_barrier();
 
   const float c2 = p.scale_log2, sc = p.scale;
-  const int nb = (p.n_depth + NGRP - 1) / NGRP;
-  for (int ib = 0; ib < nb; ++ib) {
-    const int i = ib * NGRP + grp;
-    const bool valid = i < p.n_depth;
-    const int ic = valid ? i : p.n_depth - 1;
-    const int64_t de = ((n * p.S_cap + ic) * p.Hkv + hk) * D + 8 * cl;
+  auto process = [&](int ib, const Raw8<BF16>& kr, const Raw8<BF16>& vr) __attribute__((always_inline)) {
+    const bool valid = ib * NGRP + grp < p.n_depth;
     float kd8[8], vd8[8], dk8[8], dv8[8];
-    load8<BF16>(p.kd, de, kd8);
-    load8<BF16>(p.vd, de, vd8);
+    widen8<BF16>(kr, kd8);
+    widen8<BF16>(vr, vd8);
 #pragma unroll
     for (int j = 0; j < 8; ++j) dk8[j] = dv8[j] = 0.f;
     for (int g = 0; g < G; ++g) {
-      const int h = hk * G + g;
-      const int64_t e = (n * p.Hq + h) * D + 8 * cl;
       float q8[8], do8[8];
-      load8<BF16>(p.q, e, q8);
-      load8<!GF32>(p.dout, e, do8);
+      if constexpr (G1) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          q8[j] = q1[j];
+          do8[j] = do1[j];
+        }
+      } else {
+        const int64_t e = (n * p.Hq + hk * G + g) * D + 8 * cl;
+        load8<BF16>(p.q, e, q8);
+        load8<!GF32>(p.dout, e, do8);
+      }
       float b = 0.f, dp = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -174,19 +241,47 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_prep_kernel(const Bwd
         dk8[j] = fmaf(ds, q8[j], dk8[j]);
         part[j] = ds * kd8[j];
       }
+      if constexpr (G1) {  // summed over slots in registers, over lane groups at the end
 #pragma unroll
-      for (int off = LPR; off < 64; off <<= 1)
+        for (int j = 0; j < 8; ++j) dq1[j] += part[j];
+      } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) part[j] += __shfl_xor(part[j], off);
-      if (grp == 0) {
+        for (int off = LPR; off < 64; off <<= 1)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) dqd[g * D + 8 * cl + j] += part[j];
+          for (int j = 0; j < 8; ++j) part[j] += __shfl_xor(part[j], off);
+        if (grp == 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dqd[g * D + 8 * cl + j] += part[j];
+        }
       }
     }
     if (valid) {
+      const int64_t de = slot_elem(ib);
       store_n<GF32, 8>(p.dkd, de, dk8);
       store_n<GF32, 8>(p.dvd, de, dv8);
     }
+  };
+  // two slot batches in flight: batch ib + 1 loads while batch ib is processed
+  for (int ib = 0; ib < nb; ib += 2) {
+    if (ib + 1 < nb) {
+      kdr[1] = load_raw8<BF16>(p.kd, slot_elem(ib + 1));
+      vdr[1] = load_raw8<BF16>(p.vd, slot_elem(ib + 1));
+    }
+    process(ib, kdr[0], vdr[0]);
+    if (ib + 1 >= nb) break;
+    if (ib + 2 < nb) {
+      kdr[0] = load_raw8<BF16>(p.kd, slot_elem(ib + 2));
+      vdr[0] = load_raw8<BF16>(p.vd, slot_elem(ib + 2));
+    }
+    process(ib + 1, kdr[1], vdr[1]);
+  }
+  if constexpr (G1) {
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dq1[j] += __shfl_xor(dq1[j], off);
+    if (grp == 0) store_n<true, 8>(p.dq_depth, (n * p.Hq + hk) * D + 8 * cl, dq1);
+    return;
   }
   __builtin_amdgcn_wave_barrier();
   // the G heads of this KV head are contiguous in dq_depth: G * D floats
@@ -232,14 +327,20 @@ __device__ __forceinline__ bbf16x8 tr_operand(const unsigned char* tile, int r0,
 }
 
 // ---------------------------------------------------------------- dq (bf16)
+#ifdef MODA_BWD_DQ_OCC1
+#define MODA_BWD_DQ_ATTR __attribute__((amdgpu_waves_per_eu(1, 1)))
+#else
+#define MODA_BWD_DQ_ATTR
+#endif
 template <int D, bool GF32>
-__global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(64 * kBwdWaves) MODA_BWD_DQ_ATTR void moda_bwd_dq_kernel(const BwdParams p) {
   constexpr int KC = D / 16, DT = D / 32;
-  constexpr int PITCH = D * 2 + 16;
+  constexpr int PITCH = D * 2 + kPad;
   constexpr int CPR = D * 2 / 16;                      // 16-byte chunks per row
   constexpr int NLD = kTile * CPR / (64 * kBwdWaves);  // chunks per thread per tile
-  __shared__ __align__(16) unsigned char ks[kTile * PITCH];
-  __shared__ __align__(16) unsigned char vs[kTile * PITCH];
+  // two buffers: the tile after next is stored while the current one is read
+  __shared__ __align__(16) unsigned char kbuf[2][kTile * PITCH];
+  __shared__ __align__(16) unsigned char vbuf[2][kTile * PITCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 31, hh = lane >> 5;
 
   int64_t rest = blockIdx.x;
@@ -289,21 +390,25 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dq_kernel(const BwdPa
       vreg[u] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + e);
     }
   };
-  auto sstore = [&]() __attribute__((always_inline)) {
+  auto sstore = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int idx = tid + 64 * kBwdWaves * u, row = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<uint4*>(ks + row * PITCH + 16 * ch) = kreg[u];
-      *reinterpret_cast<uint4*>(vs + row * PITCH + 16 * ch) = vreg[u];
+      *reinterpret_cast<uint4*>(kbuf[b] + row * PITCH + 16 * ch) = kreg[u];
+      *reinterpret_cast<uint4*>(vbuf[b] + row * PITCH + 16 * ch) = vreg[u];
     }
   };
 
+  // Tile kb is read from buffer kb % 2; tile kb + 1 arrives in registers during
+  // step kb and is stored into the other buffer, which every wave finished reading
+  // before the barrier that ended step kb - 1.
   gload(0);
+  sstore(0);
+  __syncthreads();
+  if (nkb > 1) gload(1);
   for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();  // every wave is done reading the previous tile
-    sstore();
-    __syncthreads();
-    if (kb + 1 < nkb) gload(kb + 1);
+    const unsigned char* ks = kbuf[kb & 1];
+    const unsigned char* vs = vbuf[kb & 1];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int64_t k0 = (int64_t)kb * kTile + 32 * st;
@@ -343,6 +448,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dq_kernel(const BwdPa
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<PITCH>(ks, 32 * st + 16 * part, dt, lane),
                                                             pk_b8(dsp + 4 * part), acc[dt], 0, 0, 0);
     }
+    if (kb + 1 < nkb) sstore((kb + 1) & 1);
+    __syncthreads();
+    if (kb + 2 < nkb) gload(kb + 2);
   }
 
   if (!row_ok) return;
@@ -370,13 +478,14 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dq_kernel(const BwdPa
 template <int D, bool GF32>
 __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdParams p) {
   constexpr int KC = D / 16, DT = D / 32;
-  constexpr int PITCH = D * 2 + 16;
+  constexpr int PITCH = D * 2 + kPad;
   constexpr int CPR = D * 2 / 16;
   constexpr int NLD = kTile * CPR / (64 * kBwdWaves);
-  __shared__ __align__(16) unsigned char qs[kTile * PITCH];
-  __shared__ __align__(16) unsigned char os[kTile * PITCH];  // dout
-  __shared__ __align__(16) float lse2s[kTile];
-  __shared__ __align__(16) float dels[kTile];
+  // two buffers: the tile after next is stored while the current one is read
+  __shared__ __align__(16) unsigned char qbuf[2][kTile * PITCH];
+  __shared__ __align__(16) unsigned char obuf[2][kTile * PITCH];  // dout
+  __shared__ __align__(16) float lbuf[2][kTile];
+  __shared__ __align__(16) float dbuf[2][kTile];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 31, hh = lane >> 5;
 
   int64_t rest = blockIdx.x;
@@ -434,25 +543,32 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdP
       dreg = p.delta[(int64_t)h * p.total_tokens + nq];
     }
   };
-  auto sstore = [&]() __attribute__((always_inline)) {
+  auto sstore = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int idx = tid + 64 * kBwdWaves * u, row = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<uint4*>(qs + row * PITCH + 16 * ch) = qreg[u];
-      *reinterpret_cast<uint4*>(os + row * PITCH + 16 * ch) = oreg[u];
+      *reinterpret_cast<uint4*>(qbuf[b] + row * PITCH + 16 * ch) = qreg[u];
+      *reinterpret_cast<uint4*>(obuf[b] + row * PITCH + 16 * ch) = oreg[u];
     }
     if (tid < kTile) {
-      lse2s[tid] = lreg;
-      dels[tid] = dreg;
+      lbuf[b][tid] = lreg;
+      dbuf[b][tid] = dreg;
     }
   };
 
-  if (nsteps > 0) gload(0);
+  // as in the dq kernel: step i reads buffer i % 2 while step i + 1's tile is
+  // stored into the other one
+  if (nsteps > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  if (nsteps > 1) gload(1);
   for (int step = 0; step < nsteps; ++step) {
-    __syncthreads();
-    sstore();
-    __syncthreads();
-    if (step + 1 < nsteps) gload(step + 1);
+    const unsigned char* qs = qbuf[step & 1];
+    const unsigned char* os = obuf[step & 1];
+    const float* lse2s = lbuf[step & 1];
+    const float* dels = dbuf[step & 1];
     const int64_t tq0 = tstart + (int64_t)(step % ntq) * kTile;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -501,6 +617,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdP
                                                             pk_b8(dsp + 4 * part), dka[dt], 0, 0, 0);
         }
     }
+    if (step + 1 < nsteps) sstore((step + 1) & 1);
+    __syncthreads();
+    if (step + 2 < nsteps) gload(step + 2);
   }
 
   if (!key_ok) return;
@@ -647,12 +766,17 @@ hipError_t launch_bwd_d(const BwdParams& p, bool bf16, bool grad_f32, hipStream_
   const dim3 block(64 * kBwdWaves);
   const size_t prep_lds = (size_t)kBwdWaves * prep_wave_floats(p.G, D) * sizeof(float);
   const dim3 prep_grid((unsigned)((p.total_tokens * p.Hkv + kBwdWaves - 1) / kBwdWaves));
-  if (bf16 && grad_f32)
-    hipLaunchKernelGGL((moda_bwd_prep_kernel<D, true, true>), prep_grid, block, prep_lds, stream, p);
-  else if (bf16)
-    hipLaunchKernelGGL((moda_bwd_prep_kernel<D, true, false>), prep_grid, block, prep_lds, stream, p);
-  else
-    hipLaunchKernelGGL((moda_bwd_prep_kernel<D, false, true>), prep_grid, block, prep_lds, stream, p);
+  const bool g1 = p.G == 1;
+  if (bf16 && grad_f32) {
+    if (g1) hipLaunchKernelGGL((moda_bwd_prep_kernel<D, true, true, true>), prep_grid, block, prep_lds, stream, p);
+    else hipLaunchKernelGGL((moda_bwd_prep_kernel<D, true, true, false>), prep_grid, block, prep_lds, stream, p);
+  } else if (bf16) {
+    if (g1) hipLaunchKernelGGL((moda_bwd_prep_kernel<D, true, false, true>), prep_grid, block, prep_lds, stream, p);
+    else hipLaunchKernelGGL((moda_bwd_prep_kernel<D, true, false, false>), prep_grid, block, prep_lds, stream, p);
+  } else {
+    if (g1) hipLaunchKernelGGL((moda_bwd_prep_kernel<D, false, true, true>), prep_grid, block, prep_lds, stream, p);
+    else hipLaunchKernelGGL((moda_bwd_prep_kernel<D, false, true, false>), prep_grid, block, prep_lds, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (bf16) {
