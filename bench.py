@@ -38,6 +38,8 @@ CACHE_DEFEAT_BYTES = 768 << 20  # > 256 MB Infinity Cache + 8 x 4 MB L2
 KERNEL_SOURCES = ["moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_attn.hip", "moda_internal.h"]  # the forward path
 DECODE_SOURCES = ["moda_decode.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h"]
 BWD_SOURCES = ["moda_bwd.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h"]
+WRITER_SOURCES = ["moda_depth_kv.hip", "moda_attn.hip", "moda_internal.h"]
+WRITER_METRIC = "depth-KV writer HBM GB/s (one layer's K/V rows into one slot of the depth cache)"
 BWD_METRIC = "fused seq+depth attention bwd TFLOP/s (dq, dk, dv, dk_depth, dv_depth)"
 DECODE_METRIC = "MoDA decode step (joint seq+depth softmax, one token per sequence) HBM GB/s"
 
@@ -191,7 +193,7 @@ def write_traffic(w, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cmds)
         f.write("\n".join(lines) + "\n")
 
 
-def write_trace_summary(w, trace_dir, log_path, cmd, backward=False) -> None:
+def write_trace_summary(w, trace_dir, log_path, cmd, backward=False, writer=False) -> None:
     """Text summary of a rocprofv3 --kernel-trace --stats run of bench.py."""
     stats = _read_csv(os.path.join(trace_dir, "run_kernel_stats.csv"))
     bench_line = None
@@ -202,6 +204,9 @@ def write_trace_summary(w, trace_dir, log_path, cmd, backward=False) -> None:
     if backward:  # a backward step is three kernels
         parts = ["moda_bwd_prep_kernel", "moda_bwd_dq", "moda_bwd_dkv"]
         kname = "backward (prep + dq + dk/dv kernels)"
+    elif writer:
+        parts = ["moda_depth_kv_write_kernel"]
+        kname = parts[0]
     elif _is_decode(w):  # a decode step is the partial kernel and the merge kernel
         parts = [kernel_name(w), "moda_decode_merge_kernel"]
         kname = kernel_name(w)
@@ -228,7 +233,7 @@ def write_trace_summary(w, trace_dir, log_path, cmd, backward=False) -> None:
               f"value {bench_line['value']} {bench_line['unit']}; roofline {bench_line['roofline']['bound']} "
               f"{bench_line['roofline']['achieved']:.1f} {bench_line['roofline']['unit']} "
               f"(frac {bench_line['roofline']['frac']:.3f}); kernel sources sha {bench_line['kernel_source_sha']}."]
-    prefix = "moda_bwd" if backward else _summary_prefix(w)
+    prefix = "moda_bwd" if backward else "moda_depth_kv" if writer else _summary_prefix(w)
     with open(os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_kernel_trace.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -626,6 +631,75 @@ def cpu_baseline_backward(w, budget_s: float) -> dict:
                       f"({flops / 1e9:.2f} GFLOP in {compute_s:.1f} s; operands regenerated on the host, not timed)"}
 
 
+def bench_writer(args, w, dev) -> int:
+    """One step = one depth-KV write: every token's K and V rows of the workload
+    into one slot of its depth cache (slots cycling over S_cap, as a layer stack or
+    a bounded ring buffer writes them)."""
+    import torch
+
+    from joint_sequence_depth_amd import depth_kv_write
+    from workloads import configs
+
+    dt = torch.bfloat16 if w.bf16 else torch.float32
+    x = configs.make_device(w, dev)
+    S_cap = max(1, w.s_cap)
+    kd = torch.zeros(w.shape_depth()[:-3] + (S_cap, w.n_heads_kv, w.head_dim), dtype=dt, device=dev)
+    vd = torch.zeros_like(kd)
+    torch.cuda.synchronize()
+
+    def step(i):
+        depth_kv_write(x["k"], x["v"], kd, vd, i % S_cap)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    steps = args.steps or 200
+    steps = max(S_cap, steps // S_cap * S_cap)
+    stream = torch.cuda.current_stream(dev)
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(S_cap):
+                step(i)
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    if graph is not None:
+        for _ in range(steps // S_cap):
+            graph.replay()
+    else:
+        for i in range(steps):
+            step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    ok = bool(torch.equal(kd[..., S_cap - 1, :, :], x["k"]) and torch.equal(vd[..., 0, :, :], x["v"]))
+    nbytes = 4.0 * w.n_tokens * w.n_heads_kv * w.head_dim * w.elem_bytes()
+    gbs = nbytes / (ms / 1e3) / 1e9
+    rec = {
+        "metric": WRITER_METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.bf16 else "f32",
+        "data": "synthetic (seeded counter-based N(0,1) quantile grid)",
+        "config": {"workload": w.name, "pass": "depth-kv writer", "tokens": w.n_tokens, "n_heads_kv": w.n_heads_kv,
+                   "head_dim": w.head_dim, "depth_capacity": S_cap, "graph": graph is not None},
+        "kernel": "moda_depth_kv_write_kernel", "kernel_source_sha": kernel_source_sha(WRITER_SOURCES),
+        "copies_match": ok,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0 if ok else 1
+
+
 def _lead_index(w, s, L):
     import numpy as np
 
@@ -651,6 +725,7 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="small_bf16")
     ap.add_argument("--backward", action="store_true", help="time the backward pass of the workload instead")
+    ap.add_argument("--writer", action="store_true", help="time the depth-KV writer on the workload's shapes instead")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
@@ -669,7 +744,7 @@ def main(argv=None) -> int:
         w = configs.WORKLOADS.get(args.workload) or configs.DECODE_WORKLOADS[args.workload]
         if args.summarize_trace:
             write_trace_summary(w, args.summarize_trace[0], args.summarize_trace[1], " ".join(args.profile_cmd),
-                                backward=args.backward)
+                                backward=args.backward, writer=args.writer)
         if args.write_traffic:
             write_traffic(w, *args.write_traffic, args.profile_cmd)
         return 0
@@ -708,6 +783,8 @@ def main(argv=None) -> int:
     w = configs.WORKLOADS[args.workload]
     if args.backward:
         return bench_backward(args, w, dev)
+    if args.writer:
+        return bench_writer(args, w, dev)
     batch_bytes = w.total_bytes()
     n_batches = max(1, min(32, math.ceil(CACHE_DEFEAT_BYTES / batch_bytes)))
     print(f"# workload {w.name}: {w.desc}; {n_batches} input batch(es) of {batch_bytes / 1e6:.1f} MB", file=sys.stderr,

@@ -1,6 +1,6 @@
 /*
  * moda_attn.h - C ABI of the MoDA joint sequence/depth attention (forward,
- * backward and decode step) on AMD Instinct MI355X (gfx950).
+ * backward, decode step and depth-KV writer) on AMD Instinct MI355X (gfx950).
  *
  * Operator: "Mixture-of-Depths Attention" (arXiv 2603.15619), MoDA deck slide
  * "One denominator allocates probability across both memories" (teaching form of
@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MODA_ABI_VERSION 3
+#define MODA_ABI_VERSION 4
 
 /* status codes */
 #define MODA_OK 0
@@ -181,6 +181,32 @@ int moda_attn_bwd_varlen(const void* q, const void* k, const void* v, const void
 /* Workspace bytes the backward needs for N = total tokens (B * T), or -1 for
  * invalid sizes. */
 int64_t moda_attn_bwd_workspace_size(int64_t total_tokens, int32_t n_heads_q, int32_t head_dim, int32_t n_depth);
+
+/*
+ * Depth-KV writer: stores one layer's key and value rows of every token into
+ * slot `slot` of the depth cache that later layers read (MoDA deck, slide "Reuse
+ * attention KV; add a projection for FFN inputs": a layer's attention KV is kept
+ * for later layers; the FFN input's KV projection fills further slots, written
+ * with the same call from the projection's output).
+ *
+ *   k_src, v_src       [N, Hkv, d]            (batch layout: N = B * T)
+ *   k_depth, v_depth   [N, S_cap, Hkv, d]     slot `slot` of every token is overwritten
+ *
+ * All in `dtype`; 0 <= slot < depth_capacity (S_cap); Hkv * d * element bytes a
+ * multiple of 16; all pointers 16-byte aligned, device memory owned by the
+ * caller; sources and destinations must not overlap. Nothing else is written.
+ * A bounded slot buffer (the paper's future work, as the deck quotes it on slide
+ * "The main open cost is retaining and reading depth history") writes entry w to
+ * slot w mod S_cap and reads n_depth = min(w + 1, S_cap) slots: the joint softmax
+ * is invariant to the order of its keys, so that is a sliding window over the
+ * most recent S_cap entries. A window [o, o + n) of a longer slot axis is read by
+ * passing k_depth + o * Hkv * d (and v_depth likewise) with the same
+ * depth_capacity and n_depth = n, o + n <= S_cap.
+ * n_tokens == 0 returns MODA_OK with no launch.
+ */
+int moda_depth_kv_write(const void* k_src, const void* v_src, void* k_depth, void* v_depth, int32_t dtype,
+                        int64_t n_tokens, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t slot,
+                        void* stream);
 
 /* Description of the last non-OK status returned on the calling thread ("" if none). */
 const char* moda_last_error(void);

@@ -1,5 +1,5 @@
-"""MoDA joint sequence/depth attention on MI355X (gfx950): forward, backward and
-decode step.
+"""MoDA joint sequence/depth attention on MI355X (gfx950): forward, backward,
+decode step and depth-KV writer.
 
 The computation lives in libmoda_attn.so (hand-written HIP kernels behind the C
 ABI declared in include/moda_attn.h); this package only marshals torch tensors.
@@ -12,8 +12,9 @@ from ._lib import (  # noqa: F401
     attn_fwd,
     bwd_workspace_size,
     decode_workspace_size,
+    depth_kv_write,
     lib,
 )
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "bwd_workspace_size", "decode_workspace_size", "lib", "ModaError",
-           "EXPORTS"]
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "depth_kv_write", "bwd_workspace_size", "decode_workspace_size",
+           "lib", "ModaError", "EXPORTS"]

@@ -30,8 +30,8 @@ STATUS_NAMES = {
 
 # every symbol include/moda_attn.h declares
 EXPORTS = ("moda_attn_fwd", "moda_attn_fwd_varlen", "moda_attn_decode", "moda_attn_decode_workspace_size",
-           "moda_attn_bwd", "moda_attn_bwd_varlen", "moda_attn_bwd_workspace_size", "moda_last_error",
-           "moda_abi_version")
+           "moda_attn_bwd", "moda_attn_bwd_varlen", "moda_attn_bwd_workspace_size", "moda_depth_kv_write",
+           "moda_last_error", "moda_abi_version")
 
 _lib = None
 
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.moda_attn_bwd_varlen.restype = ctypes.c_int
         L.moda_attn_bwd_workspace_size.argtypes = [i64, i32, i32, i32]
         L.moda_attn_bwd_workspace_size.restype = ctypes.c_int64
+        L.moda_depth_kv_write.argtypes = [vp] * 4 + [i32, i64, i32, i32, i32, i32, vp]
+        L.moda_depth_kv_write.restype = ctypes.c_int
         L.moda_last_error.argtypes = []
         L.moda_last_error.restype = ctypes.c_char_p
         L.moda_abi_version.argtypes = []
@@ -83,6 +85,18 @@ def _check(status: int):
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def _window(k_depth, v_depth, slot_offset: int, n_depth: int, s_cap: int, row_elems: int):
+    """Depth base pointers of the slot window [slot_offset, slot_offset + n_depth)."""
+    if k_depth is None:
+        if slot_offset:
+            raise ValueError("slot_offset needs depth tensors")
+        return None, None
+    if slot_offset < 0 or n_depth < 0 or slot_offset + n_depth > s_cap:
+        raise ValueError(f"slot window [{slot_offset}, {slot_offset + n_depth}) exceeds S_cap = {s_cap}")
+    off = slot_offset * row_elems * k_depth.element_size()
+    return k_depth.data_ptr() + off, v_depth.data_ptr() + off
 
 
 def _dtype_code(t) -> int:
@@ -111,6 +125,7 @@ def attn_fwd(
     stream=None,
     out_dtype=None,
     return_lse: bool = True,
+    slot_offset: int = 0,
 ):
     """MoDA joint sequence/depth attention forward through the C ABI.
 
@@ -121,6 +136,8 @@ def attn_fwd(
     depth tensors); ``scale`` to 1/sqrt(d). ``out_dtype`` (torch.float32 is allowed
     for bfloat16 inputs) defaults to q's dtype, or to ``out``'s when it is given.
     With ``return_lse=False`` no lse is written (NULL at the C ABI) and None is returned.
+    ``slot_offset`` reads the window of slots [slot_offset, slot_offset + n_depth)
+    (the depth base pointers move by that many slots; the slot stride stays S_cap).
     """
     import torch
 
@@ -150,7 +167,8 @@ def attn_fwd(
     else:
         s_cap = 0
     if n_depth is None:
-        n_depth = s_cap
+        n_depth = s_cap - slot_offset
+    kd_ptr, vd_ptr = _window(k_depth, v_depth, slot_offset, n_depth, s_cap, Hkv * d)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out_dtype is None:
@@ -184,13 +202,13 @@ def attn_fwd(
             cu_host = cu_seqlens.cpu()
             max_seqlen = int((cu_host[1:] - cu_host[:-1]).max()) if n_seqs > 0 else 0
         status = L.moda_attn_fwd_varlen(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(k_depth), _ptr(v_depth), _ptr(out), _ptr(lse),
+            _ptr(q), _ptr(k), _ptr(v), kd_ptr, vd_ptr, _ptr(out), _ptr(lse),
             code, out_code, _ptr(cu_seqlens), n_seqs, q.shape[0], int(max_seqlen), Hq, Hkv, d, s_cap, int(n_depth),
             int(bool(causal)), float(scale), stream,
         )
     else:
         status = L.moda_attn_fwd(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(k_depth), _ptr(v_depth), _ptr(out), _ptr(lse),
+            _ptr(q), _ptr(k), _ptr(v), kd_ptr, vd_ptr, _ptr(out), _ptr(lse),
             code, out_code, q.shape[0], q.shape[1], Hq, Hkv, d, s_cap, int(n_depth), int(bool(causal)), float(scale), stream,
         )
     _check(status)
@@ -388,3 +406,29 @@ def attn_bwd(
                                  int(bool(causal)), float(scale), _ptr(workspace), wsb, stream)
     _check(status)
     return dq, dk, dv, dkd, dvd
+
+
+def depth_kv_write(k_src, v_src, k_depth, v_depth, slot: int, stream=None):
+    """Store k_src/v_src ([B,T,Hkv,d] or [N,Hkv,d]) into slot ``slot`` of the depth
+    cache k_depth/v_depth ([B,T,S_cap,Hkv,d] or [N,S_cap,Hkv,d]) in place. For a
+    bounded slot buffer pass slot = w % S_cap for the w-th entry written."""
+    import torch
+
+    for t in (k_src, v_src, k_depth, v_depth):
+        if not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError("all tensors must be contiguous GPU tensors")
+    if k_src.shape != v_src.shape or k_depth.shape != v_depth.shape:
+        raise ValueError("k and v tensors must match in shape")
+    lead = k_src.dim() - 2
+    if k_depth.dim() != lead + 3 or k_depth.shape[:lead] != k_src.shape[:lead] or k_depth.shape[-2:] != k_src.shape[-2:]:
+        raise ValueError(f"depth cache must be [..., S_cap, Hkv, d] for sources {tuple(k_src.shape)}")
+    if len({t.dtype for t in (k_src, v_src, k_depth, v_depth)}) != 1:
+        raise TypeError("all tensors must share one dtype")
+    n = 1
+    for x in k_src.shape[:lead]:
+        n *= x
+    if stream is None:
+        stream = torch.cuda.current_stream(k_src.device).cuda_stream
+    _check(lib().moda_depth_kv_write(_ptr(k_src), _ptr(v_src), _ptr(k_depth), _ptr(v_depth), _dtype_code(k_src), n,
+                                     k_src.shape[-2], k_src.shape[-1], k_depth.shape[lead], int(slot), stream))
+    return k_depth, v_depth

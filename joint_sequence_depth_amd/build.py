@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmoda_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["moda_attn.hip", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_decode.hip", "moda_bwd.hip"]
+SOURCES = ["moda_attn.hip", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_decode.hip", "moda_bwd.hip",
+           "moda_depth_kv.hip"]
 # Sources whose kernels keep matrix-core accumulators in AGPRs (the backward
 # holds two 128 x 32 fp32 accumulators per wave, more than the VGPRs alone)
 AGPR_ACCUMULATORS = {"moda_bwd.hip"}

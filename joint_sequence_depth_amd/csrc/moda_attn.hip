@@ -430,6 +430,30 @@ int moda_attn_bwd_varlen(const void* q, const void* k, const void* v, const void
   return launch_bwd_checked(p, a, n_seqs, max_seqlen, static_cast<hipStream_t>(stream));
 }
 
+int moda_depth_kv_write(const void* k_src, const void* v_src, void* k_depth, void* v_depth, int32_t dtype,
+                        int64_t n_tokens, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t slot,
+                        void* stream) {
+  if (n_tokens < 0) return fail(MODA_ERR_SHAPE, "n_tokens must be >= 0");
+  if (n_tokens == 0) {
+    g_err[0] = '\0';
+    return MODA_OK;
+  }
+  if (!k_src || !v_src || !k_depth || !v_depth) return fail(MODA_ERR_NULL, "all four tensors must be non-NULL");
+  if (dtype != MODA_DTYPE_F32 && dtype != MODA_DTYPE_BF16) return fail(MODA_ERR_DTYPE, "unknown dtype code %d", dtype);
+  if (n_heads_kv < 1 || head_dim < 1) return fail(MODA_ERR_SHAPE, "n_heads_kv and head_dim must be >= 1");
+  if (depth_capacity < 1 || slot < 0 || slot >= depth_capacity)
+    return fail(MODA_ERR_SHAPE, "need 0 <= slot (%d) < depth_capacity (%d)", slot, depth_capacity);
+  const int64_t row_bytes = (int64_t)n_heads_kv * head_dim * (dtype == MODA_DTYPE_BF16 ? 2 : 4);
+  if (row_bytes % 16) return fail(MODA_ERR_SHAPE, "n_heads_kv * head_dim * element bytes must be a multiple of 16");
+  if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_depth) || !aligned16(v_depth))
+    return fail(MODA_ERR_ALIGN, "all four tensors must be 16-byte aligned");
+  moda::DepthWriteParams p{k_src, v_src, k_depth, v_depth, n_tokens, row_bytes / 16, depth_capacity, slot};
+  const hipError_t err = moda::launch_depth_kv_write(p, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(MODA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  g_err[0] = '\0';
+  return MODA_OK;
+}
+
 const char* moda_last_error(void) { return g_err; }
 
 int32_t moda_abi_version(void) { return MODA_ABI_VERSION; }

@@ -97,6 +97,19 @@ struct BwdParams {
 
 hipError_t launch_bwd(const BwdParams& p, int head_dim, bool bf16, bool grad_f32, hipStream_t stream);
 
+// Depth-KV writer (moda_depth_kv.hip): rows of row_vecs 16-byte vectors per token.
+struct DepthWriteParams {
+  const void* k_src;
+  const void* v_src;
+  void* k_depth;
+  void* v_depth;
+  int64_t n_tokens;
+  int64_t row_vecs;  // H_kv * d * element bytes / 16
+  int32_t S_cap;
+  int32_t slot;
+};
+hipError_t launch_depth_kv_write(const DepthWriteParams& p, hipStream_t stream);
+
 // One decode step (one new token per sequence); see moda_decode.hip.
 // Element offsets: q, out: (b * Hq + h) * D + c; caches: ((b * T_max + j) * Hkv + hk) * D + c;
 // depth: ((b * S_cap + i) * Hkv + hk) * D + c; lse: b * Hq + h.

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moda_abi_version() == 3
+    assert L.moda_abi_version() == 4
 
 
 def test_status_codes_match_header():
@@ -155,6 +155,7 @@ def test_ctypes_signatures():
     assert len(L.moda_attn_bwd.argtypes) == 27
     assert len(L.moda_attn_bwd_varlen.argtypes) == 29
     assert len(L.moda_attn_bwd_workspace_size.argtypes) == 4
+    assert len(L.moda_depth_kv_write.argtypes) == 11
     assert L.moda_last_error.restype is ctypes.c_char_p
 
 
@@ -298,3 +299,32 @@ def test_bwd_workspace_size():
     assert L.moda_attn_bwd_workspace_size(64, 4, 64, 3) == 1024 + 64 * 4 * 64 * 4
     need = L.moda_attn_bwd_workspace_size(16, 4, 64, 4)
     assert callb(ws_bytes=need - 1) == 2 and "workspace" in err()
+
+
+def callw(ks=P, vs=P, kd=P, vd=P, dtype=1, N=16, Hkv=2, d=64, Scap=4, slot=1):
+    return _lib.lib().moda_depth_kv_write(ks, vs, kd, vd, dtype, N, Hkv, d, Scap, slot, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(ks=None), 1),
+        (dict(vd=None), 1),
+        (dict(dtype=7), 3),
+        (dict(slot=4), 2),
+        (dict(slot=-1), 2),
+        (dict(Scap=0, slot=0), 2),
+        (dict(Hkv=0), 2),
+        (dict(N=-1), 2),
+        (dict(Hkv=1, d=4), 2),  # 8-byte rows
+        (dict(kd=P + 8), 4),
+    ],
+)
+def test_writer_validation_rejects(kw, code):
+    assert callw(**kw) == code
+    assert err()
+
+
+def test_writer_empty_is_ok():
+    assert callw(N=0, ks=None) == 0
+    assert err() == ""
