@@ -98,10 +98,6 @@ __device__ __forceinline__ int64_t lse_index(const BwdParams& p, int64_t n, int 
 }
 
 // ---------------------------------------------------------------- prep + depth
-// LDS floats per wave of the prep kernel (a multiple of 4, so each wave's block
-// stays 16-byte aligned).
-__host__ __device__ constexpr int prep_wave_floats(int G, int D) { return G * D + ((2 * G + 3) & ~3); }
-
 // 8 consecutive elements of a row as stored (bf16: one 16-byte word, fp32: two);
 // kept raw while the load is in flight and widened where it is used.
 template <bool BF16>
@@ -140,154 +136,179 @@ __device__ __forceinline__ void widen8(const Raw8<BF16>& r, float (&x)[8]) {
   }
 }
 
-// G1: one query head per KV head, whose q and dout slices stay in registers.
-template <int D, bool BF16, bool GF32, bool G1>
-__global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_prep_kernel(const BwdParams p) {
-  constexpr int LPR = D / 8;
-  constexpr int NGRP = 64 / LPR;
-  extern __shared__ float dyn[];  // per wave: dq_depth [G][D], lse2 [G], delta [G]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int grp = lane / LPR, cl = lane % LPR;
-  const int64_t item = (int64_t)blockIdx.x * kBwdWaves + wave;
-  if (item >= p.total_tokens * p.Hkv) return;  // no workgroup barrier below
-  const int64_t n = item / p.Hkv;
-  const int hk = (int)(item % p.Hkv);
-  const int G = G1 ? 1 : p.G;
-  float* dqd = dyn + (size_t)wave * prep_wave_floats(G, D);
-  float* lse2s = dqd + G * D;
-  float* dels = lse2s + G;
-  const int nb = p.n_depth > 0 ? (p.n_depth + NGRP - 1) / NGRP : 0;
+// Prep and depth: one wave per (token, block of NGRP consecutive KV heads); lane
+// group grp (LPR = D / 8 lanes, 8 elements each) owns KV head hb * NGRP + grp and
+// its G query heads. A step handles one slot for all the wave's KV heads, so each
+// load is NGRP consecutive rows of the slot (one contiguous run of the depth
+// cache); kPrepRing slots are in flight. Nothing crosses lane groups: dk_depth and
+// dv_depth sum the G heads in registers, and the depth share of dq sums the slots
+// in registers (GC = G in {1, 2, 4}) or in the group's own LDS block (GC = 0: any
+// G). Lane groups past the last KV head repeat it: they compute the same values
+// and store them to the same places, so no store needs a branch. The main loop
+// is straight-line (prefetches of slots past the end re-read the last slot), so
+// every wait covers exactly the load it needs.
+template <int D>
+__host__ __device__ constexpr int prep_ngrp() { return 64 / (D / 8); }
+// LDS floats per wave for GC = 0: dq share [NGRP][G][D], then lse2 and delta [NGRP][G]
+__host__ __device__ constexpr int prep_wave_floats(int G, int D) { return (64 / (D / 8)) * G * (D + 2); }
+constexpr int kPrepMaxLds = 64 * 1024;
+constexpr int kPrepRing = 4;  // slots in flight per wave
 
-  // slot batch ib: slot ib * NGRP + grp (the last slot repeated past n_depth)
-  auto slot_elem = [&](int ib) __attribute__((always_inline)) {
-    int i = ib * NGRP + grp;
-    i = i < p.n_depth ? i : p.n_depth - 1;
+template <int D, bool BF16, bool GF32, int GC>
+__global__ __launch_bounds__(256) void moda_bwd_prep_kernel(const BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int NGRP = prep_ngrp<D>();
+  constexpr bool REG = GC > 0;    // the G heads' state in registers
+  constexpr int GR = REG ? GC : 1;  // register copies
+  extern __shared__ float dyn[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
+  const int grp = lane / LPR, cl = lane % LPR;
+  const int n_hb = (p.Hkv + NGRP - 1) / NGRP;
+  const int64_t item = (int64_t)blockIdx.x * wpb + wave;
+  if (item >= p.total_tokens * n_hb) return;  // no workgroup barrier below
+  const int64_t n = item / n_hb;
+  const int hk_raw = (int)(item % n_hb) * NGRP + grp;
+  const int hk = hk_raw < p.Hkv ? hk_raw : p.Hkv - 1;
+  const int G = REG ? GC : p.G;
+  float* dqd = dyn + (size_t)wave * prep_wave_floats(G, D) + (size_t)grp * G * D;  // [G][D], GC = 0
+  float* lse2s = dyn + (size_t)wave * prep_wave_floats(G, D) + (size_t)NGRP * G * D + 2 * grp * G;
+  float* dels = lse2s + G;
+  const int S = p.n_depth;
+  auto slot_elem = [&](int i) __attribute__((always_inline)) {
+    i = i < S ? i : S - 1;
     return ((n * p.S_cap + i) * p.Hkv + hk) * D + 8 * cl;
   };
-  Raw8<BF16> kdr[2], vdr[2];
-  if (nb > 0) {  // the first slot batch is in flight while delta is computed
-    kdr[0] = load_raw8<BF16>(p.kd, slot_elem(0));
-    vdr[0] = load_raw8<BF16>(p.vd, slot_elem(0));
+  Raw8<BF16> kr[kPrepRing], vr[kPrepRing];
+  if (S > 0) {  // the first slots are in flight while delta is computed
+#pragma unroll
+    for (int j = 0; j < kPrepRing - 1; ++j) {
+      kr[j] = load_raw8<BF16>(p.kd, slot_elem(j));
+      vr[j] = load_raw8<BF16>(p.vd, slot_elem(j));
+    }
   }
 
-  float q1[8], do1[8], dq1[8];  // G1: the head's slices and its depth share of dq
-#pragma unroll
-  for (int j = 0; j < 8; ++j) dq1[j] = 0.f;
+  Raw8<BF16> qr[GR];
+  Raw8<!GF32> dor[GR];
+  float dqr[GR][8], lr[GR], dr[GR];
   for (int g = 0; g < G; ++g) {
     const int h = hk * G + g;
     const int64_t e = (n * p.Hq + h) * D + 8 * cl;
     float o8[8], d8[8];
     load8<!GF32>(p.out, e, o8);
     load8<!GF32>(p.dout, e, d8);
-    if constexpr (G1) {
-      load8<BF16>(p.q, e, q1);
+    float sdo = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) do1[j] = d8[j];
-    }
-    float s = 0.f;
+    for (int j = 0; j < 8; ++j) sdo = fmaf(o8[j], d8[j], sdo);
+    sdo = group_sum<LPR>(sdo);
+    const float l2 = p.lse[lse_index(p, n, h)] * kLog2e;
+    if (cl == 0) p.delta[(int64_t)h * p.total_tokens + n] = sdo;
+    if constexpr (REG) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s = fmaf(o8[j], d8[j], s);
-    s = group_sum<LPR>(s);
-    if (lane == 0) {
-      p.delta[(int64_t)h * p.total_tokens + n] = s;
-      dels[g] = s;
-      lse2s[g] = p.lse[lse_index(p, n, h)] * kLog2e;
-    }
-    if (grp == 0) {
+      for (int gg = 0; gg < GR; ++gg)
+        if (gg == g) {
+          qr[gg] = load_raw8<BF16>(p.q, e);
+          dor[gg] = load_raw8<!GF32>(p.dout, e);
+          lr[gg] = l2;
+          dr[gg] = sdo;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dqr[gg][j] = 0.f;
+        }
+    } else {
+      if (cl == 0) {
+        lse2s[g] = l2;
+        dels[g] = sdo;
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) dqd[g * D + 8 * cl + j] = 0.f;
     }
   }
-  if (nb == 0) return;
+  if (S <= 0) return;
   // LDS accesses of one wave complete in issue order: the values written above
   // are visible to every lane of the wave below.
   __builtin_amdgcn_wave_barrier();
 
   const float c2 = p.scale_log2, sc = p.scale;
-  auto process = [&](int ib, const Raw8<BF16>& kr, const Raw8<BF16>& vr) __attribute__((always_inline)) {
-    const bool valid = ib * NGRP + grp < p.n_depth;
-    float kd8[8], vd8[8], dk8[8], dv8[8];
-    widen8<BF16>(kr, kd8);
-    widen8<BF16>(vr, vd8);
+  // one head's contribution of slot (kd8, vd8)
+  auto head = [&](const float (&q8)[8], const float (&do8)[8], float l2, float dl, const float (&kd8)[8],
+                  const float (&vd8)[8], float (&dk8)[8], float (&dv8)[8], float (&dq8)[8])
+                  __attribute__((always_inline)) {
+    float b = 0.f, dp = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dk8[j] = dv8[j] = 0.f;
-    for (int g = 0; g < G; ++g) {
-      float q8[8], do8[8];
-      if constexpr (G1) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          q8[j] = q1[j];
-          do8[j] = do1[j];
-        }
-      } else {
-        const int64_t e = (n * p.Hq + hk * G + g) * D + 8 * cl;
-        load8<BF16>(p.q, e, q8);
-        load8<!GF32>(p.dout, e, do8);
-      }
-      float b = 0.f, dp = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        b = fmaf(q8[j], kd8[j], b);
-        dp = fmaf(do8[j], vd8[j], dp);
-      }
-      b = group_sum<LPR>(b);
-      dp = group_sum<LPR>(dp);
-      const float pr = valid ? __builtin_amdgcn_exp2f(b * c2 - lse2s[g]) : 0.f;
-      const float ds = pr * (dp - dels[g]) * sc;
-      float part[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        dv8[j] = fmaf(pr, do8[j], dv8[j]);
-        dk8[j] = fmaf(ds, q8[j], dk8[j]);
-        part[j] = ds * kd8[j];
-      }
-      if constexpr (G1) {  // summed over slots in registers, over lane groups at the end
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dq1[j] += part[j];
-      } else {
-#pragma unroll
-        for (int off = LPR; off < 64; off <<= 1)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) part[j] += __shfl_xor(part[j], off);
-        if (grp == 0) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) dqd[g * D + 8 * cl + j] += part[j];
-        }
-      }
+    for (int j = 0; j < 8; ++j) {
+      b = fmaf(q8[j], kd8[j], b);
+      dp = fmaf(do8[j], vd8[j], dp);
     }
-    if (valid) {
-      const int64_t de = slot_elem(ib);
-      store_n<GF32, 8>(p.dkd, de, dk8);
-      store_n<GF32, 8>(p.dvd, de, dv8);
+    b = group_sum<LPR>(b);
+    dp = group_sum<LPR>(dp);
+    const float pr = __builtin_amdgcn_exp2f(b * c2 - l2);
+    const float ds = pr * (dp - dl) * sc;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      dv8[j] = fmaf(pr, do8[j], dv8[j]);
+      dk8[j] = fmaf(ds, q8[j], dk8[j]);
+      dq8[j] = fmaf(ds, kd8[j], dq8[j]);
     }
   };
-  // two slot batches in flight: batch ib + 1 loads while batch ib is processed
-  for (int ib = 0; ib < nb; ib += 2) {
-    if (ib + 1 < nb) {
-      kdr[1] = load_raw8<BF16>(p.kd, slot_elem(ib + 1));
-      vdr[1] = load_raw8<BF16>(p.vd, slot_elem(ib + 1));
-    }
-    process(ib, kdr[0], vdr[0]);
-    if (ib + 1 >= nb) break;
-    if (ib + 2 < nb) {
-      kdr[0] = load_raw8<BF16>(p.kd, slot_elem(ib + 2));
-      vdr[0] = load_raw8<BF16>(p.vd, slot_elem(ib + 2));
-    }
-    process(ib + 1, kdr[1], vdr[1]);
-  }
-  if constexpr (G1) {
+  auto process = [&](int i, const Raw8<BF16>& kraw, const Raw8<BF16>& vraw) __attribute__((always_inline)) {
+    float kd8[8], vd8[8], dk8[8], dv8[8];
+    widen8<BF16>(kraw, kd8);
+    widen8<BF16>(vraw, vd8);
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1)
+    for (int j = 0; j < 8; ++j) dk8[j] = dv8[j] = 0.f;
+    if constexpr (REG) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dq1[j] += __shfl_xor(dq1[j], off);
-    if (grp == 0) store_n<true, 8>(p.dq_depth, (n * p.Hq + hk) * D + 8 * cl, dq1);
-    return;
+      for (int g = 0; g < GR; ++g) {
+        float q8[8], do8[8];
+        Raw8<BF16> qx = qr[g];
+        Raw8<!GF32> dx = dor[g];
+        if constexpr (GR > 1) {  // widen per slot: hoisting every head's widened rows costs occupancy
+#pragma unroll
+          for (int w = 0; w < (BF16 ? 1 : 2); ++w) asm volatile("" : "+v"(qx.w[w].x), "+v"(qx.w[w].y), "+v"(qx.w[w].z), "+v"(qx.w[w].w));
+#pragma unroll
+          for (int w = 0; w < (GF32 ? 2 : 1); ++w) asm volatile("" : "+v"(dx.w[w].x), "+v"(dx.w[w].y), "+v"(dx.w[w].z), "+v"(dx.w[w].w));
+        }
+        widen8<BF16>(qx, q8);
+        widen8<!GF32>(dx, do8);
+        head(q8, do8, lr[g], dr[g], kd8, vd8, dk8, dv8, dqr[g]);
+      }
+    } else {
+      for (int g = 0; g < G; ++g) {
+        const int64_t e = (n * p.Hq + hk * G + g) * D + 8 * cl;
+        float q8[8], do8[8], dq8[8];
+        load8<BF16>(p.q, e, q8);
+        load8<!GF32>(p.dout, e, do8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dq8[j] = dqd[g * D + 8 * cl + j];
+        head(q8, do8, lse2s[g], dels[g], kd8, vd8, dk8, dv8, dq8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dqd[g * D + 8 * cl + j] = dq8[j];
+      }
+    }
+    const int64_t de = slot_elem(i);
+    store_n<GF32, 8>(p.dkd, de, dk8);
+    store_n<GF32, 8>(p.dvd, de, dv8);
+  };
+  int i0 = 0;
+  for (; i0 + kPrepRing <= S; i0 += kPrepRing) {  // whole rounds: straight-line body
+#pragma unroll
+    for (int u = 0; u < kPrepRing; ++u) {
+      const int r = (u + kPrepRing - 1) % kPrepRing;
+      kr[r] = load_raw8<BF16>(p.kd, slot_elem(i0 + u + kPrepRing - 1));
+      vr[r] = load_raw8<BF16>(p.vd, slot_elem(i0 + u + kPrepRing - 1));
+      process(i0 + u, kr[u], vr[u]);
+    }
   }
-  __builtin_amdgcn_wave_barrier();
-  // the G heads of this KV head are contiguous in dq_depth: G * D floats
-  float* dst = p.dq_depth + (n * p.Hq + (int64_t)hk * G) * D;
-  for (int x = lane; x < G * D / 4; x += 64)
-    reinterpret_cast<float4*>(dst)[x] = reinterpret_cast<const float4*>(dqd)[x];
+#pragma unroll
+  for (int u = 0; u < kPrepRing - 1; ++u)  // the last slots (already loaded)
+    if (i0 + u < S) process(i0 + u, kr[u], vr[u]);
+
+  if constexpr (REG) {
+#pragma unroll
+    for (int g = 0; g < GR; ++g) store_n<true, 8>(p.dq_depth, (n * p.Hq + hk * GC + g) * D + 8 * cl, dqr[g]);
+  } else {
+    for (int g = 0; g < G; ++g)
+      store_n<true, 8>(p.dq_depth, (n * p.Hq + hk * G + g) * D + 8 * cl, dqd + g * D + 8 * cl);
+  }
 }
 
 // ---------------------------------------------------------------- bf16 helpers
@@ -327,11 +348,9 @@ __device__ __forceinline__ bbf16x8 tr_operand(const unsigned char* tile, int r0,
 }
 
 // ---------------------------------------------------------------- dq (bf16)
-#ifdef MODA_BWD_DQ_OCC1
-#define MODA_BWD_DQ_ATTR __attribute__((amdgpu_waves_per_eu(1, 1)))
-#else
-#define MODA_BWD_DQ_ATTR
-#endif
+// two waves per SIMD: the second wave's vector work overlaps the first one's
+// matrix products (with one wave per SIMD the kernel runs ~40 % longer)
+#define MODA_BWD_DQ_ATTR __attribute__((amdgpu_waves_per_eu(2, 2)))
 template <int D, bool GF32>
 __global__ __launch_bounds__(64 * kBwdWaves) MODA_BWD_DQ_ATTR void moda_bwd_dq_kernel(const BwdParams p) {
   constexpr int KC = D / 16, DT = D / 32;
@@ -378,57 +397,71 @@ __global__ __launch_bounds__(64 * kBwdWaves) MODA_BWD_DQ_ATTR void moda_bwd_dq_k
 
   const int64_t kend = p.causal ? (t0 + kBlk < sg.len ? t0 + kBlk : sg.len) : sg.len;
   const int nkb = (int)((kend + kTile - 1) / kTile);
-  uint4 kreg[NLD], vreg[NLD];
+  // the next tile's rows in flight, as vector values (not arrays, which the
+  // compiler would keep in private memory across the loop)
+  typedef uint32_t stage_t __attribute__((ext_vector_type(4 * NLD)));
+  struct Stage {
+    stage_t k, v;
+  };
   auto gload = [&](int kb) __attribute__((always_inline)) {
+    Stage g;
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int idx = tid + 64 * kBwdWaves * u, row = idx / CPR, ch = idx % CPR;
       int64_t key = (int64_t)kb * kTile + row;
       key = key < sg.len ? key : sg.len - 1;  // rows past the end repeat the last key (masked)
       const int64_t e = ((sg.start + key) * p.Hkv + hk) * D + 8 * ch;
-      kreg[u] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + e);
-      vreg[u] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + e);
+      const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + e);
+      const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) + e);
+      g.k[4 * u] = a.x;
+      g.k[4 * u + 1] = a.y;
+      g.k[4 * u + 2] = a.z;
+      g.k[4 * u + 3] = a.w;
+      g.v[4 * u] = b.x;
+      g.v[4 * u + 1] = b.y;
+      g.v[4 * u + 2] = b.z;
+      g.v[4 * u + 3] = b.w;
     }
+    return g;
   };
-  auto sstore = [&](int b) __attribute__((always_inline)) {
+  auto sstore = [&](const Stage& g, int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int idx = tid + 64 * kBwdWaves * u, row = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<uint4*>(kbuf[b] + row * PITCH + 16 * ch) = kreg[u];
-      *reinterpret_cast<uint4*>(vbuf[b] + row * PITCH + 16 * ch) = vreg[u];
+      *reinterpret_cast<uint4*>(kbuf[b] + row * PITCH + 16 * ch) =
+          make_uint4(g.k[4 * u], g.k[4 * u + 1], g.k[4 * u + 2], g.k[4 * u + 3]);
+      *reinterpret_cast<uint4*>(vbuf[b] + row * PITCH + 16 * ch) =
+          make_uint4(g.v[4 * u], g.v[4 * u + 1], g.v[4 * u + 2], g.v[4 * u + 3]);
     }
   };
 
   // Tile kb is read from buffer kb % 2; tile kb + 1 arrives in registers during
   // step kb and is stored into the other buffer, which every wave finished reading
   // before the barrier that ended step kb - 1.
-  gload(0);
-  sstore(0);
+  Stage next = gload(0);
+  sstore(next, 0);
   __syncthreads();
-  if (nkb > 1) gload(1);
+  if (nkb > 1) next = gload(1);
   for (int kb = 0; kb < nkb; ++kb) {
     const unsigned char* ks = kbuf[kb & 1];
     const unsigned char* vs = vbuf[kb & 1];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int64_t k0 = (int64_t)kb * kTile + 32 * st;
-      if (k0 >= sg.len || (p.causal && k0 > tw + 31)) continue;  // wave-uniform
-      bf32x16 s, dp;
+    // S^T = K Q^T and dP^T = V dO^T of sub-tile st (32 keys)
+    auto sdp = [&](int st, bf32x16& s, bf32x16& dp) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const unsigned char* row = ks + (32 * st + r) * PITCH + 16 * (2 * kc + hh);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(row)), qf[kc], s, 0, 0, 0);
+        const int off = (32 * st + r) * PITCH + 16 * (2 * kc + hh);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(ks + off)), qf[kc], s, 0, 0,
+                                                    0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(vs + off)), dof[kc], dp, 0,
+                                                     0, 0);
       }
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const unsigned char* row = vs + (32 * st + r) * PITCH + 16 * (2 * kc + hh);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(row)), dof[kc], dp, 0, 0,
-                                                     0);
-      }
-      // register i holds key k0 + 8 (i / 4) + 4 hh + i % 4 of token t
-      uint32_t dsp[8];
+    };
+    // dS^T of sub-tile st as bf16 pairs; register i holds key
+    // k0 + 8 (i / 4) + 4 hh + i % 4 of token t
+    auto dscore = [&](int st, const bf32x16& s, const bf32x16& dp, uint32_t(&dsp)[8]) __attribute__((always_inline)) {
+      const int64_t k0 = (int64_t)kb * kTile + 32 * st;
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         float v2[2];
@@ -441,16 +474,32 @@ __global__ __launch_bounds__(64 * kBwdWaves) MODA_BWD_DQ_ATTR void moda_bwd_dq_k
         }
         dsp[i >> 1] = rowops::pack_bf16x2(v2[0], v2[1]);
       }
+    };
+    // dQ^T += K^T dS^T for sub-tile st
+    auto accumulate = [&](int st, const uint32_t(&dsp)[8]) __attribute__((always_inline)) {
 #pragma unroll
       for (int part = 0; part < 2; ++part)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<PITCH>(ks, 32 * st + 16 * part, dt, lane),
                                                             pk_b8(dsp + 4 * part), acc[dt], 0, 0, 0);
+    };
+    auto active = [&](int st) __attribute__((always_inline)) {
+      const int64_t k0 = (int64_t)kb * kTile + 32 * st;
+      return k0 < sg.len && !(p.causal && k0 > tw + 31);  // wave-uniform
+    };
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (!active(st)) continue;
+      bf32x16 s, dp;
+      uint32_t dsp[8];
+      sdp(st, s, dp);
+      dscore(st, s, dp, dsp);
+      accumulate(st, dsp);
     }
-    if (kb + 1 < nkb) sstore((kb + 1) & 1);
+    if (kb + 1 < nkb) sstore(next, (kb + 1) & 1);
     __syncthreads();
-    if (kb + 2 < nkb) gload(kb + 2);
+    if (kb + 2 < nkb) next = gload(kb + 2);
   }
 
   if (!row_ok) return;
@@ -570,11 +619,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdP
     const float* lse2s = lbuf[step & 1];
     const float* dels = dbuf[step & 1];
     const int64_t tq0 = tstart + (int64_t)(step % ntq) * kTile;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int64_t q0 = tq0 + 32 * st;
-      if (q0 >= sg.len || (p.causal && q0 + 31 < kw)) continue;  // wave-uniform
-      bf32x16 s, dp;
+    // S = Q K^T and dP = dO V^T of sub-tile st (32 query rows)
+    auto sdp = [&](int st, bf32x16& s, bf32x16& dp) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
@@ -585,8 +631,12 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdP
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(os + off)), vf[kc], dp, 0,
                                                      0, 0);
       }
-      // register i holds token q0 + 8 (i / 4) + 4 hh + i % 4, key `key`
-      uint32_t pp[8], dsp[8];
+    };
+    // P and dS of sub-tile st, packed to bf16 pairs; register i holds token
+    // q0 + 8 (i / 4) + 4 hh + i % 4 and key `key`
+    auto softmax = [&](int st, const bf32x16& s, const bf32x16& dp, uint32_t(&pp)[8], uint32_t(&dsp)[8])
+                       __attribute__((always_inline)) {
+      const int64_t q0 = tq0 + 32 * st;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float4 l4 = *reinterpret_cast<const float4*>(lse2s + 32 * st + 8 * j + 4 * hh);
@@ -607,6 +657,9 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdP
         dsp[2 * j] = rowops::pack_bf16x2(dsv[0], dsv[1]);
         dsp[2 * j + 1] = rowops::pack_bf16x2(dsv[2], dsv[3]);
       }
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS for sub-tile st
+    auto accumulate = [&](int st, const uint32_t(&pp)[8], const uint32_t(&dsp)[8]) __attribute__((always_inline)) {
 #pragma unroll
       for (int part = 0; part < 2; ++part)
 #pragma unroll
@@ -616,6 +669,37 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdP
           dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<PITCH>(qs, 32 * st + 16 * part, dt, lane),
                                                             pk_b8(dsp + 4 * part), dka[dt], 0, 0, 0);
         }
+    };
+    auto active = [&](int st) __attribute__((always_inline)) {
+      const int64_t q0 = tq0 + 32 * st;
+      return q0 < sg.len && !(p.causal && q0 + 31 < kw);  // wave-uniform
+    };
+    if (active(0) && active(1)) {
+      // both sub-tiles: issue order lets the matrix cores run sub-tile 1's
+      // products while the vector units compute sub-tile 0's P and dS, and
+      // sub-tile 0's dK/dV products while sub-tile 1's P and dS are computed
+      bf32x16 s0, dp0, s1, dp1;
+      uint32_t pp0[8], ds0[8], pp1[8], ds1[8];
+      sdp(0, s0, dp0);
+      sdp(1, s1, dp1);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(0, s0, dp0, pp0, ds0);
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate(0, pp0, ds0);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(1, s1, dp1, pp1, ds1);
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate(1, pp1, ds1);
+    } else {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        if (!active(st)) continue;
+        bf32x16 s, dp;
+        uint32_t pp[8], dsp[8];
+        sdp(st, s, dp);
+        softmax(st, s, dp, pp, dsp);
+        accumulate(st, pp, dsp);
+      }
     }
     if (step + 1 < nsteps) sstore((step + 1) & 1);
     __syncthreads();
@@ -761,22 +845,38 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_f32_kernel(const 
   store_n<true, 8>(p.dv, e, dv8);
 }
 
+template <int D, bool BF16, bool GF32>
+void launch_prep(int gc, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const BwdParams& p) {
+  switch (gc) {
+    case 1: hipLaunchKernelGGL((moda_bwd_prep_kernel<D, BF16, GF32, 1>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((moda_bwd_prep_kernel<D, BF16, GF32, 2>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((moda_bwd_prep_kernel<D, BF16, GF32, 4>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((moda_bwd_prep_kernel<D, BF16, GF32, 0>), grid, block, lds, stream, p); break;
+  }
+}
+
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, bool bf16, bool grad_f32, hipStream_t stream) {
   const dim3 block(64 * kBwdWaves);
-  const size_t prep_lds = (size_t)kBwdWaves * prep_wave_floats(p.G, D) * sizeof(float);
-  const dim3 prep_grid((unsigned)((p.total_tokens * p.Hkv + kBwdWaves - 1) / kBwdWaves));
-  const bool g1 = p.G == 1;
-  if (bf16 && grad_f32) {
-    if (g1) hipLaunchKernelGGL((moda_bwd_prep_kernel<D, true, true, true>), prep_grid, block, prep_lds, stream, p);
-    else hipLaunchKernelGGL((moda_bwd_prep_kernel<D, true, true, false>), prep_grid, block, prep_lds, stream, p);
-  } else if (bf16) {
-    if (g1) hipLaunchKernelGGL((moda_bwd_prep_kernel<D, true, false, true>), prep_grid, block, prep_lds, stream, p);
-    else hipLaunchKernelGGL((moda_bwd_prep_kernel<D, true, false, false>), prep_grid, block, prep_lds, stream, p);
-  } else {
-    if (g1) hipLaunchKernelGGL((moda_bwd_prep_kernel<D, false, true, true>), prep_grid, block, prep_lds, stream, p);
-    else hipLaunchKernelGGL((moda_bwd_prep_kernel<D, false, true, false>), prep_grid, block, prep_lds, stream, p);
-  }
+  // prep: G in {1, 2, 4} keeps the heads' state in registers; other G use LDS,
+  // with waves per workgroup chosen so that it stays within 64 KB
+#ifdef MODA_PREP_NO_G4
+  const int gc = (p.G == 1 || p.G == 2) ? p.G : 0;
+#else
+  const int gc = (p.G == 1 || p.G == 2 || p.G == 4) ? p.G : 0;
+#endif
+  const size_t wave_lds = gc ? 0 : (size_t)prep_wave_floats(p.G, D) * sizeof(float);
+  int wpb = 4;
+  while (wpb > 1 && wave_lds * wpb > (size_t)kPrepMaxLds) wpb /= 2;
+  const int64_t items = p.total_tokens * ((p.Hkv + prep_ngrp<D>() - 1) / prep_ngrp<D>());
+  const dim3 prep_grid((unsigned)((items + wpb - 1) / wpb)), prep_block(64 * wpb);
+  const size_t lds = wave_lds * wpb;
+  if (bf16 && grad_f32)
+    launch_prep<D, true, true>(gc, prep_grid, prep_block, lds, stream, p);
+  else if (bf16)
+    launch_prep<D, true, false>(gc, prep_grid, prep_block, lds, stream, p);
+  else
+    launch_prep<D, false, true>(gc, prep_grid, prep_block, lds, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (bf16) {
