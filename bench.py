@@ -473,6 +473,14 @@ def bench_decode(args, w, dev) -> int:
     return 0 if replay_ok else 1
 
 
+def bwd_bytes(w) -> float:
+    """Algorithmic HBM bytes of one backward step: q, k, v, out, dout, lse and the
+    depth slots read once; dq, dk, dv and the depth-slot gradients written once."""
+    e, n, d = w.elem_bytes(), w.n_tokens, w.head_dim
+    rows = n * d * e * (w.n_heads_q * 4 + w.n_heads_kv * 4)  # q, out, dout, dq; k, v, dk, dv
+    return 2.0 * w.depth_bytes() + rows + 4.0 * n * w.n_heads_q
+
+
 def bench_backward(args, w, dev) -> int:
     """One step = one backward call (prep/depth, dq and dk/dv kernels) over the
     whole workload, with q, k, v, the depth slots, out, dout and lse resident in
@@ -563,6 +571,14 @@ def bench_backward(args, w, dev) -> int:
     flops = 2.0 * (w.seq_flops() + w.depth_flops())
     tflops = flops / sec / 1e12
     peak = PEAK_BF16_TFLOPS if w.bf16 else PEAK_F32_TFLOPS
+    nbytes = bwd_bytes(w)
+    if nbytes / (PEAK_HBM_GBS * 1e9) >= flops / (peak * 1e12):  # the bound that takes longer at peak
+        gbs = nbytes / sec / 1e9
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                "traffic": None}
+    else:
+        roof = {"bound": "mfma" if w.bf16 else "alu", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                "frac": tflops / peak, "traffic": None}
     rec = {
         "metric": BWD_METRIC,
         "value": round(tflops, 3),
@@ -584,8 +600,8 @@ def bench_backward(args, w, dev) -> int:
                   "moda_bwd_prep_kernel + moda_bwd_dq_f32_kernel + moda_bwd_dkv_f32_kernel",
         "kernel_source_sha": kernel_source_sha(BWD_SOURCES),
         "replay_matches_eager": replay_ok,
-        "roofline": {"bound": "mfma" if w.bf16 else "alu", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": tflops / peak, "traffic": None},
+        "parts": {"all_bytes_gbs": round(nbytes / sec / 1e9, 1), "mfma_frac_of_peak": round(tflops / peak, 4)},
+        "roofline": roof,
         "cpu_baseline": None,
     }
     del sets, graph, ws

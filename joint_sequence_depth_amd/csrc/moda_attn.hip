@@ -240,6 +240,12 @@ int launch_bwd_checked(moda::BwdParams& p, const BwdArgs& a, int64_t n_seg, int6
   const int64_t nb = (max_len + 127) / 128;
   p.n_qblocks = (int32_t)nb;
   p.n_kblocks = (int32_t)nb;
+#ifdef MODA_BWD_NO_XCD_GROUP
+  p.xcd_group = 0;
+#else
+  // rows of the dq grid (segment, query head) and the dk/dv grid (segment, KV head)
+  p.xcd_group = (n_seg * a.Hkv) % 8 == 0 ? 1 : 0;
+#endif
   if (n_seg * a.Hq * nb > 0x7fffffffLL || p.total_tokens * a.Hq > 0x7fffffffLL * 4)
     return fail(MODA_ERR_SHAPE, "problem too large for one launch");
   const hipError_t err =

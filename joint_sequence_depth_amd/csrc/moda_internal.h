@@ -93,6 +93,7 @@ struct BwdParams {
   float scale_log2;
   int64_t lse_head_stride;    // as in Params
   int32_t lse_batch_layout;
+  int32_t xcd_group;          // 1: dq/dk-dv rows grouped per XCD (needs rows % 8 == 0 in both grids)
 };
 
 hipError_t launch_bwd(const BwdParams& p, int head_dim, bool bf16, bool grad_f32, hipStream_t stream);
