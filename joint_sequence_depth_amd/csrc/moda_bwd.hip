@@ -363,15 +363,14 @@ __global__ __launch_bounds__(64 * kBwdWaves) MODA_BWD_DQ_ATTR void moda_bwd_dq_k
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 31, hh = lane >> 5;
 
   // Workgroup order: with xcd_group, consecutive workgroups (which the hardware
-  // deals round-robin to the 8 XCDs) are mapped so that each XCD works through a
-  // contiguous range of (segment, head) rows, heaviest query block first, and the
-  // K/V tiles that a row and the other heads of its group re-read stay in that
-  // XCD's L2.
+  // deals round-robin to the 8 XCDs) are mapped so that each (segment, head) row
+  // runs on one XCD, heaviest query block first, and the K/V tiles the row
+  // re-reads stay in that XCD's L2; rows go round-robin over the XCDs, so
+  // segments of different lengths spread over all of them.
   int64_t rest = blockIdx.x;
   if (p.xcd_group) {
     const int64_t x = rest % 8, j = rest / 8;
-    const int64_t rows = (int64_t)p.n_seg * p.Hq / 8;  // rows per XCD, a contiguous range
-    rest = (x * rows + j / p.n_qblocks) * p.n_qblocks + (p.n_qblocks - 1 - j % p.n_qblocks);
+    rest = ((j / p.n_qblocks) * 8 + x) * p.n_qblocks + (p.n_qblocks - 1 - j % p.n_qblocks);
   }
   const int qb = (int)(rest % p.n_qblocks);
   rest /= p.n_qblocks;
@@ -552,8 +551,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdP
   int64_t rest = blockIdx.x;
   if (p.xcd_group) {
     const int64_t x = rest % 8, j = rest / 8;
-    const int64_t rows = (int64_t)p.n_seg * p.Hkv / 8;
-    rest = (x * rows + j / p.n_kblocks) * p.n_kblocks + j % p.n_kblocks;
+    rest = ((j / p.n_kblocks) * 8 + x) * p.n_kblocks + j % p.n_kblocks;
   }
   const int kbk = (int)(rest % p.n_kblocks);
   rest /= p.n_kblocks;
