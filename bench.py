@@ -221,7 +221,9 @@ def write_trace_summary(w, trace_dir, log_path, cmd, backward=False, writer=Fals
     lines = [f"# rocprofv3 kernel trace: {kname} on {w.name} ({w.desc})", "",
              "Command (on the GPU host; R = repository root):", f"    {cmd}", "",
              "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
-    for r in stats[:6]:
+    shown = [r for r in stats if "moda" in r["Name"]]  # the library's kernels, then the largest others
+    shown += [r for r in stats if "moda" not in r["Name"]][: max(0, 6 - len(shown))]
+    for r in shown:
         name = r["Name"]
         short = name if len(name) < 90 else name[:87] + "..."
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} "
