@@ -111,11 +111,7 @@ int dispatch(moda::Params& p, const Common& c, int64_t n_seg, int64_t max_len, h
     p.n_tiles = n_pairs * p.n_hgroups * nqb;
     p.xcd_interleave = (!split && n_pairs % 8 == 0) ? 1 : 0;
     p.qb_major = split ? 1 : 0;
-#ifdef MODA_FORCE_SERIAL_ORDER
-    p.serial_order = MODA_FORCE_SERIAL_ORDER;
-#else
     p.serial_order = 0;
-#endif
     if (nqb > kMaxTiles || p.n_tiles > kMaxTiles) return fail(MODA_ERR_SHAPE, "problem too large for one launch");
     err = moda::launch_fwd_bf16(p, c.d, gb, waves, split, c.out_dtype == MODA_DTYPE_F32, stream);
   } else {
@@ -132,10 +128,11 @@ int dispatch(moda::Params& p, const Common& c, int64_t n_seg, int64_t max_len, h
 }
 
 // ---- decode ---------------------------------------------------------------------
-#ifndef MODA_DEC_TARGET_WGS
-#define MODA_DEC_TARGET_WGS 1024
-#endif
-constexpr int64_t kDecodeTargetBlocks = MODA_DEC_TARGET_WGS;
+// Workgroups the chunking aims for. Few heads per workgroup stream rows with
+// little arithmetic each, and more, shorter chunks hide the tail (measured: MHA
+// decode 4.5 -> 4.9 TB/s at 4096); with 4 or 8 heads a row the partial kernel
+// is bound by its vector arithmetic and longer chunks amortise its set-up.
+int64_t decode_target_blocks(int heads_per_block) { return heads_per_block <= 2 ? 4096 : 1024; }
 
 // Query heads per decode workgroup: the largest of 8, 4, 2, 1 dividing G.
 int decode_heads_per_block(int G) {
@@ -144,14 +141,16 @@ int decode_heads_per_block(int G) {
   return 1;
 }
 
-// Cache rows per chunk: enough chunks for about 1024 workgroups, each a whole
-// number of the partial kernel's load rounds. Shared by the call and the
-// workspace-size query, so both see the same chunk count.
+// Cache rows per chunk: enough chunks for about decode_target_blocks
+// workgroups, each a whole number of the partial kernel's load rounds. Shared by
+// the call and the workspace-size query, so both see the same chunk count.
 int64_t decode_chunk(int64_t batch, int Hq, int Hkv, int d, int64_t T_max) {
   const int64_t unit = moda::decode_rows_per_chunk_unit(d);
-  int64_t units = batch * Hkv * (int64_t)((Hq / Hkv) / decode_heads_per_block(Hq / Hkv));
+  const int gd = decode_heads_per_block(Hq / Hkv);
+  const int64_t target = decode_target_blocks(gd);
+  int64_t units = batch * Hkv * (int64_t)((Hq / Hkv) / gd);
   if (units < 1) units = 1;
-  int64_t want = units >= kDecodeTargetBlocks ? 1 : (kDecodeTargetBlocks + units - 1) / units;
+  int64_t want = units >= target ? 1 : (target + units - 1) / units;
   int64_t chunk = (T_max + want - 1) / want;
   chunk = (chunk + unit - 1) / unit * unit;
   return chunk < unit ? unit : chunk;
@@ -240,12 +239,8 @@ int launch_bwd_checked(moda::BwdParams& p, const BwdArgs& a, int64_t n_seg, int6
   const int64_t nb = (max_len + 127) / 128;
   p.n_qblocks = (int32_t)nb;
   p.n_kblocks = (int32_t)nb;
-#ifdef MODA_BWD_NO_XCD_GROUP
-  p.xcd_group = 0;
-#else
   // rows of the dq grid (segment, query head) and the dk/dv grid (segment, KV head)
   p.xcd_group = (n_seg * a.Hkv) % 8 == 0 ? 1 : 0;
-#endif
   if (n_seg * a.Hq * nb > 0x7fffffffLL || p.total_tokens * a.Hq > 0x7fffffffLL * 4)
     return fail(MODA_ERR_SHAPE, "problem too large for one launch");
   const hipError_t err =

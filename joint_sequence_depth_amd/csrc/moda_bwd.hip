@@ -52,10 +52,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBwdWaves = 4;   // waves per workgroup, all kernels
 constexpr int kBlk = 128;      // tokens (dq) or keys (dk/dv) per workgroup
 constexpr int kTile = 64;      // keys (dq) or tokens (dk/dv) staged per step
-#ifndef MODA_BWD_PAD
-#define MODA_BWD_PAD 16
-#endif
-constexpr int kPad = MODA_BWD_PAD;  // bytes of padding per staged LDS row
+// Bytes of padding per staged LDS row (272-byte rows at d = 128 keep the 16-byte
+// row reads conflict-free; 48 bytes, free of conflicts for the transposing reads
+// too, measured no faster).
+constexpr int kPad = 16;
 
 #define MODA_BWD_TR_READ(a) __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) bi16x4*)(a))
 
@@ -875,11 +875,7 @@ hipError_t launch_bwd_d(const BwdParams& p, bool bf16, bool grad_f32, hipStream_
   const dim3 block(64 * kBwdWaves);
   // prep: G in {1, 2, 4} keeps the heads' state in registers; other G use LDS,
   // with waves per workgroup chosen so that it stays within 64 KB
-#ifdef MODA_PREP_NO_G4
-  const int gc = (p.G == 1 || p.G == 2) ? p.G : 0;
-#else
   const int gc = (p.G == 1 || p.G == 2 || p.G == 4) ? p.G : 0;
-#endif
   const size_t wave_lds = gc ? 0 : (size_t)prep_wave_floats(p.G, D) * sizeof(float);
   int wpb = 4;
   while (wpb > 1 && wave_lds * wpb > (size_t)kPrepMaxLds) wpb /= 2;

@@ -31,14 +31,8 @@ typedef __bf16 dbf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309417f;
-#ifndef MODA_DEC_WAVES
-#define MODA_DEC_WAVES 4
-#endif
-#ifndef MODA_DEC_U
-#define MODA_DEC_U 4
-#endif
-constexpr int kDecWaves = MODA_DEC_WAVES;  // waves per partial workgroup
-constexpr int kDecU = MODA_DEC_U;          // key rows per lane group per load batch
+constexpr int kDecWaves = 4;  // waves per partial workgroup (2 and 8 measured slower)
+constexpr int kDecU = 4;      // key rows per lane group per load batch (8 costs occupancy)
 
 __device__ __forceinline__ float d_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float d_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -90,13 +84,14 @@ __device__ __forceinline__ float dot8(const Slice<BF16>& q, const Slice<BF16>& k
   }
 }
 
-// Merges running state (mb, lb, ob) into (ma, la, oa), base-2 units.
-__device__ __forceinline__ void merge_state(float& ma, float& la, float (&oa)[8], float mb, float lb,
-                                            const float (&ob)[8]) {
+// Merges running state (mb, lb, rb, ob) into (ma, la, ra, oa), base-2 units.
+__device__ __forceinline__ void merge_state(float& ma, float& la, float& ra, float (&oa)[8], float mb, float lb,
+                                            float rb, const float (&ob)[8]) {
   const float m = fmaxf(ma, mb);
   const float mu = m == kNegInf ? 0.f : m;
   const float fa = __builtin_amdgcn_exp2f(ma - mu), fb = __builtin_amdgcn_exp2f(mb - mu);
   la = la * fa + lb * fb;
+  ra = ra * fa + rb * fb;
 #pragma unroll
   for (int j = 0; j < 8; ++j) oa[j] = oa[j] * fa + ob[j] * fb;
   ma = m;
@@ -139,11 +134,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void moda_decode_partial_kernel(con
 #pragma unroll
   for (int g = 0; g < GD; ++g) qs[g] = load_slice<BF16>(p.q, ((int64_t)b * p.Hq + h0 + g) * D + 8 * cl);
 
-  float m[GD], l[GD], o[GD][8];
+  // per head: running max m (base 2), sum l of the weights, sum r of the weights
+  // as rounded to bf16 for the value products (bf16 inputs; = l for fp32), and
+  // this lane's slice o of the weighted value sum
+  float m[GD], l[GD], rr[GD], o[GD][8];
 #pragma unroll
   for (int g = 0; g < GD; ++g) {
     m[g] = kNegInf;
     l[g] = 0.f;
+    rr[g] = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
   }
@@ -167,6 +166,21 @@ __global__ __launch_bounds__(64 * kDecWaves) void moda_decode_partial_kernel(con
     }
   };
   auto process = [&](int k, const Slice<BF16>(&kw)[U], const Slice<BF16>(&vw)[U]) {
+    // bf16: the values of row pairs (u, u + 1) interleaved per column, so that one
+    // v_dot2 adds both rows' weighted values: vp[u / 2][c] = (v_u[c], v_{u+1}[c])
+    uint32_t vp[U / 2][8];
+    if constexpr (BF16) {
+#pragma unroll
+      for (int u = 0; u < U; u += 2) {
+        const uint32_t a[4] = {vw[u].w[0].x, vw[u].w[0].y, vw[u].w[0].z, vw[u].w[0].w};
+        const uint32_t b[4] = {vw[u + 1].w[0].x, vw[u + 1].w[0].y, vw[u + 1].w[0].z, vw[u + 1].w[0].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          vp[u / 2][2 * w] = __builtin_amdgcn_perm(b[w], a[w], 0x05040100u);      // low halves
+          vp[u / 2][2 * w + 1] = __builtin_amdgcn_perm(b[w], a[w], 0x07060302u);  // high halves
+        }
+      }
+    }
 #pragma unroll
     for (int g = 0; g < GD; ++g) {
       float sc[U];
@@ -182,14 +196,28 @@ __global__ __launch_bounds__(64 * kDecWaves) void moda_decode_partial_kernel(con
       const float mu = mn == kNegInf ? 0.f : mn;
       const float alpha = __builtin_amdgcn_exp2f(m[g] - mu);
       l[g] *= alpha;
+      rr[g] *= alpha;
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[g][j] *= alpha;
+      if constexpr (BF16) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float pu = __builtin_amdgcn_exp2f(sc[u] - mu);
-        l[g] += pu;
+        for (int u = 0; u < U; u += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(sc[u] - mu), p1 = __builtin_amdgcn_exp2f(sc[u + 1] - mu);
+          l[g] += p0 + p1;
+          const uint32_t pk = rowops::pack_bf16x2(p0, p1);
+          rr[g] = d_dot2(pk, 0x3F803F80u, rr[g]);  // the two rounded weights (bf16 1.0 pair)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pu, elem<BF16>(vw[u], j), o[g][j]);
+          for (int j = 0; j < 8; ++j) o[g][j] = d_dot2(pk, vp[u / 2][j], o[g][j]);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float pu = __builtin_amdgcn_exp2f(sc[u] - mu);
+          l[g] += pu;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[g][j] = fmaf(pu, elem<BF16>(vw[u], j), o[g][j]);
+        }
+        rr[g] = l[g];
       }
       m[g] = mn;
     }
@@ -211,14 +239,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void moda_decode_partial_kernel(con
   for (int g = 0; g < GD; ++g) {
 #pragma unroll
     for (int off = LPR; off < 64; off <<= 1) {
-      const float mb = __shfl_xor(m[g], off), lb = __shfl_xor(l[g], off);
+      const float mb = __shfl_xor(m[g], off), lb = __shfl_xor(l[g], off), rb = __shfl_xor(rr[g], off);
       float ob[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) ob[j] = __shfl_xor(o[g][j], off);
-      merge_state(m[g], l[g], o[g], mb, lb, ob);
+      merge_state(m[g], l[g], rr[g], o[g], mb, lb, rb, ob);
     }
   }
-  __shared__ float red[kDecWaves][GD][D + 4];  // per wave: o slices, then m and l
+  __shared__ float red[kDecWaves][GD][D + 4];  // per wave: o slices, then m, l and r
   if (grp == 0) {
 #pragma unroll
     for (int g = 0; g < GD; ++g) {
@@ -227,6 +255,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void moda_decode_partial_kernel(con
       if (cl == 0) {
         red[wave][g][D] = m[g];
         red[wave][g][D + 1] = l[g];
+        red[wave][g][D + 2] = rr[g];
       }
     }
   }
@@ -235,22 +264,23 @@ __global__ __launch_bounds__(64 * kDecWaves) void moda_decode_partial_kernel(con
   float* ws = p.workspace;
   for (int t = tid; t < GD * LPR; t += 64 * kDecWaves) {
     const int g = t / LPR, c = t % LPR;
-    float ma = kNegInf, la = 0.f, oa[8];
+    float ma = kNegInf, la = 0.f, ra = 0.f, oa[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) oa[j] = 0.f;
     for (int w = 0; w < kDecWaves; ++w) {
       float ob[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) ob[j] = red[w][g][8 * c + j];
-      merge_state(ma, la, oa, red[w][g][D], red[w][g][D + 1], ob);
+      merge_state(ma, la, ra, oa, red[w][g][D], red[w][g][D + 1], red[w][g][D + 2], ob);
     }
-    // record [b][h][chunk]: o[D], m, l (stride D + 4 floats)
+    // record [b][h][chunk]: o[D], m, l, r (stride D + 4 floats)
     float* rec = ws + (((int64_t)b * p.Hq + h0 + g) * p.n_chunks + s) * (D + 4);
     *reinterpret_cast<float4*>(rec + 8 * c) = make_float4(oa[0], oa[1], oa[2], oa[3]);
     *reinterpret_cast<float4*>(rec + 8 * c + 4) = make_float4(oa[4], oa[5], oa[6], oa[7]);
     if (c == 0) {
       rec[D] = ma;
       rec[D + 1] = la;
+      rec[D + 2] = ra;
     }
   }
 }
@@ -271,7 +301,7 @@ __global__ __launch_bounds__(64) void moda_decode_merge_kernel(const DecodeParam
   for (int s = 0; s < n_used; ++s) M = fmaxf(M, recs[s * (D + 4) + D]);
   if (p.n_depth > 0) M = fmaxf(M, recs[p.n_seq_chunks * (D + 4) + D]);
   const float mu = M == kNegInf ? 0.f : M;
-  float Z = 0.f, acc[8];
+  float Z = 0.f, R = 0.f, acc[8];  // Z: sum of the weights (for lse); R: as applied to the values
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
   const int c = lane < LPR ? lane : 0;
@@ -279,6 +309,7 @@ __global__ __launch_bounds__(64) void moda_decode_merge_kernel(const DecodeParam
     const float* rec = recs + s * (D + 4);
     const float f = __builtin_amdgcn_exp2f(rec[D] - mu);
     Z = fmaf(rec[D + 1], f, Z);
+    R = fmaf(rec[D + 2], f, R);
     const float4 a = *reinterpret_cast<const float4*>(rec + 8 * c);
     const float4 bb = *reinterpret_cast<const float4*>(rec + 8 * c + 4);
     acc[0] = fmaf(a.x, f, acc[0]);
@@ -292,7 +323,7 @@ __global__ __launch_bounds__(64) void moda_decode_merge_kernel(const DecodeParam
   };
   for (int s = 0; s < n_used; ++s) add(s);
   if (p.n_depth > 0) add(p.n_seq_chunks);
-  const float inv = Z > 0.f ? 1.f / Z : 0.f;
+  const float inv = R > 0.f ? 1.f / R : 0.f;
   if (lane < LPR) {
     const int64_t e = bh * D + 8 * lane;
     if constexpr (OUT_F32) {
