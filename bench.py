@@ -598,7 +598,7 @@ def bench_backward(args, w, dev) -> int:
                    "seqlens": list(w.seqlens) if w.varlen else None, "n_heads_q": w.n_heads_q,
                    "n_heads_kv": w.n_heads_kv, "head_dim": w.head_dim, "n_depth": w.n_depth, "causal": w.causal,
                    "input_batches": n_batches, "graph": use_graph},
-        "kernel": "moda_bwd_prep_kernel + moda_bwd_dq_kernel + moda_bwd_dkv_kernel" if w.bf16 else
+        "kernel": "moda_bwd_prep_kernel + moda_bwd_dq_kernel + moda_bwd_dkv8_kernel" if w.bf16 else
                   "moda_bwd_prep_kernel + moda_bwd_dq_f32_kernel + moda_bwd_dkv_f32_kernel",
         "kernel_source_sha": kernel_source_sha(BWD_SOURCES),
         "replay_matches_eager": replay_ok,

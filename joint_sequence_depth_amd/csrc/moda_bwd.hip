@@ -24,11 +24,12 @@
 //    dQ^T += K^T dS^T through transposing LDS reads of K, with the keys of the
 //    dS^T registers and of the K^T operand in the same order. The epilogue adds
 //    the depth share.
-//  * dk/dv (bf16, matrix cores): a workgroup of 4 waves per (segment, KV head,
-//    128 keys), 32 keys per wave, looping over the G query heads and the query
-//    blocks of 64 tokens that can see them (Q, dO, lse and delta staged in LDS).
-//    S = Q K^T and dP = dO V^T put one key per lane; dV^T += dO^T P and
-//    dK^T += Q^T dS read dO^T and Q^T transposed from LDS.
+//  * dk/dv (bf16, matrix cores): a workgroup of 8 waves per (segment, KV head,
+//    128 keys), two waves per 32-key block splitting each 64-token query tile,
+//    looping over the G query heads and the tiles that can see the keys (Q, dO,
+//    lse and delta staged in LDS, K and V rows in LDS). S = Q K^T and
+//    dP = dO V^T put one key per lane; dV^T += dO^T P and dK^T += Q^T dS read
+//    dO^T and Q^T transposed from LDS.
 //  * fp32 inputs take row-wise vector kernels for dq and dk/dv instead (lanes over
 //    8-element slices, as in prep): the full-precision path.
 #include <hip/hip_runtime.h>
@@ -533,21 +534,40 @@ __global__ __launch_bounds__(64 * kBwdWaves) MODA_BWD_DQ_ATTR void moda_bwd_dq_k
 }
 
 // ---------------------------------------------------------------- dk / dv (bf16)
+// A workgroup of 8 waves owns 128 keys of one (segment, KV head) and loops over
+// the G query heads and the 64-token query tiles that can see them (Q, dO, lse
+// and delta double-buffered in LDS). The two waves of a 32-key block split each
+// tile (wave w: keys 32 (w % 4), rows 32 (w / 4) of the tile), so a SIMD runs two
+// waves, each holding one 128 x 32 dK^T and one dV^T accumulator in registers;
+// the K and V rows of the 128 keys sit in LDS as the products' B operands. At the
+// end each pair adds its two partial sums through LDS. (With 4 waves holding all
+// of a key block's tiles and K/V in registers, one wave per SIMD fit: 10-22 %
+// slower.)
+constexpr int kDkv8Waves = 8;
+
 template <int D, bool GF32>
-__global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(64 * kDkv8Waves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void moda_bwd_dkv8_kernel(const BwdParams p) {
   constexpr int KC = D / 16, DT = D / 32;
   constexpr int PITCH = D * 2 + kPad;
   constexpr int CPR = D * 2 / 16;
-  constexpr int NLD = kTile * CPR / (64 * kBwdWaves);
-  // two buffers: the tile after next is stored while the current one is read
-  __shared__ __align__(16) unsigned char qbuf[2][kTile * PITCH];
-  __shared__ __align__(16) unsigned char obuf[2][kTile * PITCH];  // dout
-  __shared__ __align__(16) float lbuf[2][kTile];
-  __shared__ __align__(16) float dbuf[2][kTile];
+  constexpr int NTH = 64 * kDkv8Waves;
+  constexpr int NLD = kTile * CPR / NTH;        // Q (and dO) chunks per thread per tile
+  constexpr int NKV = kBlk * CPR / NTH;         // K (and V) chunks per thread, once
+  constexpr int KV_BYTES = kBlk * PITCH;        // one of K, V
+  constexpr int TILE_BYTES = kTile * PITCH;     // one of Q, dO, per buffer
+  constexpr int OFF_Q = 2 * KV_BYTES;
+  constexpr int OFF_O = OFF_Q + 2 * TILE_BYTES;
+  constexpr int OFF_L = OFF_O + 2 * TILE_BYTES;
+  constexpr int OFF_D = OFF_L + 2 * kTile * 4;
+  constexpr int LDS_BYTES = OFF_D + 2 * kTile * 4;
+  static_assert(4 * 64 * 2 * DT * 16 * 4 <= LDS_BYTES, "partials of four waves fit in the LDS block");
+  __shared__ __align__(16) unsigned char sm[LDS_BYTES];
+  unsigned char* const kt = sm;
+  unsigned char* const vt = sm + KV_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 31, hh = lane >> 5;
+  const int kbw = wave & 3, half = wave >> 2;
 
-  // Workgroup order as in the dq kernel: each XCD takes whole (segment, KV head)
-  // rows, heaviest key block (the first) first, sharing the row's Q/dO tiles in L2.
   int64_t rest = blockIdx.x;
   if (p.xcd_group) {
     const int64_t x = rest % 8, j = rest / 8;
@@ -559,22 +579,22 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdP
   const int seg = (int)(rest / p.Hkv);
   const Seg sg = segment(p, seg);
   const int64_t k0 = (int64_t)kbk * kBlk;
-  if (k0 >= sg.len) return;
-  const int64_t kw = k0 + 32 * wave;
+  if (k0 >= sg.len) return;  // whole workgroup, before any barrier
+  const int64_t kw = k0 + 32 * kbw;
   const int64_t key = kw + r;
   const bool key_ok = key < sg.len;
-  const int64_t nk = sg.start + (key_ok ? key : sg.len - 1);
 
-  // K^T and V^T operands: lane (r, hh) holds key r, columns 16 kc + 8 hh .. + 7
-  bbf16x8 kf[KC], vf[KC];
-  {
-    const int64_t e = (nk * p.Hkv + hk) * D;
+  // the 128 keys' K and V rows into LDS (rows past the end repeat the last key)
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      kf[kc] = as_b8(load_chunk_bf16<false>(p.k, e + 16 * kc + 8 * hh));
-      vf[kc] = as_b8(load_chunk_bf16<false>(p.v, e + 16 * kc + 8 * hh));
-    }
+  for (int u = 0; u < NKV; ++u) {
+    const int idx = tid + NTH * u, row = idx / CPR, ch = idx % CPR;
+    int64_t kk = k0 + row;
+    kk = kk < sg.len ? kk : sg.len - 1;
+    const int64_t e = ((sg.start + kk) * p.Hkv + hk) * D + 8 * ch;
+    *reinterpret_cast<uint4*>(kt + row * PITCH + 16 * ch) = load_chunk_bf16<false>(p.k, e);
+    *reinterpret_cast<uint4*>(vt + row * PITCH + 16 * ch) = load_chunk_bf16<false>(p.v, e);
   }
+
   bf32x16 dka[DT], dva[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -585,77 +605,90 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdP
   const int64_t tstart = p.causal ? k0 / kTile * kTile : 0;
   const int ntq = (int)((sg.len - tstart + kTile - 1) / kTile);
   const int nsteps = p.G * ntq;  // (query head, query tile) pairs
-  uint4 qreg[NLD], oreg[NLD];
-  float lreg = 0.f, dreg = 0.f;
+  typedef uint32_t stage_t __attribute__((ext_vector_type(4 * NLD)));
+  struct Stage {
+    stage_t q, o;
+    float l, d;
+  };
   auto gload = [&](int step) __attribute__((always_inline)) {
+    Stage g;
     const int h = hk * p.G + step / ntq;
     const int64_t tq0 = tstart + (int64_t)(step % ntq) * kTile;
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int idx = tid + 64 * kBwdWaves * u, row = idx / CPR, ch = idx % CPR;
+      const int idx = tid + NTH * u, row = idx / CPR, ch = idx % CPR;
       int64_t tq = tq0 + row;
       tq = tq < sg.len ? tq : sg.len - 1;  // rows past the end repeat the last token (masked)
       const int64_t e = ((sg.start + tq) * p.Hq + h) * D + 8 * ch;
-      qreg[u] = load_chunk_bf16<false>(p.q, e);
-      oreg[u] = load_chunk_bf16<GF32>(p.dout, e);
+      const uint4 a = load_chunk_bf16<false>(p.q, e), b = load_chunk_bf16<GF32>(p.dout, e);
+      g.q[4 * u] = a.x;
+      g.q[4 * u + 1] = a.y;
+      g.q[4 * u + 2] = a.z;
+      g.q[4 * u + 3] = a.w;
+      g.o[4 * u] = b.x;
+      g.o[4 * u + 1] = b.y;
+      g.o[4 * u + 2] = b.z;
+      g.o[4 * u + 3] = b.w;
     }
+    g.l = g.d = 0.f;
     if (tid < kTile) {
       int64_t tq = tq0 + tid;
       tq = tq < sg.len ? tq : sg.len - 1;
       const int64_t nq = sg.start + tq;
-      lreg = p.lse[lse_index(p, nq, h)] * kLog2e;
-      dreg = p.delta[(int64_t)h * p.total_tokens + nq];
+      g.l = p.lse[lse_index(p, nq, h)] * kLog2e;
+      g.d = p.delta[(int64_t)h * p.total_tokens + nq];
     }
+    return g;
   };
-  auto sstore = [&](int b) __attribute__((always_inline)) {
+  auto sstore = [&](const Stage& g, int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int idx = tid + 64 * kBwdWaves * u, row = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<uint4*>(qbuf[b] + row * PITCH + 16 * ch) = qreg[u];
-      *reinterpret_cast<uint4*>(obuf[b] + row * PITCH + 16 * ch) = oreg[u];
+      const int idx = tid + NTH * u, row = idx / CPR, ch = idx % CPR;
+      *reinterpret_cast<uint4*>(sm + OFF_Q + b * TILE_BYTES + row * PITCH + 16 * ch) =
+          make_uint4(g.q[4 * u], g.q[4 * u + 1], g.q[4 * u + 2], g.q[4 * u + 3]);
+      *reinterpret_cast<uint4*>(sm + OFF_O + b * TILE_BYTES + row * PITCH + 16 * ch) =
+          make_uint4(g.o[4 * u], g.o[4 * u + 1], g.o[4 * u + 2], g.o[4 * u + 3]);
     }
     if (tid < kTile) {
-      lbuf[b][tid] = lreg;
-      dbuf[b][tid] = dreg;
+      reinterpret_cast<float*>(sm + OFF_L)[b * kTile + tid] = g.l;
+      reinterpret_cast<float*>(sm + OFF_D)[b * kTile + tid] = g.d;
     }
   };
 
-  // as in the dq kernel: step i reads buffer i % 2 while step i + 1's tile is
-  // stored into the other one
+  // step i reads buffer i % 2 while step i + 1's tile is stored into the other
+  Stage next;
   if (nsteps > 0) {
-    gload(0);
-    sstore(0);
+    next = gload(0);
+    sstore(next, 0);
   }
-  __syncthreads();
-  if (nsteps > 1) gload(1);
+  __syncthreads();  // also publishes the K/V rows
+  if (nsteps > 1) next = gload(1);
   for (int step = 0; step < nsteps; ++step) {
-    const unsigned char* qs = qbuf[step & 1];
-    const unsigned char* os = obuf[step & 1];
-    const float* lse2s = lbuf[step & 1];
-    const float* dels = dbuf[step & 1];
-    const int64_t tq0 = tstart + (int64_t)(step % ntq) * kTile;
-    // S = Q K^T and dP = dO V^T of sub-tile st (32 query rows)
-    auto sdp = [&](int st, bf32x16& s, bf32x16& dp) __attribute__((always_inline)) {
+    const int b = step & 1;
+    const unsigned char* qs = sm + OFF_Q + b * TILE_BYTES;
+    const unsigned char* os = sm + OFF_O + b * TILE_BYTES;
+    const float* lse2s = reinterpret_cast<const float*>(sm + OFF_L) + b * kTile;
+    const float* dels = reinterpret_cast<const float*>(sm + OFF_D) + b * kTile;
+    const int64_t q0 = tstart + (int64_t)(step % ntq) * kTile + 32 * half;
+    if (q0 < sg.len && !(p.causal && q0 + 31 < kw)) {  // wave-uniform
+      bf32x16 sc, dp;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+      for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const int off = (32 * st + r) * PITCH + 16 * (2 * kc + hh);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(qs + off)), kf[kc], s, 0, 0,
-                                                    0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(os + off)), vf[kc], dp, 0,
-                                                     0, 0);
+        const int off = (32 * half + r) * PITCH + 16 * (2 * kc + hh);   // this lane's query row
+        const int koff = (32 * kbw + r) * PITCH + 16 * (2 * kc + hh);  // this lane's key row
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(qs + off)),
+                                                     as_b8(*reinterpret_cast<const uint4*>(kt + koff)), sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_b8(*reinterpret_cast<const uint4*>(os + off)),
+                                                     as_b8(*reinterpret_cast<const uint4*>(vt + koff)), dp, 0, 0, 0);
       }
-    };
-    // P and dS of sub-tile st, packed to bf16 pairs; register i holds token
-    // q0 + 8 (i / 4) + 4 hh + i % 4 and key `key`
-    auto softmax = [&](int st, const bf32x16& s, const bf32x16& dp, uint32_t(&pp)[8], uint32_t(&dsp)[8])
-                       __attribute__((always_inline)) {
-      const int64_t q0 = tq0 + 32 * st;
+      // register i holds token q0 + 8 (i / 4) + 4 hh + i % 4 and key `key`
+      uint32_t pp[8], dsp[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4 l4 = *reinterpret_cast<const float4*>(lse2s + 32 * st + 8 * j + 4 * hh);
-        const float4 d4 = *reinterpret_cast<const float4*>(dels + 32 * st + 8 * j + 4 * hh);
+        const float4 l4 = *reinterpret_cast<const float4*>(lse2s + 32 * half + 8 * j + 4 * hh);
+        const float4 d4 = *reinterpret_cast<const float4*>(dels + 32 * half + 8 * j + 4 * hh);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
         float pv[4], dsv[4];
 #pragma unroll
@@ -663,7 +696,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdP
           const int i = 4 * j + u;
           const int64_t tq = q0 + 8 * j + 4 * hh + u;
           const bool vis = key_ok && tq < sg.len && (!p.causal || key <= tq);
-          const float pr = vis ? __builtin_amdgcn_exp2f(s[i] * c2 - lv[u]) : 0.f;
+          const float pr = vis ? __builtin_amdgcn_exp2f(sc[i] * c2 - lv[u]) : 0.f;
           pv[u] = pr;
           dsv[u] = pr * (dp[i] - dv4[u]);
         }
@@ -672,68 +705,48 @@ __global__ __launch_bounds__(64 * kBwdWaves) void moda_bwd_dkv_kernel(const BwdP
         dsp[2 * j] = rowops::pack_bf16x2(dsv[0], dsv[1]);
         dsp[2 * j + 1] = rowops::pack_bf16x2(dsv[2], dsv[3]);
       }
-    };
-    // dV^T += dO^T P and dK^T += Q^T dS for sub-tile st
-    auto accumulate = [&](int st, const uint32_t(&pp)[8], const uint32_t(&dsp)[8]) __attribute__((always_inline)) {
 #pragma unroll
       for (int part = 0; part < 2; ++part)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<PITCH>(os, 32 * st + 16 * part, dt, lane),
+          dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<PITCH>(os, 32 * half + 16 * part, dt, lane),
                                                             pk_b8(pp + 4 * part), dva[dt], 0, 0, 0);
-          dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<PITCH>(qs, 32 * st + 16 * part, dt, lane),
+          dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<PITCH>(qs, 32 * half + 16 * part, dt, lane),
                                                             pk_b8(dsp + 4 * part), dka[dt], 0, 0, 0);
         }
-    };
-    auto active = [&](int st) __attribute__((always_inline)) {
-      const int64_t q0 = tq0 + 32 * st;
-      return q0 < sg.len && !(p.causal && q0 + 31 < kw);  // wave-uniform
-    };
-    if (active(0) && active(1)) {
-      // both sub-tiles: issue order lets the matrix cores run sub-tile 1's
-      // products while the vector units compute sub-tile 0's P and dS, and
-      // sub-tile 0's dK/dV products while sub-tile 1's P and dS are computed
-      bf32x16 s0, dp0, s1, dp1;
-      uint32_t pp0[8], ds0[8], pp1[8], ds1[8];
-      sdp(0, s0, dp0);
-      sdp(1, s1, dp1);
-      __builtin_amdgcn_sched_barrier(0);
-      softmax(0, s0, dp0, pp0, ds0);
-      __builtin_amdgcn_sched_barrier(0);
-      accumulate(0, pp0, ds0);
-      __builtin_amdgcn_sched_barrier(0);
-      softmax(1, s1, dp1, pp1, ds1);
-      __builtin_amdgcn_sched_barrier(0);
-      accumulate(1, pp1, ds1);
-    } else {
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if (!active(st)) continue;
-        bf32x16 s, dp;
-        uint32_t pp[8], dsp[8];
-        sdp(st, s, dp);
-        softmax(st, s, dp, pp, dsp);
-        accumulate(st, pp, dsp);
-      }
     }
-    if (step + 1 < nsteps) sstore((step + 1) & 1);
+    if (step + 1 < nsteps) sstore(next, (step + 1) & 1);
     __syncthreads();
-    if (step + 2 < nsteps) gload(step + 2);
+    if (step + 2 < nsteps) next = gload(step + 2);
   }
 
-  if (!key_ok) return;
+  // the second wave of each key block hands its partial sums to the first
+  float* part = reinterpret_cast<float*>(sm) + (size_t)kbw * 64 * 2 * DT * 16 + (size_t)lane * 2 * DT * 16;
+  if (half == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        *reinterpret_cast<float4*>(part + dt * 16 + i) = make_float4(dka[dt][i], dka[dt][i + 1], dka[dt][i + 2], dka[dt][i + 3]);
+        *reinterpret_cast<float4*>(part + (DT + dt) * 16 + i) =
+            make_float4(dva[dt][i], dva[dt][i + 1], dva[dt][i + 2], dva[dt][i + 3]);
+      }
+  }
+  __syncthreads();
+  if (half == 1 || !key_ok) return;
+  const int64_t nk = sg.start + key;
   const int64_t e = (nk * p.Hkv + hk) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = 32 * dt + 8 * j + 4 * hh;
-      float xk[4], xv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        xk[u] = dka[dt][4 * j + u] * p.scale;
-        xv[u] = dva[dt][4 * j + u];
-      }
+      const float4 pk = *reinterpret_cast<const float4*>(part + dt * 16 + 4 * j);
+      const float4 pv = *reinterpret_cast<const float4*>(part + (DT + dt) * 16 + 4 * j);
+      const float xk[4] = {(dka[dt][4 * j] + pk.x) * p.scale, (dka[dt][4 * j + 1] + pk.y) * p.scale,
+                           (dka[dt][4 * j + 2] + pk.z) * p.scale, (dka[dt][4 * j + 3] + pk.w) * p.scale};
+      const float xv[4] = {dva[dt][4 * j] + pv.x, dva[dt][4 * j + 1] + pv.y, dva[dt][4 * j + 2] + pv.z,
+                           dva[dt][4 * j + 3] + pv.w};
       store_n<GF32, 4>(p.dk, e + c, xk);
       store_n<GF32, 4>(p.dv, e + c, xv);
     }
@@ -893,12 +906,13 @@ hipError_t launch_bwd_d(const BwdParams& p, bool bf16, bool grad_f32, hipStream_
   if (bf16) {
     const dim3 gq((unsigned)((int64_t)p.n_seg * p.Hq * p.n_qblocks));
     const dim3 gk((unsigned)((int64_t)p.n_seg * p.Hkv * p.n_kblocks));
+    const dim3 block8(64 * kDkv8Waves);
     if (grad_f32) {
       hipLaunchKernelGGL((moda_bwd_dq_kernel<D, true>), gq, block, 0, stream, p);
-      hipLaunchKernelGGL((moda_bwd_dkv_kernel<D, true>), gk, block, 0, stream, p);
+      hipLaunchKernelGGL((moda_bwd_dkv8_kernel<D, true>), gk, block8, 0, stream, p);
     } else {
       hipLaunchKernelGGL((moda_bwd_dq_kernel<D, false>), gq, block, 0, stream, p);
-      hipLaunchKernelGGL((moda_bwd_dkv_kernel<D, false>), gk, block, 0, stream, p);
+      hipLaunchKernelGGL((moda_bwd_dkv8_kernel<D, false>), gk, block8, 0, stream, p);
     }
   } else {
     const dim3 gq((unsigned)((p.total_tokens * p.Hq + kBwdWaves - 1) / kBwdWaves));
