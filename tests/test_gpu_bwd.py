@@ -120,9 +120,12 @@ def test_bwd_not_causal(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_bwd_varlen(dtype):
-    _full_compare(workload(dtype=dtype, head_dim=64, seqlens=(5, 130, 64, 1, 200), n_heads_q=4, n_heads_kv=1,
-                           n_depth=3, seed=1400))
+@pytest.mark.parametrize("lens,causal", [((5, 130, 64, 1, 200), True), ((5, 1, 130, 64, 0, 257), True),
+                                         ((70, 0, 33), False)])
+def test_bwd_varlen(dtype, lens, causal):
+    # includes empty sequences (equal offsets) and a non-causal packed case
+    _full_compare(workload(dtype=dtype, head_dim=64, seqlens=lens, n_heads_q=4, n_heads_kv=1, n_depth=3,
+                           causal=causal, seed=1400 + len(lens)))
 
 
 def test_bwd_fp32_gradients_of_bf16_inputs():
