@@ -40,7 +40,8 @@ __device__ __forceinline__ float d_dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dbf16x2, a), __builtin_bit_cast(dbf16x2, b), c, false);
 }
 
-// 8 consecutive elements of a row, as stored (bf16: one 16-byte word; fp32: two).
+// 8 consecutive elements of a row, as stored (bf16: one 16-byte word; fp32: two),
+// loaded with the non-temporal hint: a step reads each cache and slot row once.
 template <bool BF16>
 struct Slice {
   uint4 w[BF16 ? 1 : 2];
@@ -49,11 +50,11 @@ template <bool BF16>
 __device__ __forceinline__ Slice<BF16> load_slice(const void* base, int64_t elem) {
   Slice<BF16> s;
   if constexpr (BF16) {
-    s.w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+    s.w[0] = rowops::stream_load16(static_cast<const uint16_t*>(base) + elem);
   } else {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem);
-    s.w[0] = p[0];
-    s.w[1] = p[1];
+    const float* p = static_cast<const float*>(base) + elem;
+    s.w[0] = rowops::stream_load16(p);
+    s.w[1] = rowops::stream_load16(p + 4);
   }
   return s;
 }

@@ -24,7 +24,9 @@
 //    covers 64 / LPR slot rows (one per token). Each slot row is read ONCE and
 //    dotted with all GB query heads of the group (v_dot2_f32_bf16 on the packed
 //    operands, DPP group sums). Loads run NBUF - 1 batches of U slots ahead of the
-//    arithmetic in register buffers. Finished row states (m, acc, o) go to LDS.
+//    arithmetic in register buffers and carry the non-temporal hint (the slots are
+//    read once; the sequence K/V blocks are read again by later query blocks and
+//    should keep their L2 lines). Finished row states (m, acc, o) go to LDS.
 //
 //  * the sequence loop (MFMA-bound): a flash-style loop over 64-key blocks.
 //    S^T = K Q^T on v_mfma_f32_32x32x16_bf16 puts one query row per lane (lanes l
@@ -49,6 +51,7 @@
 #include <type_traits>
 
 #include "moda_internal.h"
+#include "moda_rowops.h"
 
 namespace moda {
 namespace {
@@ -329,8 +332,8 @@ moda_fwd_bf16_kernel(const Params p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int slot = ch * U + u < n_depth ? ch * U + u : n_depth - 1;
-      kw[u] = ldg16(KD + base + slot * slot_stride);
-      vw[u] = ldg16(VD + base + slot * slot_stride);
+      kw[u] = rowops::stream_load16(KD + base + slot * slot_stride);
+      vw[u] = rowops::stream_load16(VD + base + slot * slot_stride);
     }
     if constexpr (QPRE) {  // every step: a fixed load count keeps the wait counts exact
 #pragma unroll

@@ -27,6 +27,15 @@ __device__ __forceinline__ float group_sum(float s) {
   return s;
 }
 
+// One 16-byte load with the non-temporal hint: for streams read once (depth slots,
+// a decode step's cache rows), so that they do not push data that is read again
+// (a sequence's K/V blocks) out of L2.
+__device__ __forceinline__ uint4 stream_load16(const void* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // 8 consecutive elements at element offset `elem` as fp32 (bf16 or fp32 storage).
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* base, int64_t elem, float (&x)[8]) {
