@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector
 CACHE_DEFEAT_BYTES = 768 << 20  # > 256 MB Infinity Cache + 8 x 4 MB L2
-KERNEL_SOURCES = ["moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_attn.hip", "moda_internal.h"]  # the forward path
+KERNEL_SOURCES = ["moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h"]  # the forward path
 DECODE_SOURCES = ["moda_decode.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h"]
 BWD_SOURCES = ["moda_bwd.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h"]
 WRITER_SOURCES = ["moda_depth_kv.hip", "moda_attn.hip", "moda_internal.h"]
