@@ -38,9 +38,10 @@
 //    NST - 1 blocks ahead, and are read back as MFMA operands, V through the
 //    gfx950 transposing LDS read.
 //
-// The two workgroups that share a CU run the two parts in opposite order, so one
-// streams depth rows from HBM while the other keeps the matrix cores busy; each
-// wave then merges its two partial states, normalises once and writes.
+// Workgroups start at different times (a new one takes each freed slot), so while
+// one streams its depth rows from HBM its CU neighbour is usually in its sequence
+// loop on the matrix cores; each wave then merges its two partial states,
+// normalises once and writes.
 //
 // Rounding: QK^T and PV accumulate in fp32; P is rounded to bf16 (RNE) before PV;
 // the output is written in fp32, or rounded to bf16 (RNE) once, after the single
@@ -474,10 +475,11 @@ moda_fwd_bf16_kernel(const Params p) {
     m_run = m_new;
   };
 
-  // Shared tiles: the two workgroups that share a CU run the depth pass first and
-  // last in turn (the first round of workgroups on an XCD's 32 CUs starts with it,
-  // the second with the sequence loop), so one streams from HBM while the other
-  // keeps the matrix cores busy. Split tiles at D = 64: the depth loads are issued
+  // Shared tiles: the depth pass runs first (serial_order 1, the host's choice:
+  // faster than alternating the order between workgroup rounds, 0, or running it
+  // last, 2), so the workgroup's HBM phase precedes its matrix-core phase and the
+  // staggered starts of the workgroups on a CU overlap the two. Split tiles at
+  // D = 64: the depth loads are issued
   // as the sequence loop starts and consumed after it, which hides their latency
   // (at D = 128 the loop needs those registers; the pass follows the loop).
   constexpr bool EARLY_DEPTH = MODE == kSerial && SPLIT && D == 64;
