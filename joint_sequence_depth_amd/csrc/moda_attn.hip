@@ -111,7 +111,6 @@ int dispatch(moda::Params& p, const Common& c, int64_t n_seg, int64_t max_len, h
     p.n_tiles = n_pairs * p.n_hgroups * nqb;
     p.xcd_interleave = (!split && n_pairs % 8 == 0) ? 1 : 0;
     p.qb_major = split ? 1 : 0;
-    p.serial_order = 1;  // depth pass first in every workgroup
     if (nqb > kMaxTiles || p.n_tiles > kMaxTiles) return fail(MODA_ERR_SHAPE, "problem too large for one launch");
     err = moda::launch_fwd_bf16(p, c.d, gb, waves, split, c.out_dtype == MODA_DTYPE_F32, stream);
   } else {

@@ -475,17 +475,17 @@ moda_fwd_bf16_kernel(const Params p) {
     m_run = m_new;
   };
 
-  // Shared tiles: the depth pass runs first (serial_order 1, the host's choice:
-  // faster than alternating the order between workgroup rounds, 0, or running it
-  // last, 2), so the workgroup's HBM phase precedes its matrix-core phase and the
-  // staggered starts of the workgroups on a CU overlap the two. Split tiles at
+  // Shared tiles: the depth pass runs first, so the workgroup's HBM phase
+  // precedes its matrix-core phase and the staggered starts of the workgroups on
+  // a CU overlap the two. Fixed at compile time: the depth buffers are then never
+  // live together with the output accumulators, which removes the register spills
+  // a depth-last path forced on the D = 128 instances. Split tiles at
   // D = 64: the depth loads are issued
   // as the sequence loop starts and consumed after it, which hides their latency
   // (at D = 128 the loop needs those registers; the pass follows the loop).
   constexpr bool EARLY_DEPTH = MODE == kSerial && SPLIT && D == 64;
-  const bool depth_first = MODE == kSerial && !SPLIT &&
-                           (p.serial_order == 0 ? (((blockIdx.x >> 3) >> 5) & 1) == 0 : p.serial_order == 1);
-  if (MODE == kSerial && depth_first) {
+  constexpr bool depth_first = MODE == kSerial && !SPLIT;
+  if constexpr (depth_first) {
     depth_begin();
     depth_end();
     __syncthreads();
@@ -852,12 +852,6 @@ moda_fwd_bf16_kernel(const Params p) {
       m_run = m_new;
     }
     if constexpr (MODE == kSerial) depth_fold();
-  } else if (MODE == kSerial && !depth_first) {
-    __syncthreads();  // every wave's loads have landed: the K/V area is free
-    depth_begin();
-    depth_end();
-    __syncthreads();
-    depth_fold();
   }
 
   // ---- normalise once and write ------------------------------------------------

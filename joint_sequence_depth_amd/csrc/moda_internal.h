@@ -38,8 +38,6 @@ struct Params {
   int32_t lse_batch_layout;   // 1: base = s * Hq * T; 0: base = seg_start
   int32_t xcd_interleave;     // 1: (segment, KV head) pairs go round-robin to the 8 XCDs
   int32_t qb_major;           // 1: tiles ordered by query block across all pairs (heaviest first)
-  int32_t serial_order;       // bf16 shared tiles with depth slots: 0 = depth pass first and
-                              // last in turn (by workgroup round), 1 = depth pass first, 2 = last
   int64_t n_tiles;
 };
 
