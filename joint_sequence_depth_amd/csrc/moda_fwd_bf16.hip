@@ -475,16 +475,18 @@ moda_fwd_bf16_kernel(const Params p) {
     m_run = m_new;
   };
 
-  // Shared tiles: the depth pass runs first, so the workgroup's HBM phase
+  // Shared tiles, GB < 4: the depth pass runs first, so the workgroup's HBM phase
   // precedes its matrix-core phase and the staggered starts of the workgroups on
   // a CU overlap the two. Fixed at compile time: the depth buffers are then never
-  // live together with the output accumulators, which removes the register spills
-  // a depth-last path forced on the D = 128 instances. Split tiles at
+  // live together with the output accumulators, which avoids the register spills
+  // a depth-last path costs the D = 128 instances. GB = 4 (four heads share each
+  // depth row, so the sequence loop outweighs the depth stream): the pass runs
+  // last, which measured faster despite those spills. Split tiles at
   // D = 64: the depth loads are issued
   // as the sequence loop starts and consumed after it, which hides their latency
   // (at D = 128 the loop needs those registers; the pass follows the loop).
   constexpr bool EARLY_DEPTH = MODE == kSerial && SPLIT && D == 64;
-  constexpr bool depth_first = MODE == kSerial && !SPLIT;
+  constexpr bool depth_first = MODE == kSerial && !SPLIT && GB < 4;
   if constexpr (depth_first) {
     depth_begin();
     depth_end();
@@ -852,6 +854,12 @@ moda_fwd_bf16_kernel(const Params p) {
       m_run = m_new;
     }
     if constexpr (MODE == kSerial) depth_fold();
+  } else if constexpr (MODE == kSerial && !depth_first) {
+    __syncthreads();  // every wave's loads have landed: the K/V area is free
+    depth_begin();
+    depth_end();
+    __syncthreads();
+    depth_fold();
   }
 
   // ---- normalise once and write ------------------------------------------------
