@@ -225,10 +225,6 @@ def scalar_ref(q, k, v, k_depth, v_depth, n_depth, causal=True, scale=None):
 # token floor(j_d / L) with L slots per token.
 
 
-def expanded_token(i_q: int, G: int) -> int:
-    return i_q // G
-
-
 def sequence_visible(i_q: int, i_k: int, G: int) -> bool:
     return i_q // G >= i_k
 

@@ -431,6 +431,61 @@ def pin_backward_empty_depth_is_sdpa_autograd(orc):
             assert np.max(np.abs(mine - ref)) < 1e-12, np.max(np.abs(mine - ref))
 
 
+# p23 ----------------------------------------------------------------------------
+def _gather_row(q, k, v, kd, vd, S, cu, s, t, h, G, causal):
+    """Operands of row (segment s, token t, head h) of a packed problem, gathered
+    the way the sampled GPU checks gather them."""
+    a, b = int(cu[s]), int(cu[s + 1])
+    hk = h // G
+    J = np.arange(a, a + t + 1) if causal else np.arange(a, b)
+    n = a + t
+    kd_row = kd[n, :S, hk] if S > 0 else None
+    vd_row = vd[n, :S, hk] if S > 0 else None
+    return q[n, h], k[J, hk], v[J, hk], kd_row, vd_row
+
+
+def pin_joint_rows(orc):
+    """The one-row form used by the full-size sampled checks: (1) equals the
+    whole-tensor oracle row by row (causal and not, with and without depth slots,
+    grouped heads, packed segments of unequal length); (2) reproduces the hand
+    example on its own; (3) stays finite when a depth logit dominates by 10^4
+    (the max must run over the depth logits too) and returns that slot's value."""
+    rng = np.random.default_rng(23)
+    for causal, S, (Hq, Hkv), lens in [(True, 3, (4, 2), (5, 1, 9)), (False, 2, (2, 2), (7, 4)),
+                                       (True, 0, (3, 1), (6, 2)), (False, 0, (4, 4), (3,)),
+                                       (True, 4, (6, 3), (8,))]:
+        N, d, G = sum(lens), 6, Hq // Hkv
+        q = rng.standard_normal((N, Hq, d))
+        k = rng.standard_normal((N, Hkv, d))
+        v = rng.standard_normal((N, Hkv, d))
+        kd = rng.standard_normal((N, S + 1, Hkv, d))
+        vd = rng.standard_normal((N, S + 1, Hkv, d))
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        o, lse = orc.joint_attention(q, k, v, kd, vd, S, causal, 0.45, cu_seqlens=cu)
+        for s, L in enumerate(lens):
+            for t in range(L):
+                for h in range(Hq):
+                    ro, rl = orc.joint_rows(*_gather_row(q, k, v, kd, vd, S, cu, s, t, h, G, causal), 0.45)
+                    n = int(cu[s]) + t
+                    assert np.max(np.abs(ro - o[n, h])) < 1e-13, (causal, S, s, t, h)
+                    assert abs(rl - lse[h, n]) < 1e-13
+    # (2) hand example: weights 1 and 3
+    with open(os.path.join(GOLDEN, "hand_example.json")) as f:
+        g = json.load(f)
+    o, lse = orc.joint_rows(np.array([g["q"]]), np.array([[g["k"]]]), np.array([[g["v"]]]),
+                            np.array([[math.log(3.0)]]), np.array([[g["v_depth"]]]), g["scale"])
+    assert abs(o.item() - g["out"]) < 1e-15 and abs(lse - math.log(4.0)) < 1e-15
+    # (3) a dominant depth logit (1e4 above every sequence logit)
+    q_row = np.array([1.0, 0.0])
+    ks = np.array([[0.0, 1.0], [0.5, 2.0]])
+    vs = np.array([[1.0, 2.0], [3.0, 4.0]])
+    kdr = np.array([[1e4, 0.0], [-1.0, 0.0]])
+    vdr = np.array([[-7.0, 5.0], [9.0, 9.0]])
+    o, lse = orc.joint_rows(q_row, ks, vs, kdr, vdr, 1.0)
+    assert np.all(np.isfinite(o)) and np.isfinite(lse)
+    assert np.max(np.abs(o - vdr[0])) < 1e-12 and abs(lse - 1e4) < 1e-9
+
+
 ALL_PINS = [
     pin_empty_depth_is_sdpa,
     pin_equal_logits_plain_mean,
@@ -454,4 +509,5 @@ ALL_PINS = [
     pin_backward_finite_differences,
     pin_backward_sums,
     pin_backward_empty_depth_is_sdpa_autograd,
+    pin_joint_rows,
 ]

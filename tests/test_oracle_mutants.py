@@ -45,6 +45,12 @@ MUTANTS = {
     "bwd_dv_from_dS": ("dv[st : st + kend, hk] += Pa.T @ dO[r0:r1]", "dv[st : st + kend, hk] += dSa.T @ dO[r0:r1]"),
     "bwd_diagonal_dropped": ("rows[:, None] >= np.arange(kend)", "rows[:, None] > np.arange(kend)"),
     "bwd_depth_values_as_keys": ("VD = vdp[st:en, :n_depth, hk]", "VD = kdp[st:en, :n_depth, hk]"),
+    "rows_depth_logit_unscaled": ("b = scale * (kd_row @ q_row)", "b = kd_row @ q_row"),
+    "rows_depth_out_of_max": ("M = max(a.max(initial=-np.inf), b.max(initial=-np.inf))",
+                              "M = a.max(initial=-np.inf)"),
+    "rows_depth_out_of_denominator": ("Z = w.sum() + u.sum()", "Z = w.sum()"),
+    "rows_lse_base_two": ("return o, M + math.log(Z)", "return o, M + math.log2(Z)"),
+    "rows_depth_keys_as_values": ("u @ vd_row", "u @ kd_row"),
 }
 
 
