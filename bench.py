@@ -3,16 +3,22 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 
 One step = one launch of the fused forward (sequence + depth, all rows, all heads)
-over one batch of seeded synthetic inputs already resident in HBM. Consecutive
-steps cycle through enough independent input batches that the 256 MB Infinity
-Cache cannot hold them, so every step streams its operands from HBM. The timed
-steps are replayed as a HIP graph (one graph launch per pass over the batches) so
-that host launch overhead does not enter the per-step time.
+over one batch of seeded synthetic inputs already resident in HBM. The default
+workload is packed_bf16 (8 packed sequences, 65536 tokens, 16 heads, d = 128, 62
+depth slots), the largest configuration that fits one GPU. Consecutive steps
+cycle through enough independent input batches that the 256 MB Infinity Cache
+cannot hold them, so every step streams its operands from HBM. The timed steps
+are replayed as a HIP graph (one graph launch per pass over the batches) so that
+host launch overhead does not enter the per-step time.
 
 Prints one JSON line. ``value`` = (sequence + depth FLOPs) per step / step time.
 ``roofline`` rates the fused kernel against the bound that limits it at this
 workload (HBM bytes or bf16 MFMA FLOPs, whichever takes longer at peak).
-``cpu_baseline`` times the fp64 oracle on a bounded sample on the host.
+``parts`` times the sequence part alone (TFLOP/s, fraction of bf16 MFMA peak)
+and the depth part alone (depth-KV GB/s, fraction of HBM peak) with the same
+kernel code, next to the rates this GPU attains on a plain streaming read and a
+register-only MFMA loop. ``cpu_baseline`` times the fp64 oracle on a bounded
+sample on the host.
 """
 from __future__ import annotations
 
@@ -52,10 +58,11 @@ def kernel_source_sha(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_name(w) -> str:
+def kernel_name(w, phase: int = 3) -> str:
     """The kernel instance the library launches for this workload (mirrors the
     host dispatch: heads per workgroup, waves per workgroup, depth schedule,
-    shared or split tiles)."""
+    shared or split tiles); ``phase`` 1 or 2 names the sequence-only or
+    depth-only launch."""
     if _is_decode(w):
         G = w.group
         gd = next(g for g in (8, 4, 2, 1) if G % g == 0)
@@ -75,7 +82,7 @@ def kernel_name(w) -> str:
             break
     if waves == 0:
         waves, split = 2, True
-    mode = 0 if w.n_depth == 0 else 1
+    mode = 2 if phase == 2 else 0 if (w.n_depth == 0 or phase == 1) else 1
     return f"moda_fwd_bf16_kernel<{w.head_dim}, {gb}, {waves}, {mode}, false, {str(split).lower()}>"
 
 
@@ -741,12 +748,13 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: about 2 s of GPU time)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="small_bf16")
+    ap.add_argument("--workload", default="packed_bf16")
     ap.add_argument("--backward", action="store_true", help="time the backward pass of the workload instead")
     ap.add_argument("--writer", action="store_true", help="time the depth-KV writer on the workload's shapes instead")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
+    ap.add_argument("--no-parts", action="store_true", help="skip the sequence-only and depth-only timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "LOG"),
@@ -803,6 +811,8 @@ def main(argv=None) -> int:
         return bench_backward(args, w, dev)
     if args.writer:
         return bench_writer(args, w, dev)
+    peaks = attained_peaks(dev)
+    print(f"# attained peaks: {peaks}", file=sys.stderr, flush=True)
     batch_bytes = w.total_bytes()
     n_batches = max(1, min(32, math.ceil(CACHE_DEFEAT_BYTES / batch_bytes)))
     print(f"# workload {w.name}: {w.desc}; {n_batches} input batch(es) of {batch_bytes / 1e6:.1f} MB", file=sys.stderr,
@@ -814,55 +824,18 @@ def main(argv=None) -> int:
     outs = [torch.empty(w.shape_q(), dtype=odt, device=dev) for _ in range(n_batches)]
     lses = [torch.empty(w.shape_lse(), dtype=torch.float32, device=dev) for _ in range(n_batches)]
     torch.cuda.synchronize()
-
-    def step(i):
-        x = inputs[i % n_batches]
-        attn_fwd(x["q"], x["k"], x["v"], x["kd"], x["vd"], n_depth=w.n_depth, causal=w.causal, scale=w.scale,
-                 cu_seqlens=cu, max_seqlen=max_len, out=outs[i % n_batches], lse=lses[i % n_batches])
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # rough per-step time to size the timed region
-    t0 = time.perf_counter()
-    for i in range(n_batches):
-        step(i)
-    torch.cuda.synchronize()
-    rough = (time.perf_counter() - t0) / n_batches
-    steps = args.steps or max(n_batches, int(2.0 / max(rough, 1e-6)))
-    steps = max(n_batches, (steps // n_batches) * n_batches)  # whole passes over the batches
-
     stream = torch.cuda.current_stream(dev)
-    use_graph = not args.no_graph
-    graph = None
-    if use_graph:
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            step(0)  # one eager call on the capture stream before capture
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(n_batches):
-                step(i)
-        torch.cuda.synchronize()
-        for _ in range(2):
-            graph.replay()
-        torch.cuda.synchronize()
 
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    if use_graph:
-        for _ in range(steps // n_batches):
-            graph.replay()
-    else:
-        for i in range(steps):
-            step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    def make_step(phase):
+        def step(i):
+            x = inputs[i % n_batches]
+            attn_fwd(x["q"], x["k"], x["v"], x["kd"], x["vd"], n_depth=w.n_depth, causal=w.causal, scale=w.scale,
+                     cu_seqlens=cu, max_seqlen=max_len, out=outs[i % n_batches], lse=lses[i % n_batches],
+                     phase=phase)
+        return step
+
+    step = make_step(3)
+    ms, steps, use_graph = time_steps(step, n_batches, args, dev, stream)
     sec = ms / 1e3
 
     # replayed results must equal an eager call on the same inputs (bitwise)
@@ -876,8 +849,46 @@ def main(argv=None) -> int:
     if not replay_ok:
         print("error: timed replays differ from an eager call", file=sys.stderr)
 
+    # the two parts alone, from the same kernel code (the other part compiled out)
+    part_ms = {}
+    if w.bf16 and w.n_depth > 0 and not args.no_parts:
+        for phase in (1, 2):
+            part_ms[phase], _, _ = time_steps(make_step(phase), n_batches, args, dev, stream)
+            print(f"# phase {phase}: {part_ms[phase]:.4f} ms per launch", file=sys.stderr, flush=True)
+
     flops = w.seq_flops() + w.depth_flops()
     tflops = flops / sec / 1e12
+    peak_f = PEAK_BF16_TFLOPS if w.bf16 else PEAK_F32_TFLOPS
+    parts = {
+        "fused": {
+            "ms": round(ms, 5),
+            "seq_tflops": round(w.seq_flops() / sec / 1e12, 3),
+            "mfma_frac_of_peak": round(tflops / peak_f, 4),
+            "depth_kv_gbs": round(w.depth_bytes() / sec / 1e9, 1),
+            "all_bytes_gbs": round(w.total_bytes() / sec / 1e9, 1),
+            "hbm_frac_of_peak": round(w.total_bytes() / sec / 1e9 / PEAK_HBM_GBS, 4),
+        },
+        "attained_peaks": peaks,
+    }
+    if part_ms:
+        s1, s2 = part_ms[1] / 1e3, part_ms[2] / 1e3
+        seq_tf = w.seq_flops() / s1 / 1e12
+        dep_gbs = w.depth_bytes() / s2 / 1e9
+        dep_all = (w.depth_bytes() + depth_phase_other_bytes(w)) / s2 / 1e9
+        parts["sequence_only"] = {
+            "ms": round(part_ms[1], 5), "kernel": kernel_name(w, phase=1), "tflops": round(seq_tf, 2),
+            "mfma_frac_of_peak": round(seq_tf / PEAK_BF16_TFLOPS, 4),
+            "mfma_frac_of_attained": round(seq_tf / peaks["mfma_bf16_tflops"], 4),
+        }
+        parts["depth_only"] = {
+            "ms": round(part_ms[2], 5), "kernel": kernel_name(w, phase=2), "depth_kv_gbs": round(dep_gbs, 1),
+            "hbm_frac_of_peak": round(dep_gbs / PEAK_HBM_GBS, 4),
+            "hbm_frac_of_attained": round(dep_gbs / peaks["hbm_stream_read_gbs"], 4),
+            "all_bytes_gbs": round(dep_all, 1),
+        }
+        # depth bytes over the time the fused launch spends beyond the sequence part alone
+        extra = sec - s1
+        parts["depth_kv_gbs_beside_sequence"] = round(w.depth_bytes() / extra / 1e9, 1) if extra > 0 else None
     rec = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -904,25 +915,126 @@ def main(argv=None) -> int:
             "input_batches": n_batches,
             "graph": use_graph,
         },
-        "parts": {
-            "seq_tflops_in_fused": round(w.seq_flops() / sec / 1e12, 3),
-            "mfma_frac_of_peak": round(tflops / (PEAK_BF16_TFLOPS if w.bf16 else PEAK_F32_TFLOPS), 4),
-            "depth_kv_gbs_in_fused": round(w.depth_bytes() / sec / 1e9, 1),
-            "all_bytes_gbs": round(w.total_bytes() / sec / 1e9, 1),
-            "hbm_frac_of_peak": round(w.total_bytes() / sec / 1e9 / PEAK_HBM_GBS, 4),
-        },
+        "parts": parts,
         "kernel": kernel_name(w),
         "kernel_source_sha": kernel_source_sha(),
         "replay_matches_eager": replay_ok,
         "roofline": roofline(w, sec),
         "cpu_baseline": None,
     }
-    del inputs, outs, lses, graph
+    del inputs, outs, lses
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(rec), flush=True)
     return 0 if replay_ok else 1
+
+
+def depth_phase_other_bytes(w) -> float:
+    """Bytes the depth-only launch moves besides the depth slots: q read, out and
+    lse written once."""
+    e = w.elem_bytes()
+    return w.n_tokens * w.n_heads_q * (2 * w.head_dim * e + 4.0)
+
+
+def time_steps(step, n_batches, args, dev, stream):
+    """Warm-up, then whole passes over the input batches replayed as one HIP graph
+    per pass (or launched from the host with --no-graph), timed with events on the
+    stream the kernels run on. Returns (ms per step, steps, graph used)."""
+    import torch
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # rough per-step time to size the timed region
+    t0 = time.perf_counter()
+    for i in range(n_batches):
+        step(i)
+    torch.cuda.synchronize()
+    rough = (time.perf_counter() - t0) / n_batches
+    steps = args.steps or max(n_batches, int(2.0 / max(rough, 1e-6)))
+    steps = max(n_batches, (steps // n_batches) * n_batches)  # whole passes over the batches
+    use_graph = not args.no_graph
+    graph = None
+    if use_graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0)  # one eager call on the capture stream before capture
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n_batches):
+                step(i)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    if use_graph:
+        for _ in range(steps // n_batches):
+            graph.replay()
+    else:
+        for i in range(steps):
+            step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return start.elapsed_time(end) / steps, steps, use_graph
+
+
+def attained_peaks(dev) -> dict:
+    """The rates this GPU reaches on a plain 16-byte streaming read of 4 GiB and on
+    a register-only bf16 MFMA loop (libmoda_peaks.so), each the best of 5 timed
+    launches after one warm-up."""
+    import ctypes
+
+    import torch
+
+    from joint_sequence_depth_amd import build as _b
+
+    L = ctypes.CDLL(_b.PEAKS_PATH)
+    L.moda_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                        ctypes.c_void_p]
+    L.moda_peak_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    L.moda_peak_mfma_flops_per_launch.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    L.moda_peak_mfma_flops_per_launch.restype = ctypes.c_double
+    stream = torch.cuda.current_stream(dev)
+    nbytes, wg_read = 4 << 30, 4096
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(7)
+    sink = torch.empty(8192, dtype=torch.float32, device=dev)
+    iters, wg_mfma = 2048, 2048
+
+    def best(fn):
+        fn()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        return min(ts)
+
+    def read():
+        rc = L.moda_peak_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), wg_read, stream.cuda_stream)
+        assert rc == 0, rc
+
+    def mfma():
+        rc = L.moda_peak_mfma_bf16(iters, sink.data_ptr(), wg_mfma, stream.cuda_stream)
+        assert rc == 0, rc
+
+    t_read = best(read)
+    t_mfma = best(mfma)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"hbm_stream_read_gbs": round(nbytes / t_read / 1e9, 1),
+            "mfma_bf16_tflops": round(L.moda_peak_mfma_flops_per_launch(iters, wg_mfma) / t_mfma / 1e12, 1)}
 
 
 if __name__ == "__main__":

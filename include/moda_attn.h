@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MODA_ABI_VERSION 4
+#define MODA_ABI_VERSION 5
 
 /* status codes */
 #define MODA_OK 0
@@ -97,6 +97,32 @@ int moda_attn_fwd_varlen(const void* q, const void* k, const void* v, const void
                          const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen,
                          int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
                          int32_t n_depth, int32_t causal, float scale, void* stream);
+
+/*
+ * The two parts of the forward, one at a time (for measuring each part and for
+ * checking the merge of their partial results; not needed to compute the
+ * operator). MoDA deck, slide "Shared online-softmax states preserve the joint
+ * operator": the sequence blocks and the depth blocks update one running
+ * softmax state, so each part alone is a softmax of its own, and the operator is
+ * their merge by log-sum-exp:
+ *   phase_mask 1: out = softmax over the sequence keys alone, lse = its log-sum-exp;
+ *   phase_mask 2: out = softmax over the token's depth slots alone (n_depth > 0);
+ *   phase_mask 3: the operator (identical to moda_attn_fwd / moda_attn_fwd_varlen).
+ * With (o_s, l_s) and (o_d, l_d) from phases 1 and 2, l = ln(e^l_s + e^l_d) and
+ * out = e^(l_s - l) o_s + e^(l_d - l) o_d. Each phase runs the kernel of the fused
+ * call with the other part compiled out. Arguments, checks and errors as for
+ * moda_attn_fwd / moda_attn_fwd_varlen; MODA_ERR_VALUE for any other phase_mask
+ * and for phase_mask 2 with n_depth == 0.
+ */
+int moda_attn_fwd_phases(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
+                         void* out, float* lse, int32_t dtype, int32_t out_dtype, int64_t batch, int64_t seqlen,
+                         int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
+                         int32_t n_depth, int32_t causal, float scale, int32_t phase_mask, void* stream);
+int moda_attn_fwd_varlen_phases(const void* q, const void* k, const void* v, const void* k_depth,
+                                const void* v_depth, void* out, float* lse, int32_t dtype, int32_t out_dtype,
+                                const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen,
+                                int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
+                                int32_t n_depth, int32_t causal, float scale, int32_t phase_mask, void* stream);
 
 /*
  * One decode step: a single new token per sequence attends, through the same

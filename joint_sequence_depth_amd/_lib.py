@@ -29,7 +29,8 @@ STATUS_NAMES = {
 }
 
 # every symbol include/moda_attn.h declares
-EXPORTS = ("moda_attn_fwd", "moda_attn_fwd_varlen", "moda_attn_decode", "moda_attn_decode_workspace_size",
+EXPORTS = ("moda_attn_fwd", "moda_attn_fwd_varlen", "moda_attn_fwd_phases", "moda_attn_fwd_varlen_phases",
+           "moda_attn_decode", "moda_attn_decode_workspace_size",
            "moda_attn_bwd", "moda_attn_bwd_varlen", "moda_attn_bwd_workspace_size", "moda_depth_kv_write",
            "moda_last_error", "moda_abi_version")
 
@@ -57,6 +58,10 @@ def lib() -> ctypes.CDLL:
         L.moda_attn_fwd.restype = ctypes.c_int
         L.moda_attn_fwd_varlen.argtypes = [vp] * 7 + [i32, i32, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32, f32, vp]
         L.moda_attn_fwd_varlen.restype = ctypes.c_int
+        L.moda_attn_fwd_phases.argtypes = L.moda_attn_fwd.argtypes[:-1] + [i32, vp]
+        L.moda_attn_fwd_phases.restype = ctypes.c_int
+        L.moda_attn_fwd_varlen_phases.argtypes = L.moda_attn_fwd_varlen.argtypes[:-1] + [i32, vp]
+        L.moda_attn_fwd_varlen_phases.restype = ctypes.c_int
         L.moda_attn_decode.argtypes = [vp] * 7 + [i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp, i64, vp]
         L.moda_attn_decode.restype = ctypes.c_int
         L.moda_attn_decode_workspace_size.argtypes = [i64, i32, i32, i32, i32]
@@ -126,6 +131,7 @@ def attn_fwd(
     out_dtype=None,
     return_lse: bool = True,
     slot_offset: int = 0,
+    phase: int = 3,
 ):
     """MoDA joint sequence/depth attention forward through the C ABI.
 
@@ -138,6 +144,10 @@ def attn_fwd(
     With ``return_lse=False`` no lse is written (NULL at the C ABI) and None is returned.
     ``slot_offset`` reads the window of slots [slot_offset, slot_offset + n_depth)
     (the depth base pointers move by that many slots; the slot stride stays S_cap).
+    ``phase`` 1 or 2 computes the sequence part or the depth part alone (each its
+    own softmax, for measurement and for the merge check); 3, the default, is the
+    operator. Packed calls need ``max_seqlen`` (the longest sequence): the binding
+    never reads ``cu_seqlens`` back from the device.
     """
     import torch
 
@@ -199,18 +209,20 @@ def attn_fwd(
             raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
         n_seqs = cu_seqlens.numel() - 1
         if max_seqlen is None:
-            cu_host = cu_seqlens.cpu()
-            max_seqlen = int((cu_host[1:] - cu_host[:-1]).max()) if n_seqs > 0 else 0
-        status = L.moda_attn_fwd_varlen(
-            _ptr(q), _ptr(k), _ptr(v), kd_ptr, vd_ptr, _ptr(out), _ptr(lse),
-            code, out_code, _ptr(cu_seqlens), n_seqs, q.shape[0], int(max_seqlen), Hq, Hkv, d, s_cap, int(n_depth),
-            int(bool(causal)), float(scale), stream,
-        )
+            raise ValueError("packed calls need max_seqlen (the longest sequence); cu_seqlens stays on the device")
+        args = (_ptr(q), _ptr(k), _ptr(v), kd_ptr, vd_ptr, _ptr(out), _ptr(lse), code, out_code, _ptr(cu_seqlens),
+                n_seqs, q.shape[0], int(max_seqlen), Hq, Hkv, d, s_cap, int(n_depth), int(bool(causal)), float(scale))
+        if phase == 3:
+            status = L.moda_attn_fwd_varlen(*args, stream)
+        else:
+            status = L.moda_attn_fwd_varlen_phases(*args, int(phase), stream)
     else:
-        status = L.moda_attn_fwd(
-            _ptr(q), _ptr(k), _ptr(v), kd_ptr, vd_ptr, _ptr(out), _ptr(lse),
-            code, out_code, q.shape[0], q.shape[1], Hq, Hkv, d, s_cap, int(n_depth), int(bool(causal)), float(scale), stream,
-        )
+        args = (_ptr(q), _ptr(k), _ptr(v), kd_ptr, vd_ptr, _ptr(out), _ptr(lse), code, out_code, q.shape[0],
+                q.shape[1], Hq, Hkv, d, s_cap, int(n_depth), int(bool(causal)), float(scale))
+        if phase == 3:
+            status = L.moda_attn_fwd(*args, stream)
+        else:
+            status = L.moda_attn_fwd_phases(*args, int(phase), stream)
     _check(status)
     return out, lse
 
@@ -335,7 +347,8 @@ def attn_bwd(
     tensors). Slots [n_depth, S_cap) of the depth gradients are zero when this
     function allocates them, and left untouched in a caller's ``grads``, a
     tuple of five preallocated tensors, and ``workspace`` (a uint8 device tensor of
-    ``bwd_workspace_size`` bytes) make the call allocation-free."""
+    ``bwd_workspace_size`` bytes) make the call allocation-free. Packed calls need
+    ``max_seqlen``."""
     import torch
 
     varlen = cu_seqlens is not None
@@ -396,8 +409,7 @@ def attn_bwd(
             raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
         n_seqs = cu_seqlens.numel() - 1
         if max_seqlen is None:
-            cu_host = cu_seqlens.cpu()
-            max_seqlen = int((cu_host[1:] - cu_host[:-1]).max()) if n_seqs > 0 else 0
+            raise ValueError("packed calls need max_seqlen (the longest sequence); cu_seqlens stays on the device")
         status = L.moda_attn_bwd_varlen(*ptrs, code, gcode, _ptr(cu_seqlens), n_seqs, N, int(max_seqlen), Hq, Hkv, d,
                                         s_cap, int(n_depth), int(bool(causal)), float(scale), _ptr(workspace), wsb,
                                         stream)

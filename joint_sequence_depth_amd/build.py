@@ -8,6 +8,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -15,8 +16,16 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmoda_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+PEAKS_PATH = os.path.join(PKG, "libmoda_peaks.so")  # measurement only (include/moda_peaks.h)
 SOURCES = ["moda_attn.hip", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_decode.hip", "moda_bwd.hip",
            "moda_depth_kv.hip"]
+# Compilation units: (source, object stem, extra flags). The bf16 forward's
+# template instances are split by head dim and query heads per workgroup, one
+# unit each, so that they compile side by side.
+UNITS = [(src, src[:-4], []) for src in SOURCES if src != "moda_fwd_bf16.hip"] + [
+    ("moda_fwd_bf16.hip", f"moda_fwd_bf16_d{d}_g{g}", [f"-DMODA_FWD_D={d}", f"-DMODA_FWD_GB={g}"])
+    for d in (64, 128) for g in (1, 2, 4)
+]
 # Sources whose kernels keep matrix-core accumulators in AGPRs (the backward
 # holds two 128 x 32 fp32 accumulators per wave, more than the VGPRs alone)
 AGPR_ACCUMULATORS = {"moda_bwd.hip"}
@@ -59,15 +68,21 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *compile_flags(src), "-c", os.path.join(CSRC, src), "-o", obj]
-        _run(cmd, verbose)
-        objs.append(obj)
-    tmp = LIB_PATH + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB_PATH)
+    objs = [os.path.join(objdir, stem + ".o") for _, stem, _ in UNITS]
+    cmds = [[cc, *compile_flags(src), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+            for (src, _, extra), obj in zip(UNITS, objs)]
+    # one hipcc per unit, side by side (each is a separate process); the
+    # attained-peak microbenchmarks go into a library of their own
+    peaks_obj = os.path.join(objdir, "moda_peaks.o")
+    cmds.append([cc, *compile_flags("moda_peaks.hip"), "-c", os.path.join(CSRC, "moda_peaks.hip"), "-o", peaks_obj])
+    workers = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for f in [ex.submit(_run, cmd, verbose) for cmd in cmds]:
+            f.result()
+    for path, ob in ((LIB_PATH, objs), (PEAKS_PATH, [peaks_obj])):
+        tmp = path + ".tmp"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *ob, "-o", tmp], verbose)
+        os.replace(tmp, path)
     return LIB_PATH
 
 

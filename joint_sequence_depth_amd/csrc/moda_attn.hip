@@ -79,7 +79,23 @@ moda::Params base_params(const Common& c) {
   p.n_depth = c.n_depth;
   p.causal = c.causal;
   p.scale_log2 = c.scale * 1.4426950408889634f;
+  p.phase = moda::kPhaseBoth;
   return p;
+}
+
+hipError_t launch_fwd_bf16(const moda::Params& p, int d, int gb, int waves, bool split, bool out_f32,
+                           hipStream_t stream) {
+  const int phase = p.phase;
+  if (d == 64) {
+    if (gb == 1) return moda::launch_fwd_bf16_dg<64, 1>(p, waves, split, phase, out_f32, stream);
+    if (gb == 2) return moda::launch_fwd_bf16_dg<64, 2>(p, waves, split, phase, out_f32, stream);
+    if (gb == 4) return moda::launch_fwd_bf16_dg<64, 4>(p, waves, split, phase, out_f32, stream);
+  } else if (d == 128) {
+    if (gb == 1) return moda::launch_fwd_bf16_dg<128, 1>(p, waves, split, phase, out_f32, stream);
+    if (gb == 2) return moda::launch_fwd_bf16_dg<128, 2>(p, waves, split, phase, out_f32, stream);
+    if (gb == 4) return moda::launch_fwd_bf16_dg<128, 4>(p, waves, split, phase, out_f32, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 // Fills the work decomposition and launches. max_len bounds every segment length.
@@ -112,7 +128,7 @@ int dispatch(moda::Params& p, const Common& c, int64_t n_seg, int64_t max_len, h
     p.xcd_interleave = (!split && n_pairs % 8 == 0) ? 1 : 0;
     p.qb_major = split ? 1 : 0;
     if (nqb > kMaxTiles || p.n_tiles > kMaxTiles) return fail(MODA_ERR_SHAPE, "problem too large for one launch");
-    err = moda::launch_fwd_bf16(p, c.d, gb, waves, split, c.out_dtype == MODA_DTYPE_F32, stream);
+    err = launch_fwd_bf16(p, c.d, gb, waves, split, c.out_dtype == MODA_DTYPE_F32, stream);
   } else {
     const int64_t nqb = (max_len + moda::kF32BlockRows - 1) / moda::kF32BlockRows;
     p.n_hgroups = 1;
@@ -249,14 +265,20 @@ int launch_bwd_checked(moda::BwdParams& p, const BwdArgs& a, int64_t n_seg, int6
   return MODA_OK;
 }
 
-}  // namespace
+// phase_mask: kPhaseBoth (the operator), kPhaseSeq or kPhaseDepth (one part's
+// own softmax). Checked after the no-op cases, like every other argument.
+int check_phase(int32_t phase, int32_t n_depth) {
+  if (phase != moda::kPhaseSeq && phase != moda::kPhaseDepth && phase != moda::kPhaseBoth)
+    return fail(MODA_ERR_VALUE, "phase_mask must be 1 (sequence), 2 (depth) or 3 (both), got %d", phase);
+  if (phase == moda::kPhaseDepth && n_depth == 0)
+    return fail(MODA_ERR_VALUE, "the depth phase alone needs n_depth > 0");
+  return MODA_OK;
+}
 
-extern "C" {
-
-int moda_attn_fwd(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth, void* out,
-                  float* lse, int32_t dtype, int32_t out_dtype, int64_t batch, int64_t seqlen, int32_t n_heads_q, int32_t n_heads_kv,
-                  int32_t head_dim, int32_t depth_capacity, int32_t n_depth, int32_t causal, float scale,
-                  void* stream) {
+int fwd_batch(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth, void* out,
+              float* lse, int32_t dtype, int32_t out_dtype, int64_t batch, int64_t seqlen, int32_t n_heads_q,
+              int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t n_depth, int32_t causal,
+              float scale, int32_t phase, void* stream) {
   if (batch < 0 || seqlen < 0) return fail(MODA_ERR_SHAPE, "batch and seqlen must be >= 0");
   const Common c{q,        k,          v,        k_depth,        v_depth, out,     lse,    dtype,
                  out_dtype, n_heads_q, n_heads_kv, head_dim, depth_capacity, n_depth, causal, scale};
@@ -264,10 +286,13 @@ int moda_attn_fwd(const void* q, const void* k, const void* v, const void* k_dep
     g_err[0] = '\0';
     return MODA_OK;
   }
-  const int rc = check_common(c);
+  int rc = check_common(c);
+  if (rc != MODA_OK) return rc;
+  rc = check_phase(phase, n_depth);
   if (rc != MODA_OK) return rc;
   if (batch > 0x7fffffffLL) return fail(MODA_ERR_SHAPE, "batch too large");
   moda::Params p = base_params(c);
+  p.phase = phase;
   p.cu_seqlens = nullptr;
   p.uniform_len = seqlen;
   p.total_tokens = batch * seqlen;
@@ -277,11 +302,10 @@ int moda_attn_fwd(const void* q, const void* k, const void* v, const void* k_dep
   return dispatch(p, c, batch, seqlen, static_cast<hipStream_t>(stream));
 }
 
-int moda_attn_fwd_varlen(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
-                         void* out, float* lse, int32_t dtype, int32_t out_dtype, const int32_t* cu_seqlens, int32_t n_seqs,
-                         int64_t total_tokens, int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv,
-                         int32_t head_dim, int32_t depth_capacity, int32_t n_depth, int32_t causal, float scale,
-                         void* stream) {
+int fwd_varlen(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth, void* out,
+               float* lse, int32_t dtype, int32_t out_dtype, const int32_t* cu_seqlens, int32_t n_seqs,
+               int64_t total_tokens, int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+               int32_t depth_capacity, int32_t n_depth, int32_t causal, float scale, int32_t phase, void* stream) {
   if (n_seqs < 0 || total_tokens < 0 || max_seqlen < 0)
     return fail(MODA_ERR_SHAPE, "n_seqs, total_tokens and max_seqlen must be >= 0");
   const Common c{q,        k,          v,        k_depth,        v_depth, out,     lse,    dtype,
@@ -292,10 +316,13 @@ int moda_attn_fwd_varlen(const void* q, const void* k, const void* v, const void
   }
   if (!cu_seqlens) return fail(MODA_ERR_NULL, "cu_seqlens must be non-NULL");
   if ((int64_t)max_seqlen > total_tokens) return fail(MODA_ERR_SHAPE, "max_seqlen exceeds total_tokens");
-  const int rc = check_common(c);
+  int rc = check_common(c);
+  if (rc != MODA_OK) return rc;
+  rc = check_phase(phase, n_depth);
   if (rc != MODA_OK) return rc;
   if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return fail(MODA_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
   moda::Params p = base_params(c);
+  p.phase = phase;
   p.cu_seqlens = cu_seqlens;
   p.uniform_len = 0;
   p.total_tokens = total_tokens;
@@ -303,6 +330,110 @@ int moda_attn_fwd_varlen(const void* q, const void* k, const void* v, const void
   p.lse_head_stride = total_tokens;
   p.lse_batch_layout = 0;
   return dispatch(p, c, n_seqs, max_seqlen, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+namespace moda {
+
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+int decode_prepare(const DecodeArgs& a, DecodePlan& plan) {
+  if (a.batch < 0) return fail(MODA_ERR_SHAPE, "batch must be >= 0");
+  const Common c{a.q,         a.k_cache,  a.v_cache,  a.k_depth,        a.v_depth, a.out,     a.lse,
+                 a.dtype,     a.out_dtype, a.n_heads_q, a.n_heads_kv, a.head_dim, a.depth_capacity,
+                 a.n_depth,   1,          a.scale};
+  if (a.batch == 0) {
+    g_err[0] = '\0';
+    return kNothingToLaunch;
+  }
+  const int rc = check_common(c);
+  if (rc != MODA_OK) return rc;
+  if (a.max_cache_len < 1) return fail(MODA_ERR_SHAPE, "max_cache_len must be >= 1");
+  if (!a.cache_seqlens) return fail(MODA_ERR_NULL, "cache_seqlens must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(a.cache_seqlens) & 3u)
+    return fail(MODA_ERR_ALIGN, "cache_seqlens must be 4-byte aligned");
+  if (a.batch > 0x7fffffffLL) return fail(MODA_ERR_SHAPE, "batch too large");
+  DecodeParams& p = plan.p;
+  p = DecodeParams{};
+  p.q = a.q;
+  p.kc = a.k_cache;
+  p.vc = a.v_cache;
+  p.kd = a.n_depth > 0 ? a.k_depth : nullptr;
+  p.vd = a.n_depth > 0 ? a.v_depth : nullptr;
+  p.out = a.out;
+  p.lse = a.lse;
+  p.cache_seqlens = a.cache_seqlens;
+  p.workspace = nullptr;
+  p.B = a.batch;
+  p.T_max = a.max_cache_len;
+  p.Hq = a.n_heads_q;
+  p.Hkv = a.n_heads_kv;
+  p.G = a.n_heads_q / a.n_heads_kv;
+  plan.heads_per_block = decode_heads_per_block(p.G);
+  p.n_hgroups = p.G / plan.heads_per_block;
+  p.S_cap = a.depth_capacity;
+  p.n_depth = a.n_depth;
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.chunk = decode_chunk(a.batch, a.n_heads_q, a.n_heads_kv, a.head_dim, a.max_cache_len);
+  p.n_seq_chunks = (int32_t)((a.max_cache_len + p.chunk - 1) / p.chunk);
+  p.n_chunks = p.n_seq_chunks + 1;
+  p.n_partial_blocks = a.batch * a.n_heads_kv * p.n_hgroups * p.n_chunks;
+  if (p.n_partial_blocks > 0x7fffffffLL || a.batch * a.n_heads_q > 0x7fffffffLL)
+    return fail(MODA_ERR_SHAPE, "problem too large for one launch");
+  plan.head_dim = a.head_dim;
+  plan.bf16 = a.dtype == MODA_DTYPE_BF16;
+  plan.out_f32 = a.out_dtype == MODA_DTYPE_F32;
+  plan.workspace_bytes = decode_workspace_bytes(a.batch, a.n_heads_q, a.n_heads_kv, a.head_dim, a.max_cache_len);
+  return MODA_OK;
+}
+
+int decode_launch(DecodePlan& plan, void* workspace, hipStream_t stream) {
+  plan.p.workspace = static_cast<float*>(workspace);
+  const hipError_t err = launch_decode(plan.p, plan.head_dim, plan.heads_per_block, plan.bf16, plan.out_f32, stream);
+  if (err != hipSuccess) return fail(MODA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  g_err[0] = '\0';
+  return MODA_OK;
+}
+
+}  // namespace moda
+
+extern "C" {
+
+int moda_attn_fwd(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth, void* out,
+                  float* lse, int32_t dtype, int32_t out_dtype, int64_t batch, int64_t seqlen, int32_t n_heads_q, int32_t n_heads_kv,
+                  int32_t head_dim, int32_t depth_capacity, int32_t n_depth, int32_t causal, float scale,
+                  void* stream) {
+  return fwd_batch(q, k, v, k_depth, v_depth, out, lse, dtype, out_dtype, batch, seqlen, n_heads_q, n_heads_kv,
+                   head_dim, depth_capacity, n_depth, causal, scale, moda::kPhaseBoth, stream);
+}
+
+int moda_attn_fwd_varlen(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
+                         void* out, float* lse, int32_t dtype, int32_t out_dtype, const int32_t* cu_seqlens, int32_t n_seqs,
+                         int64_t total_tokens, int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv,
+                         int32_t head_dim, int32_t depth_capacity, int32_t n_depth, int32_t causal, float scale,
+                         void* stream) {
+  return fwd_varlen(q, k, v, k_depth, v_depth, out, lse, dtype, out_dtype, cu_seqlens, n_seqs, total_tokens,
+                    max_seqlen, n_heads_q, n_heads_kv, head_dim, depth_capacity, n_depth, causal, scale,
+                    moda::kPhaseBoth, stream);
+}
+
+int moda_attn_fwd_phases(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
+                         void* out, float* lse, int32_t dtype, int32_t out_dtype, int64_t batch, int64_t seqlen,
+                         int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
+                         int32_t n_depth, int32_t causal, float scale, int32_t phase_mask, void* stream) {
+  return fwd_batch(q, k, v, k_depth, v_depth, out, lse, dtype, out_dtype, batch, seqlen, n_heads_q, n_heads_kv,
+                   head_dim, depth_capacity, n_depth, causal, scale, phase_mask, stream);
+}
+
+int moda_attn_fwd_varlen_phases(const void* q, const void* k, const void* v, const void* k_depth,
+                                const void* v_depth, void* out, float* lse, int32_t dtype, int32_t out_dtype,
+                                const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen,
+                                int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
+                                int32_t n_depth, int32_t causal, float scale, int32_t phase_mask, void* stream) {
+  return fwd_varlen(q, k, v, k_depth, v_depth, out, lse, dtype, out_dtype, cu_seqlens, n_seqs, total_tokens,
+                    max_seqlen, n_heads_q, n_heads_kv, head_dim, depth_capacity, n_depth, causal, scale, phase_mask,
+                    stream);
 }
 
 int64_t moda_attn_decode_workspace_size(int64_t batch, int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
@@ -318,56 +449,19 @@ int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, co
                      const int32_t* cache_seqlens, int64_t batch, int32_t max_cache_len, int32_t n_heads_q,
                      int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t n_depth, float scale,
                      void* workspace, int64_t workspace_bytes, void* stream) {
-  if (batch < 0) return fail(MODA_ERR_SHAPE, "batch must be >= 0");
-  const Common c{q,        k_cache,    v_cache,  k_depth,        v_depth, out,     lse,   dtype,
-                 out_dtype, n_heads_q, n_heads_kv, head_dim, depth_capacity, n_depth, 1,     scale};
-  if (batch == 0) {
-    g_err[0] = '\0';
-    return MODA_OK;
-  }
-  const int rc = check_common(c);
+  const moda::DecodeArgs a{q,          k_cache,  v_cache,   k_depth,        v_depth, out,   lse,
+                           dtype,      out_dtype, cache_seqlens, batch,     max_cache_len, n_heads_q, n_heads_kv,
+                           head_dim,   depth_capacity, n_depth, scale};
+  moda::DecodePlan plan;
+  int rc = moda::decode_prepare(a, plan);
+  if (rc == moda::kNothingToLaunch) return MODA_OK;
   if (rc != MODA_OK) return rc;
-  if (max_cache_len < 1) return fail(MODA_ERR_SHAPE, "max_cache_len must be >= 1");
-  if (!cache_seqlens) return fail(MODA_ERR_NULL, "cache_seqlens must be non-NULL");
-  if (reinterpret_cast<uintptr_t>(cache_seqlens) & 3u) return fail(MODA_ERR_ALIGN, "cache_seqlens must be 4-byte aligned");
-  if (batch > 0x7fffffffLL) return fail(MODA_ERR_SHAPE, "batch too large");
-  const int64_t need = decode_workspace_bytes(batch, n_heads_q, n_heads_kv, head_dim, max_cache_len);
   if (!workspace) return fail(MODA_ERR_NULL, "workspace must be non-NULL");
   if (!aligned16(workspace)) return fail(MODA_ERR_ALIGN, "workspace must be 16-byte aligned");
-  if (workspace_bytes < need)
+  if (workspace_bytes < plan.workspace_bytes)
     return fail(MODA_ERR_SHAPE, "workspace too small: %lld bytes given, %lld needed", (long long)workspace_bytes,
-                (long long)need);
-  moda::DecodeParams p{};
-  p.q = q;
-  p.kc = k_cache;
-  p.vc = v_cache;
-  p.kd = n_depth > 0 ? k_depth : nullptr;
-  p.vd = n_depth > 0 ? v_depth : nullptr;
-  p.out = out;
-  p.lse = lse;
-  p.cache_seqlens = cache_seqlens;
-  p.workspace = static_cast<float*>(workspace);
-  p.B = batch;
-  p.T_max = max_cache_len;
-  p.Hq = n_heads_q;
-  p.Hkv = n_heads_kv;
-  p.G = n_heads_q / n_heads_kv;
-  const int gd = decode_heads_per_block(p.G);
-  p.n_hgroups = p.G / gd;
-  p.S_cap = depth_capacity;
-  p.n_depth = n_depth;
-  p.scale_log2 = scale * 1.4426950408889634f;
-  p.chunk = decode_chunk(batch, n_heads_q, n_heads_kv, head_dim, max_cache_len);
-  p.n_seq_chunks = (int32_t)((max_cache_len + p.chunk - 1) / p.chunk);
-  p.n_chunks = p.n_seq_chunks + 1;
-  p.n_partial_blocks = batch * n_heads_kv * p.n_hgroups * p.n_chunks;
-  if (p.n_partial_blocks > 0x7fffffffLL || batch * n_heads_q > 0x7fffffffLL)
-    return fail(MODA_ERR_SHAPE, "problem too large for one launch");
-  const hipError_t err = moda::launch_decode(p, head_dim, gd, dtype == MODA_DTYPE_BF16, out_dtype == MODA_DTYPE_F32,
-                                             static_cast<hipStream_t>(stream));
-  if (err != hipSuccess) return fail(MODA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
-  g_err[0] = '\0';
-  return MODA_OK;
+                (long long)plan.workspace_bytes);
+  return moda::decode_launch(plan, workspace, static_cast<hipStream_t>(stream));
 }
 
 int64_t moda_attn_bwd_workspace_size(int64_t total_tokens, int32_t n_heads_q, int32_t head_dim, int32_t n_depth) {

@@ -198,8 +198,9 @@ __device__ __forceinline__ Tile decode_tile(const Params& p) {
 }
 
 enum Mode : int {
-  kNoDepth = 0,  // n_depth == 0: sequence loop only
-  kSerial = 1,   // every wave runs a depth pass and the sequence loop, one after the other
+  kNoDepth = 0,    // sequence keys only (n_depth == 0, or the sequence phase alone)
+  kSerial = 1,     // every wave runs a depth pass and the sequence loop, one after the other
+  kDepthOnly = 2,  // depth slots only (the depth phase alone): the sequence loop is skipped
 };
 
 // LDS. Stages hold one K or V block each: BN rows of D bf16 without padding, the
@@ -295,7 +296,9 @@ moda_fwd_bf16_kernel(const Params p) {
   const float c2 = p.scale_log2;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(p.q);
   const int64_t kend = p.causal ? (len < t0 + TOK ? len : t0 + TOK) : len;
-  const int nkb = (int)((kend + BN - 1) / BN);  // sequence key blocks
+  constexpr bool SEQ = MODE != kDepthOnly;   // the sequence keys enter this launch's softmax
+  constexpr bool DEPTH = MODE != kNoDepth;   // the depth slots do
+  const int nkb = SEQ ? (int)((kend + BN - 1) / BN) : 0;  // sequence key blocks
 
   float* od = reinterpret_cast<float*>(smem + SM::OD_OFF);  // [ROWS][OS]
   float* md = reinterpret_cast<float*>(smem + SM::MD_OFF);  // [ROWS]
@@ -485,8 +488,8 @@ moda_fwd_bf16_kernel(const Params p) {
   // D = 64: the depth loads are issued
   // as the sequence loop starts and consumed after it, which hides their latency
   // (at D = 128 the loop needs those registers; the pass follows the loop).
-  constexpr bool EARLY_DEPTH = MODE == kSerial && SPLIT && D == 64;
-  constexpr bool depth_first = MODE == kSerial && !SPLIT && GB < 4;
+  constexpr bool EARLY_DEPTH = DEPTH && SPLIT && D == 64;
+  constexpr bool depth_first = (MODE == kSerial && GB < 4 && !SPLIT) || (MODE == kDepthOnly && !SPLIT);
   if constexpr (depth_first) {
     depth_begin();
     depth_end();
@@ -814,7 +817,7 @@ moda_fwd_bf16_kernel(const Params p) {
   if constexpr (SPLIT) {
     // finish the depth pass (its own LDS area), then merge the partial states of
     // waves 1 .. NW - 1 into wave 0's through the (now free) stage bytes
-    if constexpr (MODE == kSerial) {
+    if constexpr (DEPTH) {
       if constexpr (!EARLY_DEPTH) depth_begin();
       depth_end();
     }
@@ -853,8 +856,8 @@ moda_fwd_bf16_kernel(const Params p) {
         }
       m_run = m_new;
     }
-    if constexpr (MODE == kSerial) depth_fold();
-  } else if constexpr (MODE == kSerial && !depth_first) {
+    if constexpr (DEPTH) depth_fold();
+  } else if constexpr (DEPTH && !depth_first) {
     __syncthreads();  // every wave's loads have landed: the K/V area is free
     depth_begin();
     depth_end();
@@ -905,43 +908,33 @@ hipError_t launch_t(const Params& p, bool out_f32, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// phase: kPhaseBoth (the operator), kPhaseSeq (sequence keys only) or
+// kPhaseDepth (depth slots only, n_depth > 0): the same kernel code with the
+// other part compiled out.
 template <int D, int GB, int NW, bool SPLIT>
-hipError_t launch_d(const Params& p, bool out_f32, hipStream_t stream) {
-  if (p.n_depth == 0) return launch_t<D, GB, NW, kNoDepth, SPLIT>(p, out_f32, stream);
+hipError_t launch_d(const Params& p, int phase, bool out_f32, hipStream_t stream) {
+  if (phase == kPhaseDepth) return launch_t<D, GB, NW, kDepthOnly, SPLIT>(p, out_f32, stream);
+  if (p.n_depth == 0 || phase == kPhaseSeq) return launch_t<D, GB, NW, kNoDepth, SPLIT>(p, out_f32, stream);
   return launch_t<D, GB, NW, kSerial, SPLIT>(p, out_f32, stream);
-}
-
-template <int D, int GB>
-hipError_t launch_w(const Params& p, int waves, bool split, bool out_f32, hipStream_t stream) {
-  if (split) {
-    if (waves == kSplitWaves<D>) return launch_d<D, GB, kSplitWaves<D>, true>(p, out_f32, stream);
-    return hipErrorInvalidValue;
-  }
-  switch (waves) {
-    case 1: return launch_d<D, GB, 1, false>(p, out_f32, stream);
-    case 2: return launch_d<D, GB, 2, false>(p, out_f32, stream);
-    case 4: return launch_d<D, GB, 4, false>(p, out_f32, stream);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <int D>
-hipError_t launch_g(const Params& p, int heads_per_block, int waves, bool split, bool out_f32, hipStream_t stream) {
-  switch (heads_per_block) {
-    case 1: return launch_w<D, 1>(p, waves, split, out_f32, stream);
-    case 2: return launch_w<D, 2>(p, waves, split, out_f32, stream);
-    case 4: return launch_w<D, 4>(p, waves, split, out_f32, stream);
-  }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const Params& p, int head_dim, int heads_per_block, int waves, bool split, bool out_f32,
-                           hipStream_t stream) {
-  if (head_dim == 128) return launch_g<128>(p, heads_per_block, waves, split, out_f32, stream);
-  if (head_dim == 64) return launch_g<64>(p, heads_per_block, waves, split, out_f32, stream);
+// Every (head dim, heads per workgroup) pair is instantiated in a compilation
+// unit of its own (MODA_FWD_D / MODA_FWD_GB), so the instances build in parallel.
+template <int D, int GB>
+hipError_t launch_fwd_bf16_dg(const Params& p, int waves, bool split, int phase, bool out_f32, hipStream_t stream) {
+  if (split) {
+    if (waves == kSplitWaves<D>) return launch_d<D, GB, kSplitWaves<D>, true>(p, phase, out_f32, stream);
+    return hipErrorInvalidValue;
+  }
+  if (waves == 2) return launch_d<D, GB, 2, false>(p, phase, out_f32, stream);
+  if (waves == 4) return launch_d<D, GB, 4, false>(p, phase, out_f32, stream);
   return hipErrorInvalidValue;
 }
+
+#if defined(MODA_FWD_D) && defined(MODA_FWD_GB)
+template hipError_t launch_fwd_bf16_dg<MODA_FWD_D, MODA_FWD_GB>(const Params&, int, bool, int, bool, hipStream_t);
+#endif
 
 }  // namespace moda

@@ -91,8 +91,8 @@ __global__ __launch_bounds__(64) void moda_fwd_f32_kernel(const Params p) {
   for (int c = 0; c < D; ++c) o[c] = 0.f;
   float m = NEG_INF, l = 0.f;
 
-  // depth slots of this token
-  if (valid && p.n_depth > 0) {
+  // depth slots of this token (left out when the launch computes the sequence part alone)
+  if (valid && p.n_depth > 0 && (p.phase & kPhaseDepth)) {
     const float* KD = static_cast<const float*>(p.kd);
     const float* VD = static_cast<const float*>(p.vd);
     for (int i = 0; i < p.n_depth; ++i) {
@@ -102,7 +102,8 @@ __global__ __launch_bounds__(64) void moda_fwd_f32_kernel(const Params p) {
   }
   // sequence keys j <= t (all of the segment without the causal mask)
   const int64_t last_row = (t0 + 63 < len - 1) ? t0 + 63 : len - 1;
-  const int64_t jmax = p.causal ? last_row : len - 1;
+  // (no keys when the launch computes the depth part alone)
+  const int64_t jmax = !(p.phase & kPhaseSeq) ? -1 : p.causal ? last_row : len - 1;
   const int64_t my_jmax = p.causal ? t : len - 1;
   for (int64_t j = 0; j <= jmax; ++j) {
     if (valid && j <= my_jmax) {

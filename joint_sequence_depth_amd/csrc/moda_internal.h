@@ -38,12 +38,20 @@ struct Params {
   int32_t lse_batch_layout;   // 1: base = s * Hq * T; 0: base = seg_start
   int32_t xcd_interleave;     // 1: (segment, KV head) pairs go round-robin to the 8 XCDs
   int32_t qb_major;           // 1: tiles ordered by query block across all pairs (heaviest first)
+  int32_t phase;              // kPhaseBoth, or one part alone (kPhaseSeq / kPhaseDepth)
   int64_t n_tiles;
 };
 
-// Launchers (return the hipError_t of the launch).
-hipError_t launch_fwd_bf16(const Params& p, int head_dim, int heads_per_block, int waves, bool split, bool out_f32,
-                           hipStream_t stream);
+// Which key sets enter the softmax of a forward launch: both (the operator), or
+// one alone (its partial softmax, for measuring and checking the two parts).
+constexpr int kPhaseSeq = 1;
+constexpr int kPhaseDepth = 2;
+constexpr int kPhaseBoth = 3;
+
+// Launchers (return the hipError_t of the launch). The bf16 kernel's instances
+// are split by head dim D and query heads per workgroup GB (moda_fwd_bf16.hip).
+template <int D, int GB>
+hipError_t launch_fwd_bf16_dg(const Params& p, int waves, bool split, int phase, bool out_f32, hipStream_t stream);
 hipError_t launch_fwd_f32(const Params& p, int head_dim, hipStream_t stream);
 
 // Expanded query rows (tokens x grouped heads) per bf16 wave; a workgroup has 1,
@@ -137,5 +145,34 @@ struct DecodeParams {
 int decode_rows_per_chunk_unit(int head_dim);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int heads_per_block, bool bf16, bool out_f32,
                          hipStream_t stream);
+
+// The arguments of one decode step as the C ABI takes them (without workspace).
+struct DecodeArgs {
+  const void *q, *k_cache, *v_cache, *k_depth, *v_depth;
+  void* out;
+  float* lse;
+  int32_t dtype, out_dtype;
+  const int32_t* cache_seqlens;
+  int64_t batch;
+  int32_t max_cache_len, n_heads_q, n_heads_kv, head_dim, depth_capacity, n_depth;
+  float scale;
+};
+// A checked decode step: kernel parameters (all but the workspace) and the
+// workspace it needs.
+struct DecodePlan {
+  DecodeParams p;
+  int head_dim, heads_per_block;
+  bool bf16, out_f32;
+  int64_t workspace_bytes;
+};
+constexpr int kNothingToLaunch = -1;  // decode_prepare: a valid empty problem (batch 0)
+// Host checks of a decode step (no HIP call): MODA_OK with `plan` filled,
+// kNothingToLaunch, or an error status with the per-thread message set.
+int decode_prepare(const DecodeArgs& a, DecodePlan& plan);
+// Launches both decode kernels with `workspace` (plan.workspace_bytes of device
+// memory); MODA_OK or MODA_ERR_HIP.
+int decode_launch(DecodePlan& plan, void* workspace, hipStream_t stream);
+// Sets the per-thread message moda_last_error() returns; returns `code`.
+int set_error(int code, const char* msg);
 
 }  // namespace moda

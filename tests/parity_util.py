@@ -16,6 +16,8 @@ for fp32 inputs and <= 1e-3 for bf16 inputs.
 from __future__ import annotations
 
 import dataclasses
+import json
+import os
 
 import numpy as np
 
@@ -26,6 +28,19 @@ TOL_F32 = 1e-5
 TOL_BF16_REL_RMS = 2e-2
 TOL_LSE_F32 = 1e-5
 TOL_LSE_BF16 = 1e-3
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+# (check, max error, worst error/bound) of every comparison made in this process,
+# printed at the end of the pytest run (tests/conftest.py)
+RESULTS: list = []
+
+
+def stored_rms(name: str) -> float:
+    """RMS of the whole reference output of a sampled workload, written by
+    tests/golden/make_output_rms.py from the oracle alone."""
+    with open(os.path.join(GOLDEN, "output_rms.json")) as f:
+        return float(json.load(f)[name]["rms"])
 
 
 def workload(**kw) -> configs.Workload:
@@ -47,6 +62,7 @@ def run_hip(w: configs.Workload, dev="cuda", batch_index=0, inputs=None, out_f32
     cu = None
     if w.varlen:
         cu = torch.from_numpy(w.cu_seqlens()).to(dev)
+        call_kw.setdefault("max_seqlen", max(w.lengths))
     if out_f32:
         call_kw["out_dtype"] = torch.float32
     out, lse = attn_fwd(x["q"], x["k"], x["v"], x["kd"], x["vd"], n_depth=w.n_depth, causal=w.causal,
@@ -72,11 +88,14 @@ def half_ulp_bf16(x):
     return np.where(x != 0, np.ldexp(1.0, e - 9), 0.0)
 
 
-def tolerance(w, ref, out_bf16=True):
-    """Per-element bound (array) for an output compared with the fp64 reference."""
+def tolerance(w, ref, out_bf16=True, rms=None):
+    """Per-element bound (array) for an output compared with the fp64 reference.
+    ``rms``: the RMS of the whole reference output when ``ref`` holds only some of
+    its rows (default: the RMS of ``ref`` itself)."""
     if not w.bf16:
         return np.full(ref.shape, TOL_F32)
-    rms = float(np.sqrt(np.mean(ref**2))) if ref.size else 1.0
+    if rms is None:
+        rms = float(np.sqrt(np.mean(ref**2))) if ref.size else 1.0
     e = TOL_BF16_REL_RMS * rms
     tol = np.full(ref.shape, e)
     if out_bf16:
@@ -84,7 +103,7 @@ def tolerance(w, ref, out_bf16=True):
     return tol
 
 
-def check_out(w, out, ref, what="", out_bf16=None):
+def check_out(w, out, ref, what="", out_bf16=None, rms=None):
     """Assert the bound elementwise; returns (max error, max error / bound)."""
     if out_bf16 is None:
         out_bf16 = w.bf16
@@ -92,9 +111,10 @@ def check_out(w, out, ref, what="", out_bf16=None):
     if not out.size:
         return 0.0, 0.0
     diff = np.abs(out - ref)
-    tol = tolerance(w, ref, out_bf16)
+    tol = tolerance(w, ref, out_bf16, rms)
     ratio = float(np.max(diff / tol))
     err = float(np.max(diff))
+    RESULTS.append((what or w.name, err, ratio))
     assert ratio <= 1.0, f"{what}: max|out-ref| = {err:.3e}, worst error/bound = {ratio:.3f}"
     return err, ratio
 
@@ -172,6 +192,46 @@ def gpu_row(w, out, lse, s, t, h):
 
 def with_(w, **kw):
     return dataclasses.replace(w, **kw)
+
+
+# --------------------------------------------------------------------------- tile schedules
+
+# Mid-size shapes that reach every tile schedule of the bf16 kernel (the host picks
+# it from the tile count): shared tiles of 4 and 2 waves, one, two or four query
+# heads per workgroup, both head dims, and split tiles (waves dividing one tile's
+# key blocks). Each names the kernel instance it must reach. "whole" cases are
+# small enough for the oracle to compute their whole output in seconds; the
+# others are checked on sampled rows against the RMS of their whole output.
+SCHEDULE_CASES = {
+    "shared4_d64": dict(head_dim=64, batch=4, seqlen=2048, n_heads_q=16, n_heads_kv=16, n_depth=8,
+                        kernel="<64, 1, 4, 1, false, false>"),
+    "shared2_d64": dict(head_dim=64, batch=1, seqlen=2048, n_heads_q=16, n_heads_kv=16, n_depth=8,
+                        kernel="<64, 1, 2, 1, false, false>"),
+    "split_d64_g2": dict(head_dim=64, batch=1, seqlen=1024, n_heads_q=8, n_heads_kv=4, n_depth=11,
+                         kernel="<64, 2, 2, 1, false, true>"),
+    "shared2_d128_g4": dict(head_dim=128, batch=1, seqlen=2048, n_heads_q=16, n_heads_kv=4, n_depth=9,
+                            kernel="<128, 4, 2, 1, false, false>"),
+    "shared4_d128_g2": dict(head_dim=128, batch=2, seqlen=2048, n_heads_q=16, n_heads_kv=8, n_depth=6,
+                            kernel="<128, 2, 4, 1, false, false>"),
+    "split_d128": dict(head_dim=128, batch=1, seqlen=1500, n_heads_q=4, n_heads_kv=4, n_depth=13,
+                       kernel="<128, 1, 2, 1, false, true>"),
+    # whole-output cases
+    "whole_shared2_d64_g4": dict(head_dim=64, batch=1, seqlen=1024, n_heads_q=32, n_heads_kv=8, n_depth=5,
+                                 kernel="<64, 4, 2, 1, false, false>", whole=True),
+    "whole_shared4_d64_g4": dict(head_dim=64, batch=2, seqlen=2048, n_heads_q=32, n_heads_kv=8, n_depth=5,
+                                 kernel="<64, 4, 4, 1, false, false>", whole=True),
+    "whole_shared4_d64_g2": dict(head_dim=64, batch=2, seqlen=2048, n_heads_q=16, n_heads_kv=8, n_depth=7,
+                                 kernel="<64, 2, 4, 1, false, false>", whole=True),
+    "whole_shared2_d128_g4": dict(head_dim=128, batch=1, seqlen=2048, n_heads_q=16, n_heads_kv=4, n_depth=9,
+                                  kernel="<128, 4, 2, 1, false, false>", whole=True),
+    "whole_shared4_d128_g1": dict(head_dim=128, batch=4, seqlen=2048, n_heads_q=8, n_heads_kv=8, n_depth=9,
+                                  kernel="<128, 1, 4, 1, false, false>", whole=True),
+}
+
+
+def schedule_workload(case: str) -> configs.Workload:
+    kw = {k: v for k, v in SCHEDULE_CASES[case].items() if k not in ("kernel", "whole")}
+    return workload(name=case, dtype="bf16", seed=40 + list(SCHEDULE_CASES).index(case), **kw)
 
 
 # --------------------------------------------------------------------------- backward

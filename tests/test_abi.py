@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moda_abi_version() == 4
+    assert L.moda_abi_version() == 5
 
 
 def test_status_codes_match_header():
@@ -138,6 +138,79 @@ def test_varlen_validation_rejects(kw, code):
     assert err()
 
 
+def callp(phase, **kw):
+    a = dict(A)
+    a.update(kw)
+    L = _lib.lib()
+    return L.moda_attn_fwd_phases(a["q"], a["k"], a["v"], a["kd"], a["vd"], a["out"], a["lse"], a["dtype"],
+                                  a["odt"], a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["Scap"], a["S"], a["causal"],
+                                  a["scale"], phase, None)
+
+
+def callvp(phase, cu=P, n_seqs=2, N=16, max_len=8, **kw):
+    a = dict(A)
+    a.update(kw)
+    L = _lib.lib()
+    return L.moda_attn_fwd_varlen_phases(a["q"], a["k"], a["v"], a["kd"], a["vd"], a["out"], a["lse"], a["dtype"],
+                                         a["odt"], cu, n_seqs, N, max_len, a["Hq"], a["Hkv"], a["d"], a["Scap"],
+                                         a["S"], a["causal"], a["scale"], phase, None)
+
+
+@pytest.mark.parametrize("phase", [0, 4, -1, 7])
+def test_phases_reject_unknown_mask(phase):
+    assert callp(phase) == 7 and "phase_mask" in err()
+    assert callvp(phase) == 7 and "phase_mask" in err()
+
+
+def test_depth_phase_needs_slots():
+    assert callp(2, S=0, kd=None, vd=None) == 7 and "n_depth" in err()
+    assert callvp(2, S=0, kd=None, vd=None) == 7 and "n_depth" in err()
+
+
+def test_phases_check_like_the_fused_call():
+    # the same argument checks run first (bad head_dim), and empty problems stay no-ops
+    for phase in (1, 2, 3):
+        assert callp(phase, d=96) == 5
+        assert callvp(phase, d=96) == 5
+        assert callp(phase, B=0) == 0
+        assert callvp(phase, n_seqs=0) == 0
+
+
+def test_packed_call_needs_max_seqlen(monkeypatch):
+    # the binding never copies cu_seqlens back to the host: max_seqlen is required
+    import torch
+
+    class Dev:  # a stand-in with the attributes the binding checks before the library call
+        def __init__(self, shape, dtype=torch.bfloat16):
+            self.shape, self.dtype = torch.Size(shape), dtype
+            self.device = torch.device("cuda", 0)
+
+        def dim(self):
+            return len(self.shape)
+
+        def is_contiguous(self):
+            return True
+
+        def numel(self):
+            n = 1
+            for x in self.shape:
+                n *= x
+            return n
+
+        def element_size(self):
+            return 2
+
+        def data_ptr(self):
+            return P
+
+    q, k = Dev((16, 4, 64)), Dev((16, 2, 64))
+    out, lse = Dev((16, 4, 64)), Dev((4, 16), torch.float32)
+    cu = Dev((3,), torch.int32)
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda *a: type("S", (), {"cuda_stream": 0})())
+    with pytest.raises(ValueError, match="max_seqlen"):
+        _lib.attn_fwd(q, k, k, out=out, lse=lse, cu_seqlens=cu)
+
+
 def test_python_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libmoda_attn.so")
@@ -149,6 +222,8 @@ def test_ctypes_signatures():
     L = _lib.lib()
     assert len(L.moda_attn_fwd.argtypes) == 19
     assert len(L.moda_attn_fwd_varlen.argtypes) == 21
+    assert len(L.moda_attn_fwd_phases.argtypes) == 20
+    assert len(L.moda_attn_fwd_varlen_phases.argtypes) == 22
     assert len(L.moda_attn_decode.argtypes) == 21
     assert len(L.moda_attn_decode_workspace_size.argtypes) == 5
     assert L.moda_attn_decode_workspace_size.restype is ctypes.c_int64

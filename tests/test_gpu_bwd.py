@@ -42,11 +42,12 @@ def _run(w, grad_f32=False, grads=None):
     x = configs.make_device(w, "cuda")
     gdt = torch.float32 if (grad_f32 or not w.bf16) else torch.bfloat16
     cu = torch.from_numpy(w.cu_seqlens()).cuda() if w.varlen else None
+    ml = max(w.lengths) if w.varlen else None
     out, lse = attn_fwd(x["q"], x["k"], x["v"], x["kd"], x["vd"], n_depth=w.n_depth, causal=w.causal, scale=w.scale,
-                        cu_seqlens=cu, out_dtype=gdt)
+                        cu_seqlens=cu, max_seqlen=ml, out_dtype=gdt)
     dout = configs.make_dout_device(w, "cuda", gdt)
     g = attn_bwd(x["q"], x["k"], x["v"], x["kd"], x["vd"], out, dout, lse, n_depth=w.n_depth, causal=w.causal,
-                 scale=w.scale, cu_seqlens=cu, grads=grads)
+                 scale=w.scale, cu_seqlens=cu, max_seqlen=ml, grads=grads)
     torch.cuda.synchronize()
     return g, gdt == torch.bfloat16
 
