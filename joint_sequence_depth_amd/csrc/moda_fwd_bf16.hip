@@ -43,9 +43,10 @@
 // loop on the matrix cores; each wave then merges its two partial states,
 // normalises once and writes.
 //
-// Rounding: QK^T and PV accumulate in fp32; P is rounded to bf16 (RNE) before PV;
+// Rounding: QK^T and PV accumulate in fp32; P enters PV as the sum of two bf16
+// values (its rounding and the rounding of the remainder, 16 significant bits);
 // the output is written in fp32, or rounded to bf16 (RNE) once, after the single
-// normalisation.
+// normalisation by the fp32 sum of the weights.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -447,9 +448,8 @@ moda_fwd_bf16_kernel(const Params p) {
   const bool row_valid = tq < len;
 
   f32x16 acc[DT];
-  // running max (base 2), denominator of the unrounded p (for lse) and of the
-  // weights actually applied to V (for the output); one half of the keys per lane
-  float m_run = NEG_INF, l_run = 0.f, r_run = 0.f;
+  // running max (base 2) and denominator (one half of the keys per lane)
+  float m_run = NEG_INF, l_run = 0.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -464,7 +464,6 @@ moda_fwd_bf16_kernel(const Params p) {
     const float f_dep = fast_exp2(m_d - m_use);
     const float a_d = hh == 0 ? ad[rowb] * f_dep : 0.f;
     l_run = l_run * f_seq + a_d;
-    r_run = r_run * f_seq + a_d;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -661,7 +660,6 @@ moda_fwd_bf16_kernel(const Params p) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - m_new);  // m_run = -inf at first: alpha = 0
       l_run *= alpha;
-      r_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -670,18 +668,21 @@ moda_fwd_bf16_kernel(const Params p) {
     }
     return (m_run == NEG_INF) ? 0.f : m_run;
   };
-  // p = 2^(s c2 - m) rounded to bf16 (packed pairs) for the P.V product, pair q of
-  // the 16 per lane. The output is normalised by the sum of exactly those rounded
-  // values (a bf16 dot with (1, 1)), so the weights on V sum to one and a dominant
-  // key keeps weight 1 whatever the reference max; lse uses the sum of the
-  // unrounded p.
-  auto exp_pair = [&](const f32x16(&s)[2], float m_use, int q, uint32_t(&pp)[2][8], float& lsum, float& rsum) MODA_INL {
+  // p = 2^(s c2 - m) as the sum of two bf16 values for the P.V product, pair q of
+  // the 16 per lane: ph = bf16(p) and pl = bf16(p - ph), so that ph + pl carries 16
+  // significant bits. One bf16 weight alone (8 bits) moves a row that averages few
+  // values by up to ~2^-9 of their spread, more than 2e-2 of the RMS of a whole
+  // long-context output; with the low part the applied weights equal p to ~2^-17
+  // and the output is normalised by the sum of the unrounded p, as lse is.
+  auto exp_pair = [&](const f32x16(&s)[2], float m_use, int q, uint32_t(&ph)[2][8], uint32_t(&pl)[2][8],
+                      float& lsum) MODA_INL {
     const int se = q >> 3, j = q & 7;
     const float p0 = fast_exp2(fmaf(s[se][2 * j], c2, -m_use));
     const float p1 = fast_exp2(fmaf(s[se][2 * j + 1], c2, -m_use));
     lsum += p0 + p1;
-    pp[se][j] = pack_bf16(p0, p1);
-    rsum = dot2(pp[se][j], 0x3F803F80u, rsum);
+    const uint32_t h = pack_bf16(p0, p1);
+    ph[se][j] = h;
+    pl[se][j] = pack_bf16(p0 - lo_bf16(h), p1 - hi_bf16(h));
   };
   // B operand of PV MFMA i: the packed probabilities of key tile st, half part.
   auto pfrag = [](const uint32_t(&pp)[2][8], int i) MODA_INL {
@@ -724,8 +725,8 @@ moda_fwd_bf16_kernel(const Params p) {
     const float m_use = max_and_rescale(scur);
     const unsigned char* ks = kst + stage_of(i + 1) * SM::STAGE;
     const unsigned char* vs = vst + stage_of(i) * SM::STAGE;
-    uint32_t pp[2][8];
-    float lsum = 0.f, rsum = 0.f;
+    uint32_t ph[2][8], pl[2][8];
+    float lsum = 0.f;
     bf16x8 a0 = kread(ks, 0), a1 = kread(ks, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -742,20 +743,20 @@ moda_fwd_bf16_kernel(const Params p) {
         snext[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kc], snext[st], 0, 0, 0);
       }
 #pragma unroll
-      for (int q = i * 16 / NQK; q < (i + 1) * 16 / NQK; ++q) exp_pair(scur, m_use, q, pp, lsum, rsum);
+      for (int q = i * 16 / NQK; q < (i + 1) * 16 / NQK; ++q) exp_pair(scur, m_use, q, ph, pl, lsum);
       __builtin_amdgcn_sched_barrier(0);
       a0 = a1;
       a1 = a2;
     }
     l_run += lsum;
-    r_run += rsum;
     bf16x8 b0 = vread(vs, 0), b1 = vread(vs, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       bf16x8 b2 = b1;
       if (i + 2 < NPV) b2 = vread(vs, i + 2);
-      acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, pfrag(pp, i), acc[i % DT], 0, 0, 0);
+      acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, pfrag(ph, i), acc[i % DT], 0, 0, 0);
+      acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, pfrag(pl, i), acc[i % DT], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       b0 = b1;
       b1 = b2;
@@ -775,16 +776,18 @@ moda_fwd_bf16_kernel(const Params p) {
     if (active(kb)) {
       mask_block(kb, scur);
       const float m_use = max_and_rescale(scur);
-      uint32_t pp[2][8];
-      float lsum = 0.f, rsum = 0.f;
+      uint32_t ph[2][8], pl[2][8];
+      float lsum = 0.f;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) exp_pair(scur, m_use, q, pp, lsum, rsum);
+      for (int q = 0; q < 16; ++q) exp_pair(scur, m_use, q, ph, pl, lsum);
       l_run += lsum;
-      r_run += rsum;
       const unsigned char* vs = vst + stage_of(i) * SM::STAGE;
 #pragma unroll
-      for (int j = 0; j < NPV; ++j)
-        acc[j % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vs, j), pfrag(pp, j), acc[j % DT], 0, 0, 0);
+      for (int j = 0; j < NPV; ++j) {
+        const bf16x8 b = vread(vs, j);
+        acc[j % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, pfrag(ph, j), acc[j % DT], 0, 0, 0);
+        acc[j % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, pfrag(pl, j), acc[j % DT], 0, 0, 0);
+      }
     }
     block_end();
   };
@@ -831,7 +834,7 @@ moda_fwd_bf16_kernel(const Params p) {
         for (int q4 = 0; q4 < 4; ++q4)
           *reinterpret_cast<float4*>(rec + 16 * dt + 4 * q4) =
               make_float4(acc[dt][4 * q4], acc[dt][4 * q4 + 1], acc[dt][4 * q4 + 2], acc[dt][4 * q4 + 3]);
-      *reinterpret_cast<float4*>(rec + 16 * DT) = make_float4(m_run, l_run, r_run, 0.f);
+      *reinterpret_cast<float4*>(rec + 16 * DT) = make_float4(m_run, l_run, 0.f, 0.f);
     }
     __syncthreads();
     if (wave > 0) return;
@@ -843,7 +846,6 @@ moda_fwd_bf16_kernel(const Params p) {
       const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
       const float f_a = fast_exp2(m_run - m_use), f_b = fast_exp2(st.x - m_use);
       l_run = l_run * f_a + st.y * f_b;
-      r_run = r_run * f_a + st.z * f_b;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -867,9 +869,8 @@ moda_fwd_bf16_kernel(const Params p) {
 
   // ---- normalise once and write ------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float r_tot = r_run + __shfl_xor(r_run, 32);
   if (row_valid) {
-    const float inv = r_tot > 0.f ? 1.f / r_tot : 0.f;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t obase = ((seg_start + tq) * Hq + hq) * (int64_t)D + 4 * hh;
     if constexpr (OUT_F32) {
       float* orow = static_cast<float*>(p.out) + obase;
