@@ -156,6 +156,27 @@ int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, co
                      int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t n_depth, float scale,
                      void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * moda_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The same two kernels pass their partial
+ * states through a device array the library holds: MODA_DECODE_SCRATCH_BYTES per
+ * GPU, set up on the first call on that GPU (the current device; `stream`, if
+ * not NULL, must belong to it) and kept until the process ends. The call
+ * allocates nothing. Steps whose moda_attn_decode_workspace_size exceeds
+ * MODA_DECODE_SCRATCH_BYTES are rejected with MODA_ERR_SHAPE (use
+ * moda_attn_decode with a workspace). All calls on one GPU share the array:
+ * calls that overlap on one GPU (other streams, other threads) race; calls in
+ * order on one stream do not. Arguments, checks, results and errors otherwise
+ * as for moda_attn_decode.
+ */
+#define MODA_DECODE_SCRATCH_BYTES (16ll << 20)
+int moda_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const void* k_depth,
+                             const void* v_depth, void* out, float* lse, int32_t dtype, int32_t out_dtype,
+                             const int32_t* cache_seqlens, int64_t batch, int32_t max_cache_len, int32_t n_heads_q,
+                             int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t n_depth,
+                             float scale, void* stream);
+
 /* Workspace bytes moda_attn_decode needs for these sizes, or -1 for invalid sizes. */
 int64_t moda_attn_decode_workspace_size(int64_t batch, int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
                                         int32_t max_cache_len);

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     ModaError,
     attn_bwd,
     attn_decode,
+    attn_decode_noalloc,
     attn_fwd,
     bwd_workspace_size,
     decode_workspace_size,
@@ -16,5 +17,5 @@ from ._lib import (  # noqa: F401
     lib,
 )
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "depth_kv_write", "bwd_workspace_size", "decode_workspace_size",
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_decode_noalloc", "depth_kv_write", "bwd_workspace_size", "decode_workspace_size",
            "lib", "ModaError", "EXPORTS"]

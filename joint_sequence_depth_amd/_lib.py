@@ -30,7 +30,7 @@ STATUS_NAMES = {
 
 # every symbol include/moda_attn.h declares
 EXPORTS = ("moda_attn_fwd", "moda_attn_fwd_varlen", "moda_attn_fwd_phases", "moda_attn_fwd_varlen_phases",
-           "moda_attn_decode", "moda_attn_decode_workspace_size",
+           "moda_attn_decode", "moda_attn_decode_noalloc", "moda_attn_decode_workspace_size",
            "moda_attn_bwd", "moda_attn_bwd_varlen", "moda_attn_bwd_workspace_size", "moda_depth_kv_write",
            "moda_last_error", "moda_abi_version")
 
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.moda_attn_fwd_varlen_phases.restype = ctypes.c_int
         L.moda_attn_decode.argtypes = [vp] * 7 + [i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp, i64, vp]
         L.moda_attn_decode.restype = ctypes.c_int
+        L.moda_attn_decode_noalloc.argtypes = [vp] * 7 + [i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp]
+        L.moda_attn_decode_noalloc.restype = ctypes.c_int
         L.moda_attn_decode_workspace_size.argtypes = [i64, i32, i32, i32, i32]
         L.moda_attn_decode_workspace_size.restype = ctypes.c_int64
         L.moda_attn_bwd.argtypes = [vp] * 13 + [i32, i32, i64, i64, i32, i32, i32, i32, i32, i32, f32, vp, i64, vp]
@@ -309,6 +311,54 @@ def attn_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_depth), _ptr(v_depth), _ptr(out), _ptr(lse),
         _dtype_code(q), _dtype_code(out), _ptr(cache_seqlens), B, T_max, Hq, Hkv, d, s_cap, int(n_depth),
         float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(), stream,
+    )
+    _check(status)
+    return out, lse
+
+
+DECODE_SCRATCH_BYTES = 16 << 20  # MODA_DECODE_SCRATCH_BYTES
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, cache_seqlens, out, k_depth=None, v_depth=None,
+                        n_depth: Optional[int] = None, scale: Optional[float] = None, lse=None, stream=None):
+    """One decode step through ``moda_attn_decode_noalloc``: as ``attn_decode``, but
+    the partial states go through the library's own per-GPU scratch array, so
+    neither the library nor this binding allocates anything: ``out`` (and ``lse``,
+    if wanted; None = not written) are the caller's. Steps needing more than
+    DECODE_SCRATCH_BYTES of scratch are rejected. Calls that overlap on one GPU
+    share the scratch and race. Returns (out, lse)."""
+    import torch
+
+    for t in (q, k_cache, v_cache, cache_seqlens, k_depth, v_depth, out, lse):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if t is not None and t.device.type != "cuda":
+            raise ValueError("all tensors must be on the GPU")
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B,Hq,d] and the caches [B,T_max,Hkv,d]")
+    B, Hq, d = q.shape
+    T_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != d or out.shape != q.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} cache{tuple(k_cache.shape)} out{tuple(out.shape)}")
+    if cache_seqlens.dtype != torch.int32 or tuple(cache_seqlens.shape) != (B,):
+        raise ValueError("cache_seqlens must be int32 [B] on the device")
+    if lse is not None and (tuple(lse.shape) != (B, Hq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, Hq]")
+    s_cap = 0
+    if k_depth is not None:
+        if v_depth is None or k_depth.shape != v_depth.shape or k_depth.dim() != 4:
+            raise ValueError("k_depth and v_depth must both be [B,S_cap,Hkv,d]")
+        s_cap = k_depth.shape[1]
+    if n_depth is None:
+        n_depth = s_cap
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    status = lib().moda_attn_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_depth), _ptr(v_depth), _ptr(out), _ptr(lse),
+        _dtype_code(q), _dtype_code(out), _ptr(cache_seqlens), B, T_max, Hq, Hkv, d, s_cap, int(n_depth),
+        float(scale), stream,
     )
     _check(status)
     return out, lse

@@ -225,6 +225,7 @@ def test_ctypes_signatures():
     assert len(L.moda_attn_fwd_phases.argtypes) == 20
     assert len(L.moda_attn_fwd_varlen_phases.argtypes) == 22
     assert len(L.moda_attn_decode.argtypes) == 21
+    assert len(L.moda_attn_decode_noalloc.argtypes) == 19
     assert len(L.moda_attn_decode_workspace_size.argtypes) == 5
     assert L.moda_attn_decode_workspace_size.restype is ctypes.c_int64
     assert len(L.moda_attn_bwd.argtypes) == 27
@@ -266,6 +267,21 @@ def calld(seqlens=P, Tmax=32, ws=P, ws_bytes=1 << 30, **kw):
 def test_decode_validation_rejects(kw, code):
     assert calld(**kw) == code
     assert err()
+
+
+def test_decode_noalloc_rejects_steps_beyond_its_scratch():
+    # B = 256, Hq = Hkv = 64, d = 128: two chunks of 132 floats per (sequence, head)
+    # need 17.3 MB > MODA_DECODE_SCRATCH_BYTES; rejected on the host, before any
+    # HIP call (without a GPU a HIP call would report MODA_ERR_HIP instead)
+    L = _lib.lib()
+    B, Hq, Hkv, d, T = 256, 64, 64, 128, 16
+    assert L.moda_attn_decode_workspace_size(B, Hq, Hkv, d, T) > _lib.DECODE_SCRATCH_BYTES
+    rc = L.moda_attn_decode_noalloc(P, P, P, None, None, P, None, 1, 1, P, B, T, Hq, Hkv, d, 0, 0, 0.088, None)
+    assert rc == 2 and "scratch" in err()
+    # the same argument checks as moda_attn_decode run first
+    assert L.moda_attn_decode_noalloc(None, P, P, None, None, P, None, 1, 1, P, 1, T, 2, 2, 64, 0, 0, 0.1, None) == 1
+    assert L.moda_attn_decode_noalloc(P, P, P, None, None, P, None, 1, 1, P, 1, T, 2, 2, 96, 0, 0, 0.1, None) == 5
+    assert L.moda_attn_decode_noalloc(P, P, P, None, None, P, None, 1, 1, P, 0, T, 2, 2, 64, 0, 0, 0.1, None) == 0
 
 
 def test_decode_empty_batch_is_ok_without_launch():
