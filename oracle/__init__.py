@@ -12,6 +12,7 @@ from .moda_oracle import (  # noqa: F401
     joint_attention_backward,
     joint_rows,
     scalar_ref,
+    select_slots,
     separate_then_add,
     sequence_only,
     sequence_visible,

@@ -77,6 +77,8 @@ def joint_attention(
     cu_seqlens=None,
     row_block: int = 256,
     mode: str = "joint",
+    depth_topk: Optional[int] = None,
+    depth_recent: int = 0,
 ):
     """MoDA forward in float64. Returns (out, lse).
 
@@ -88,6 +90,16 @@ def joint_attention(
     ``mode`` selects which keys enter the single softmax: "joint" (the operator),
     "sequence" (depth slots dropped) or "depth" (sequence keys dropped). The last
     two are the partial softmaxes used by the merge identity in the tests.
+
+    ``depth_topk`` (None = every slot): a bounded read of the depth history, the
+    top-S / sliding-window / hybrid buffer that the MoDA deck lists as future work
+    (slide "The main open cost is retaining and reading depth history", paper Sec.
+    6.1-6.2), which the pages name but do not define. Reading taken: of a row's
+    slots [0, n_depth), the last ``depth_recent`` always enter; of the others, the
+    ``depth_topk`` with the largest depth logits b_i enter, ties going to the lower
+    slot index; the remaining slots leave the softmax (as if absent). topk = 0 with
+    recent = w is a sliding window of the w most recent slots; recent = 0 is pure
+    top-S; both > 0 is the hybrid.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     kd, vd = _f64(k_depth), _f64(v_depth)
@@ -132,9 +144,11 @@ def joint_attention(
                     parts_val.append(("seq", kend))
                 if use_depth:
                     b = scale * np.einsum("rc,rsc->rs", Q[r0:r1], Kd[r0:r1])  # [R, S]
+                    if depth_topk is not None:
+                        b = np.where(select_slots(b, depth_topk, depth_recent), b, -np.inf)
                     parts_logit.append(b)
                     parts_val.append(("depth", None))
-                M = np.max(np.concatenate(parts_logit, axis=1), axis=1)  # finite: j = t is visible
+                M = np.max(np.concatenate(parts_logit, axis=1), axis=1)  # finite when j = t is visible
                 num = np.zeros((r1 - r0, d))
                 Z = np.zeros(r1 - r0)
                 for lg, (kind, kend) in zip(parts_logit, parts_val):
@@ -151,6 +165,23 @@ def joint_attention(
         out = out.reshape(B, T, Hq, d)
         lse = lse.reshape(Hq, B, T).transpose(1, 0, 2).copy()
     return out, lse
+
+
+def select_slots(b, topk: int, recent: int = 0):
+    """Boolean [R, S] mask of the depth slots that enter each row's softmax (see
+    ``joint_attention``): the last ``recent`` slots, plus the ``topk`` largest
+    logits among the others, ties to the lower slot index (a stable sort of -b)."""
+    b = np.asarray(b, dtype=np.float64)
+    R, S = b.shape
+    recent = max(0, min(recent, S))
+    n_old = S - recent
+    keep = np.zeros((R, S), dtype=bool)
+    keep[:, n_old:] = True
+    k = max(0, min(topk, n_old))
+    if k > 0:
+        order = np.argsort(-b[:, :n_old], axis=1, kind="stable")  # descending logit, lower index first
+        np.put_along_axis(keep[:, :n_old], order[:, :k], True, axis=1)
+    return keep
 
 
 def joint_rows(q_row, k_seq, v_seq, kd_row, vd_row, scale: float):
@@ -179,11 +210,12 @@ def separate_then_add(q, k, v, k_depth, v_depth, n_depth, causal=True, scale=Non
     return o_s + o_d
 
 
-def scalar_ref(q, k, v, k_depth, v_depth, n_depth, causal=True, scale=None):
+def scalar_ref(q, k, v, k_depth, v_depth, n_depth, causal=True, scale=None, depth_topk=None, depth_recent=0):
     """Pure-Python brute force of the joint equation (batch layout, tiny shapes only).
 
     math.exp and math.fsum over explicit loops; no numpy reductions. Used to check
-    the vectorised oracle above.
+    the vectorised oracle above. With ``depth_topk`` the slots are chosen by
+    sorting (logit descending, slot index ascending) in plain Python.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     kd, vd = _f64(k_depth), _f64(v_depth)
@@ -205,8 +237,14 @@ def scalar_ref(q, k, v, k_depth, v_depth, n_depth, causal=True, scale=None):
                         continue
                     logits.append(scale * math.fsum(qt[c] * float(k[b, j, hk, c]) for c in range(d)))
                     values.append([float(x) for x in v[b, j, hk]])
-                for i in range(n_depth):
-                    logits.append(scale * math.fsum(qt[c] * float(kd[b, t, i, hk, c]) for c in range(d)))
+                dl = [scale * math.fsum(qt[c] * float(kd[b, t, i, hk, c]) for c in range(d)) for i in range(n_depth)]
+                chosen = range(n_depth)
+                if depth_topk is not None:
+                    old = n_depth - min(depth_recent, n_depth)
+                    ranked = sorted(range(old), key=lambda i: (-dl[i], i))
+                    chosen = sorted(ranked[: max(0, depth_topk)] + list(range(old, n_depth)))
+                for i in chosen:
+                    logits.append(dl[i])
                     values.append([float(x) for x in vd[b, t, i, hk]])
                 M = max(logits)
                 w = [math.exp(x - M) for x in logits]

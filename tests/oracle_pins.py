@@ -486,6 +486,65 @@ def pin_joint_rows(orc):
     assert np.max(np.abs(o - vdr[0])) < 1e-12 and abs(lse - 1e4) < 1e-9
 
 
+# p24 ----------------------------------------------------------------------------
+def _ln(x):
+    return math.log(float(x.split()[1])) if isinstance(x, str) else float(x)
+
+
+def pin_topk_hand_examples(orc):
+    """Bounded slot reads (top-S, sliding window, hybrid) worked by hand, including
+    the tie rule (tests/golden/topk_example.json)."""
+    with open(os.path.join(GOLDEN, "topk_example.json")) as f:
+        g = json.load(f)
+    one = lambda x: np.array(x, dtype=np.float64).reshape(1, 1, 1, 1)  # noqa: E731
+    for c in g["cases"]:
+        kd = np.array([_ln(x) for x in c["k_depth"]]).reshape(1, 1, 3, 1, 1)
+        vd = np.array(c["v_depth"]).reshape(1, 1, 3, 1, 1)
+        o, lse = orc.joint_attention(one(g["q"]), one(g["k"]), one(g["v"]), kd, vd, 3, True, g["scale"],
+                                     depth_topk=c["topk"], depth_recent=c["recent"])
+        assert abs(o.item() - c["out"]) < 1e-12, c
+        assert abs(lse.item() - _ln(c["lse"])) < 1e-12, c
+        keep = orc.select_slots(np.array([[_ln(x) for x in c["k_depth"]]]), c["topk"], c["recent"])
+        assert list(np.flatnonzero(keep[0])) == c["chosen"], c
+
+
+# p25 ----------------------------------------------------------------------------
+def pin_topk_limits(orc):
+    """topk covering every slot is the joint operator (bitwise); no slot at all is
+    ordinary causal attention (SDPA); topk = 0 with recent = w equals the operator
+    over the window of the last w slots."""
+    q, k, v, kd, vd = rand_case(24, B=2, T=9, Hq=4, Hkv=2, d=6, S=5)
+    o, lse = orc.joint_attention(q, k, v, kd, vd, 5, True, 0.5)
+    for topk, recent in [(5, 0), (9, 0), (0, 5), (3, 2), (2, 7)]:
+        o2, lse2 = orc.joint_attention(q, k, v, kd, vd, 5, True, 0.5, depth_topk=topk, depth_recent=recent)
+        assert np.array_equal(o, o2) and np.array_equal(lse, lse2), (topk, recent)
+    o0, _ = orc.joint_attention(q, k, v, kd, vd, 5, True, 0.5, depth_topk=0)
+    assert np.max(np.abs(o0 - _sdpa(q, k, v, True, 0.5))) < 1e-12
+    ow, lw = orc.joint_attention(q, k, v, kd, vd, 5, True, 0.5, depth_topk=0, depth_recent=2)
+    ow2, lw2 = orc.joint_attention(q, k, v, kd[:, :, 3:5], vd[:, :, 3:5], 2, True, 0.5)
+    assert np.max(np.abs(ow - ow2)) < 1e-13 and np.max(np.abs(lw - lw2)) < 1e-13
+
+
+# p26 ----------------------------------------------------------------------------
+def pin_topk_brute_force(orc):
+    """Pure-Python selection (sort by logit, then index) and fsum agree with the
+    vectorised oracle on random tiny shapes, grouped heads, causal or not."""
+    rng = np.random.default_rng(26)
+    for it in range(8):
+        T = int(rng.integers(1, 7))
+        G = int(rng.integers(1, 3))
+        Hkv = int(rng.integers(1, 3))
+        d = int(rng.integers(1, 6))
+        S = int(rng.integers(3, 7))
+        recent = int(rng.integers(0, S - 1))  # at least two older slots
+        topk = int(rng.integers(1, S - recent))  # a proper subset of them
+        causal = bool(it % 2 == 0)
+        q, k, v, kd, vd = rand_case(200 + it, B=1, T=T, Hq=G * Hkv, Hkv=Hkv, d=d, S=S, Scap=S + 1)
+        o, lse = orc.joint_attention(q, k, v, kd, vd, S, causal, 0.7, depth_topk=topk, depth_recent=recent)
+        o2, lse2 = orc.scalar_ref(q, k, v, kd, vd, S, causal, 0.7, depth_topk=topk, depth_recent=recent)
+        assert np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(lse - lse2)) < 1e-12, (it, topk, recent)
+
+
 ALL_PINS = [
     pin_empty_depth_is_sdpa,
     pin_equal_logits_plain_mean,
@@ -510,4 +569,7 @@ ALL_PINS = [
     pin_backward_sums,
     pin_backward_empty_depth_is_sdpa_autograd,
     pin_joint_rows,
+    pin_topk_hand_examples,
+    pin_topk_limits,
+    pin_topk_brute_force,
 ]

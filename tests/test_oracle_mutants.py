@@ -51,6 +51,14 @@ MUTANTS = {
     "rows_depth_out_of_denominator": ("Z = w.sum() + u.sum()", "Z = w.sum()"),
     "rows_lse_base_two": ("return o, M + math.log(Z)", "return o, M + math.log2(Z)"),
     "rows_depth_keys_as_values": ("u @ vd_row", "u @ kd_row"),
+    "topk_ties_to_higher_index": ('order = np.argsort(-b[:, :n_old], axis=1, kind="stable")',
+                                  'order = np.argsort(b[:, :n_old], axis=1, kind="stable")[:, ::-1]'),
+    "topk_smallest_logits": ('order = np.argsort(-b[:, :n_old], axis=1, kind="stable")',
+                             'order = np.argsort(b[:, :n_old], axis=1, kind="stable")'),
+    "topk_by_magnitude": ('order = np.argsort(-b[:, :n_old], axis=1, kind="stable")',
+                          'order = np.argsort(-np.abs(b[:, :n_old]), axis=1, kind="stable")'),
+    "topk_recent_off_by_one": ("keep[:, n_old:] = True", "keep[:, n_old + 1 :] = True"),
+    "topk_one_too_many": ("k = max(0, min(topk, n_old))", "k = max(0, min(topk + 1, n_old))"),
 }
 
 
