@@ -755,6 +755,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
     ap.add_argument("--no-parts", action="store_true", help="skip the sequence-only and depth-only timings")
+    ap.add_argument("--depth-topk", type=int, default=None,
+                    help="time the bounded depth reads: each row keeps this many top-logit slots")
+    ap.add_argument("--depth-recent", type=int, default=0, help="... plus this many most recent slots")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "LOG"),
@@ -826,12 +829,19 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
+    sel = {}
+    if args.depth_topk is not None:  # bounded depth reads: slot masks in a preallocated workspace
+        from joint_sequence_depth_amd import topk_workspace_size
+
+        sel = dict(depth_topk=args.depth_topk, depth_recent=args.depth_recent,
+                   workspace=torch.empty(topk_workspace_size(w.n_tokens, w.n_heads_q), dtype=torch.uint8, device=dev))
+
     def make_step(phase):
         def step(i):
             x = inputs[i % n_batches]
             attn_fwd(x["q"], x["k"], x["v"], x["kd"], x["vd"], n_depth=w.n_depth, causal=w.causal, scale=w.scale,
                      cu_seqlens=cu, max_seqlen=max_len, out=outs[i % n_batches], lse=lses[i % n_batches],
-                     phase=phase)
+                     phase=phase, **sel)
         return step
 
     step = make_step(3)
@@ -843,7 +853,7 @@ def main(argv=None) -> int:
     ref_lse = torch.empty_like(lses[0])
     x0 = inputs[0]
     attn_fwd(x0["q"], x0["k"], x0["v"], x0["kd"], x0["vd"], n_depth=w.n_depth, causal=w.causal, scale=w.scale,
-             cu_seqlens=cu, max_seqlen=max_len, out=ref_out, lse=ref_lse)
+             cu_seqlens=cu, max_seqlen=max_len, out=ref_out, lse=ref_lse, **sel)
     torch.cuda.synchronize()
     replay_ok = bool(torch.equal(ref_out, outs[0]) and torch.equal(ref_lse, lses[0]))
     if not replay_ok:
@@ -851,7 +861,7 @@ def main(argv=None) -> int:
 
     # the two parts alone, from the same kernel code (the other part compiled out)
     part_ms = {}
-    if w.bf16 and w.n_depth > 0 and not args.no_parts:
+    if w.bf16 and w.n_depth > 0 and not args.no_parts and not sel:
         for phase in (1, 2):
             part_ms[phase], _, _ = time_steps(make_step(phase), n_batches, args, dev, stream)
             print(f"# phase {phase}: {part_ms[phase]:.4f} ms per launch", file=sys.stderr, flush=True)
@@ -859,6 +869,11 @@ def main(argv=None) -> int:
     flops = w.seq_flops() + w.depth_flops()
     tflops = flops / sec / 1e12
     peak_f = PEAK_BF16_TFLOPS if w.bf16 else PEAK_F32_TFLOPS
+    if sel:
+        # bounded reads: every slot key is scored, only the kept slots' values are weighted
+        kept = min(w.n_depth, args.depth_topk + args.depth_recent)
+        flops = w.seq_flops() + 2.0 * w.n_tokens * w.n_heads_q * w.head_dim * (w.n_depth + kept)
+        tflops = flops / sec / 1e12
     parts = {
         "fused": {
             "ms": round(ms, 5),
@@ -889,6 +904,17 @@ def main(argv=None) -> int:
         # depth bytes over the time the fused launch spends beyond the sequence part alone
         extra = sec - s1
         parts["depth_kv_gbs_beside_sequence"] = round(w.depth_bytes() / extra / 1e9, 1) if extra > 0 else None
+    if sel:
+        kept = min(w.n_depth, args.depth_topk + args.depth_recent)
+        alg = w.n_tokens * w.n_heads_kv * w.head_dim * w.elem_bytes() * (w.n_depth + kept) + w.other_bytes()
+        alg += 16.0 * w.n_tokens * w.n_heads_q  # slot masks written and read
+        parts["bounded_depth_reads"] = {
+            "depth_topk": args.depth_topk, "depth_recent": args.depth_recent, "kept_slots": kept,
+            "algorithmic_bytes": alg, "gbs": round(alg / sec / 1e9, 1),
+            "hbm_frac_of_peak": round(alg / sec / 1e9 / PEAK_HBM_GBS, 4),
+            "note": "keys of every slot are read to score them; values only of the kept slots count as algorithmic "
+                    "bytes (the kernel reads all of them)",
+        }
     rec = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -914,12 +940,16 @@ def main(argv=None) -> int:
             "causal": w.causal,
             "input_batches": n_batches,
             "graph": use_graph,
+            "depth_topk": args.depth_topk,
+            "depth_recent": args.depth_recent if sel else None,
         },
         "parts": parts,
         "kernel": kernel_name(w),
         "kernel_source_sha": kernel_source_sha(),
         "replay_matches_eager": replay_ok,
-        "roofline": roofline(w, sec),
+        "roofline": roofline(w, sec) if not sel else {
+            "bound": "hbm", "achieved": parts["bounded_depth_reads"]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": parts["bounded_depth_reads"]["hbm_frac_of_peak"], "traffic": None},
         "cpu_baseline": None,
     }
     del inputs, outs, lses

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MODA_ABI_VERSION 5
+#define MODA_ABI_VERSION 6
 
 /* status codes */
 #define MODA_OK 0
@@ -123,6 +123,45 @@ int moda_attn_fwd_varlen_phases(const void* q, const void* k, const void* v, con
                                 const int32_t* cu_seqlens, int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen,
                                 int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
                                 int32_t n_depth, int32_t causal, float scale, int32_t phase_mask, void* stream);
+
+/*
+ * Bounded depth reads (top-S, sliding window or hybrid slot buffer): the operator
+ * of moda_attn_fwd / moda_attn_fwd_varlen in which each query row (token t, head
+ * h) reads only some of its depth slots. The MoDA deck lists such a bounded
+ * S << L slot buffer as future work (slide "The main open cost is retaining and
+ * reading depth history", paper Sec. 6.1-6.2) without defining it; the reading
+ * taken here: of slots [0, n_depth), the last depth_recent always enter the joint
+ * softmax; of the others, the depth_topk with the largest depth logits
+ * b_i = scale <q_t, k_depth_{t,i}> enter, ties going to the lower slot index; the
+ * other slots leave the softmax as if absent. depth_recent = 0 is top-S,
+ * depth_topk = 0 a sliding window of the depth_recent most recent slots, both > 0
+ * the hybrid. When depth_topk covers every older slot the call is the operator.
+ *
+ * A selection kernel scores every slot and writes a 64-bit slot mask per row to
+ * `workspace` (DEVICE memory of at least moda_attn_fwd_topk_workspace_size(N, Hq)
+ * bytes, 16-byte aligned, caller-owned, contents on entry irrelevant; calls that
+ * share one workspace must not overlap); the forward then reads the kept slots.
+ * Both kernels run on `stream`. The logits that decide the selection are fp32:
+ * slots whose logits tie within fp32 rounding may be chosen either way.
+ * n_depth <= 64 (MODA_ERR_UNSUPPORTED otherwise); depth_topk, depth_recent >= 0
+ * (MODA_ERR_VALUE). Other arguments, checks and errors as for moda_attn_fwd /
+ * moda_attn_fwd_varlen; MODA_ERR_SHAPE also for a too small workspace.
+ */
+int moda_attn_fwd_topk(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
+                       void* out, float* lse, int32_t dtype, int32_t out_dtype, int64_t batch, int64_t seqlen,
+                       int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
+                       int32_t n_depth, int32_t depth_topk, int32_t depth_recent, int32_t causal, float scale,
+                       void* workspace, int64_t workspace_bytes, void* stream);
+int moda_attn_fwd_varlen_topk(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
+                              void* out, float* lse, int32_t dtype, int32_t out_dtype, const int32_t* cu_seqlens,
+                              int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen, int32_t n_heads_q,
+                              int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t n_depth,
+                              int32_t depth_topk, int32_t depth_recent, int32_t causal, float scale, void* workspace,
+                              int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes of the bounded depth reads for N = total tokens (B * T), or -1
+ * for invalid sizes. */
+int64_t moda_attn_fwd_topk_workspace_size(int64_t total_tokens, int32_t n_heads_q);
 
 /*
  * One decode step: a single new token per sequence attends, through the same

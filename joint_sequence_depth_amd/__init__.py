@@ -15,7 +15,8 @@ from ._lib import (  # noqa: F401
     decode_workspace_size,
     depth_kv_write,
     lib,
+    topk_workspace_size,
 )
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_decode_noalloc", "depth_kv_write", "bwd_workspace_size", "decode_workspace_size",
-           "lib", "ModaError", "EXPORTS"]
+           "topk_workspace_size", "lib", "ModaError", "EXPORTS"]

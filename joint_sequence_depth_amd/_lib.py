@@ -30,6 +30,7 @@ STATUS_NAMES = {
 
 # every symbol include/moda_attn.h declares
 EXPORTS = ("moda_attn_fwd", "moda_attn_fwd_varlen", "moda_attn_fwd_phases", "moda_attn_fwd_varlen_phases",
+           "moda_attn_fwd_topk", "moda_attn_fwd_varlen_topk", "moda_attn_fwd_topk_workspace_size",
            "moda_attn_decode", "moda_attn_decode_noalloc", "moda_attn_decode_workspace_size",
            "moda_attn_bwd", "moda_attn_bwd_varlen", "moda_attn_bwd_workspace_size", "moda_depth_kv_write",
            "moda_last_error", "moda_abi_version")
@@ -62,6 +63,14 @@ def lib() -> ctypes.CDLL:
         L.moda_attn_fwd_phases.restype = ctypes.c_int
         L.moda_attn_fwd_varlen_phases.argtypes = L.moda_attn_fwd_varlen.argtypes[:-1] + [i32, vp]
         L.moda_attn_fwd_varlen_phases.restype = ctypes.c_int
+        L.moda_attn_fwd_topk.argtypes = L.moda_attn_fwd.argtypes[:16] + [i32, i32] + L.moda_attn_fwd.argtypes[16:18] + [
+            vp, i64, vp]
+        L.moda_attn_fwd_topk.restype = ctypes.c_int
+        L.moda_attn_fwd_varlen_topk.argtypes = L.moda_attn_fwd_varlen.argtypes[:18] + [i32, i32] + \
+            L.moda_attn_fwd_varlen.argtypes[18:20] + [vp, i64, vp]
+        L.moda_attn_fwd_varlen_topk.restype = ctypes.c_int
+        L.moda_attn_fwd_topk_workspace_size.argtypes = [i64, i32]
+        L.moda_attn_fwd_topk_workspace_size.restype = ctypes.c_int64
         L.moda_attn_decode.argtypes = [vp] * 7 + [i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp, i64, vp]
         L.moda_attn_decode.restype = ctypes.c_int
         L.moda_attn_decode_noalloc.argtypes = [vp] * 7 + [i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp]
@@ -134,6 +143,9 @@ def attn_fwd(
     return_lse: bool = True,
     slot_offset: int = 0,
     phase: int = 3,
+    depth_topk: Optional[int] = None,
+    depth_recent: int = 0,
+    workspace=None,
 ):
     """MoDA joint sequence/depth attention forward through the C ABI.
 
@@ -150,6 +162,11 @@ def attn_fwd(
     own softmax, for measurement and for the merge check); 3, the default, is the
     operator. Packed calls need ``max_seqlen`` (the longest sequence): the binding
     never reads ``cu_seqlens`` back from the device.
+    ``depth_topk`` (with ``depth_recent``) makes each row read only some of its
+    depth slots: the last ``depth_recent`` and the ``depth_topk`` others with the
+    largest depth logits (top-S, sliding window or hybrid buffer; n_depth <= 64).
+    ``workspace`` (uint8 device tensor of ``topk_workspace_size`` bytes) holds the
+    per-row slot masks; allocated here when not given.
     """
     import torch
 
@@ -206,6 +223,16 @@ def attn_fwd(
     code = _dtype_code(q)
     out_code = _dtype_code(out)
     L = lib()
+    if depth_topk is not None:
+        if phase != 3:
+            raise ValueError("bounded depth reads run the whole operator (phase 3)")
+        n_tok = q.shape[0] if varlen else q.shape[0] * q.shape[1]
+        if workspace is None:
+            workspace = torch.empty(max(topk_workspace_size(n_tok, Hq), 16), dtype=torch.uint8, device=q.device)
+        elif not workspace.is_contiguous() or workspace.device.type != "cuda":
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        sel = (int(depth_topk), int(depth_recent))
+        ws = (_ptr(workspace), workspace.numel() * workspace.element_size())
     if varlen:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
             raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
@@ -214,19 +241,31 @@ def attn_fwd(
             raise ValueError("packed calls need max_seqlen (the longest sequence); cu_seqlens stays on the device")
         args = (_ptr(q), _ptr(k), _ptr(v), kd_ptr, vd_ptr, _ptr(out), _ptr(lse), code, out_code, _ptr(cu_seqlens),
                 n_seqs, q.shape[0], int(max_seqlen), Hq, Hkv, d, s_cap, int(n_depth), int(bool(causal)), float(scale))
-        if phase == 3:
+        if depth_topk is not None:
+            status = L.moda_attn_fwd_varlen_topk(*args[:18], *sel, *args[18:], *ws, stream)
+        elif phase == 3:
             status = L.moda_attn_fwd_varlen(*args, stream)
         else:
             status = L.moda_attn_fwd_varlen_phases(*args, int(phase), stream)
     else:
         args = (_ptr(q), _ptr(k), _ptr(v), kd_ptr, vd_ptr, _ptr(out), _ptr(lse), code, out_code, q.shape[0],
                 q.shape[1], Hq, Hkv, d, s_cap, int(n_depth), int(bool(causal)), float(scale))
-        if phase == 3:
+        if depth_topk is not None:
+            status = L.moda_attn_fwd_topk(*args[:16], *sel, *args[16:], *ws, stream)
+        elif phase == 3:
             status = L.moda_attn_fwd(*args, stream)
         else:
             status = L.moda_attn_fwd_phases(*args, int(phase), stream)
     _check(status)
     return out, lse
+
+
+def topk_workspace_size(total_tokens: int, n_heads_q: int) -> int:
+    """Bytes of device workspace a bounded-depth-read forward over N tokens needs."""
+    n = lib().moda_attn_fwd_topk_workspace_size(total_tokens, n_heads_q)
+    if n < 0:
+        raise ValueError("invalid sizes")
+    return int(n)
 
 
 def decode_workspace_size(batch: int, n_heads_q: int, n_heads_kv: int, head_dim: int, max_cache_len: int) -> int:

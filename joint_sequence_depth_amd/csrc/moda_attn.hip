@@ -275,10 +275,64 @@ int check_phase(int32_t phase, int32_t n_depth) {
   return MODA_OK;
 }
 
+// Bounded depth reads (top-S / sliding window / hybrid): which slots of each row
+// enter its softmax is decided by the selection kernel into the workspace.
+struct Select {
+  bool on;
+  int32_t topk, recent;
+  void* workspace;
+  int64_t workspace_bytes;
+};
+constexpr Select kNoSelect{false, 0, 0, nullptr, 0};
+
+int64_t select_workspace_bytes(int64_t N, int Hq) { return N * (int64_t)Hq * 8; }
+
+// Host checks of a bounded read; on MODA_OK `p` reads only the kept slots: every
+// slot (no launch), none (n_depth = 0) or a mask from the selection kernel,
+// launched on `stream` before the forward.
+int prepare_select(const Select& sel, const Common& c, moda::Params& p, int64_t N, hipStream_t stream) {
+  if (!sel.on) return MODA_OK;
+  if (sel.topk < 0 || sel.recent < 0) return fail(MODA_ERR_VALUE, "depth_topk and depth_recent must be >= 0");
+  if (c.n_depth > moda::kMaxSelectSlots)
+    return fail(MODA_ERR_UNSUPPORTED, "bounded depth reads support n_depth <= %d (got %d)", moda::kMaxSelectSlots,
+                c.n_depth);
+  const int64_t need = select_workspace_bytes(N, c.Hq);
+  if (!sel.workspace) return fail(MODA_ERR_NULL, "workspace must be non-NULL");
+  if (!aligned16(sel.workspace)) return fail(MODA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (sel.workspace_bytes < need)
+    return fail(MODA_ERR_SHAPE, "workspace too small: %lld bytes given, %lld needed", (long long)sel.workspace_bytes,
+                (long long)need);
+  const int recent = sel.recent < c.n_depth ? sel.recent : c.n_depth;
+  const int n_old = c.n_depth - recent;
+  if (sel.topk >= n_old) return MODA_OK;  // every slot stays: the operator itself
+  if (sel.topk == 0 && recent == 0) {     // no slot stays
+    p.n_depth = 0;
+    p.kd = p.vd = nullptr;
+    return MODA_OK;
+  }
+  moda::SelectParams s{};
+  s.q = c.q;
+  s.kd = c.kd;
+  s.mask = static_cast<uint64_t*>(sel.workspace);
+  s.n_tokens = N;
+  s.Hq = c.Hq;
+  s.Hkv = c.Hkv;
+  s.G = c.Hq / c.Hkv;
+  s.S_cap = c.S_cap;
+  s.n_depth = c.n_depth;
+  s.topk = sel.topk;
+  s.recent = recent;
+  s.scale = c.scale;
+  const hipError_t err = moda::launch_depth_select(s, c.d, c.dtype == MODA_DTYPE_BF16, stream);
+  if (err != hipSuccess) return fail(MODA_ERR_HIP, "selection kernel launch failed: %s", hipGetErrorString(err));
+  p.depth_mask = s.mask;
+  return MODA_OK;
+}
+
 int fwd_batch(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth, void* out,
               float* lse, int32_t dtype, int32_t out_dtype, int64_t batch, int64_t seqlen, int32_t n_heads_q,
               int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t n_depth, int32_t causal,
-              float scale, int32_t phase, void* stream) {
+              float scale, int32_t phase, void* stream, const Select& sel = kNoSelect) {
   if (batch < 0 || seqlen < 0) return fail(MODA_ERR_SHAPE, "batch and seqlen must be >= 0");
   const Common c{q,        k,          v,        k_depth,        v_depth, out,     lse,    dtype,
                  out_dtype, n_heads_q, n_heads_kv, head_dim, depth_capacity, n_depth, causal, scale};
@@ -299,13 +353,16 @@ int fwd_batch(const void* q, const void* k, const void* v, const void* k_depth, 
   p.n_seg = (int32_t)batch;
   p.lse_head_stride = seqlen;
   p.lse_batch_layout = 1;
+  rc = prepare_select(sel, c, p, batch * seqlen, static_cast<hipStream_t>(stream));
+  if (rc != MODA_OK) return rc;
   return dispatch(p, c, batch, seqlen, static_cast<hipStream_t>(stream));
 }
 
 int fwd_varlen(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth, void* out,
                float* lse, int32_t dtype, int32_t out_dtype, const int32_t* cu_seqlens, int32_t n_seqs,
                int64_t total_tokens, int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
-               int32_t depth_capacity, int32_t n_depth, int32_t causal, float scale, int32_t phase, void* stream) {
+               int32_t depth_capacity, int32_t n_depth, int32_t causal, float scale, int32_t phase, void* stream,
+               const Select& sel = kNoSelect) {
   if (n_seqs < 0 || total_tokens < 0 || max_seqlen < 0)
     return fail(MODA_ERR_SHAPE, "n_seqs, total_tokens and max_seqlen must be >= 0");
   const Common c{q,        k,          v,        k_depth,        v_depth, out,     lse,    dtype,
@@ -329,6 +386,8 @@ int fwd_varlen(const void* q, const void* k, const void* v, const void* k_depth,
   p.n_seg = n_seqs;
   p.lse_head_stride = total_tokens;
   p.lse_batch_layout = 0;
+  rc = prepare_select(sel, c, p, total_tokens, static_cast<hipStream_t>(stream));
+  if (rc != MODA_OK) return rc;
   return dispatch(p, c, n_seqs, max_seqlen, static_cast<hipStream_t>(stream));
 }
 
@@ -434,6 +493,33 @@ int moda_attn_fwd_varlen_phases(const void* q, const void* k, const void* v, con
   return fwd_varlen(q, k, v, k_depth, v_depth, out, lse, dtype, out_dtype, cu_seqlens, n_seqs, total_tokens,
                     max_seqlen, n_heads_q, n_heads_kv, head_dim, depth_capacity, n_depth, causal, scale, phase_mask,
                     stream);
+}
+
+int moda_attn_fwd_topk(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
+                       void* out, float* lse, int32_t dtype, int32_t out_dtype, int64_t batch, int64_t seqlen,
+                       int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity,
+                       int32_t n_depth, int32_t depth_topk, int32_t depth_recent, int32_t causal, float scale,
+                       void* workspace, int64_t workspace_bytes, void* stream) {
+  const Select sel{true, depth_topk, depth_recent, workspace, workspace_bytes};
+  return fwd_batch(q, k, v, k_depth, v_depth, out, lse, dtype, out_dtype, batch, seqlen, n_heads_q, n_heads_kv,
+                   head_dim, depth_capacity, n_depth, causal, scale, moda::kPhaseBoth, stream, sel);
+}
+
+int moda_attn_fwd_varlen_topk(const void* q, const void* k, const void* v, const void* k_depth, const void* v_depth,
+                              void* out, float* lse, int32_t dtype, int32_t out_dtype, const int32_t* cu_seqlens,
+                              int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen, int32_t n_heads_q,
+                              int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t n_depth,
+                              int32_t depth_topk, int32_t depth_recent, int32_t causal, float scale, void* workspace,
+                              int64_t workspace_bytes, void* stream) {
+  const Select sel{true, depth_topk, depth_recent, workspace, workspace_bytes};
+  return fwd_varlen(q, k, v, k_depth, v_depth, out, lse, dtype, out_dtype, cu_seqlens, n_seqs, total_tokens,
+                    max_seqlen, n_heads_q, n_heads_kv, head_dim, depth_capacity, n_depth, causal, scale,
+                    moda::kPhaseBoth, stream, sel);
+}
+
+int64_t moda_attn_fwd_topk_workspace_size(int64_t total_tokens, int32_t n_heads_q) {
+  if (total_tokens < 0 || n_heads_q < 1) return -1;
+  return select_workspace_bytes(total_tokens, n_heads_q);
 }
 
 int64_t moda_attn_decode_workspace_size(int64_t batch, int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,

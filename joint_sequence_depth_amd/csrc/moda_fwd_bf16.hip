@@ -349,7 +349,7 @@ moda_fwd_bf16_kernel(const Params p) {
   // current token, dm / da / dacc: max, sum and weighted sum per head) belong to
   // one call of depth_end, so none of them lives across the sequence loop.
   auto process = [&](int it, const uint4(&kw)[U], const uint4(&vw)[U], const uint4(&qw)[QBUF], uint4(&qc)[GB],
-                     float(&dm)[GB], float(&da)[GB], float(&dacc)[GB][8]) MODA_INL {
+                     uint64_t(&dsel)[GB], float(&dm)[GB], float(&da)[GB], float(&dacc)[GB][8]) MODA_INL {
     const int tg = it / nch, ch = it - tg * nch;
     const int tl = tg * NGRP + d_grp;
     if (ch == 0) {
@@ -363,6 +363,8 @@ moda_fwd_bf16_kernel(const Params p) {
         } else {
           qc[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * d_cl));
         }
+        // bounded depth reads: the slots this row's selection keeps (all without one)
+        dsel[g] = p.depth_mask ? p.depth_mask[n * Hq + hbase + g] : ~0ull;
         dm[g] = NEG_INF;
         da[g] = 0.f;
 #pragma unroll
@@ -379,7 +381,9 @@ moda_fwd_bf16_kernel(const Params p) {
         sc = dot2(qc[g].z, kw[u].z, sc);
         sc = dot2(qc[g].w, kw[u].w, sc);
         sc = group_sum<LPR>(sc);
-        b[u] = (ch * U + u < n_depth) ? sc * c2 : NEG_INF;
+        const int slot = ch * U + u;
+        // (a mask exists only for n_depth <= 64; without one every bit is set)
+        b[u] = (slot < n_depth && ((dsel[g] >> (slot & 63)) & 1ull)) ? sc * c2 : NEG_INF;
       }
       float mx = b[0];
 #pragma unroll
@@ -428,12 +432,13 @@ moda_fwd_bf16_kernel(const Params p) {
   };
   auto depth_end = [&]() MODA_INL {
     uint4 qc[GB];
+    uint64_t dsel[GB];
     float dm[GB], da[GB], dacc[GB][8];
     for (int it = 0; it < n_it; it += NBUF) {
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
         issue(it + j + NBUF - 1, dkb[(j + NBUF - 1) % NBUF], dvb[(j + NBUF - 1) % NBUF], dqb[(j + NBUF - 1) % NBUF]);
-        if (it + j < n_it) process(it + j, dkb[j], dvb[j], dqb[j], qc, dm, da, dacc);
+        if (it + j < n_it) process(it + j, dkb[j], dvb[j], dqb[j], qc, dsel, dm, da, dacc);
       }
     }
   };

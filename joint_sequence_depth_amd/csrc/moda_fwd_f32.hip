@@ -95,7 +95,10 @@ __global__ __launch_bounds__(64) void moda_fwd_f32_kernel(const Params p) {
   if (valid && p.n_depth > 0 && (p.phase & kPhaseDepth)) {
     const float* KD = static_cast<const float*>(p.kd);
     const float* VD = static_cast<const float*>(p.vd);
+    // bounded depth reads: the slots this row's selection keeps (all without one)
+    const uint64_t sel = p.depth_mask ? p.depth_mask[n * p.Hq + h] : ~0ull;
     for (int i = 0; i < p.n_depth; ++i) {
+      if (!((sel >> (i & 63)) & 1ull)) continue;  // (a mask exists only for n_depth <= 64)
       const int64_t off = ((n * p.S_cap + i) * p.Hkv + hk) * (int64_t)D;
       update<D>(dot_row<D>(q, KD + off) * c2, VD + off, m, l, o);
     }

@@ -40,6 +40,9 @@ struct Params {
   int32_t qb_major;           // 1: tiles ordered by query block across all pairs (heaviest first)
   int32_t phase;              // kPhaseBoth, or one part alone (kPhaseSeq / kPhaseDepth)
   int64_t n_tiles;
+  // bounded depth reads: bit i of depth_mask[n * Hq + h] says whether slot i enters
+  // row (n, h)'s softmax (null = every slot below n_depth)
+  const uint64_t* depth_mask;
 };
 
 // Which key sets enter the softmax of a forward launch: both (the operator), or
@@ -103,6 +106,22 @@ struct BwdParams {
 };
 
 hipError_t launch_bwd(const BwdParams& p, int head_dim, bool bf16, bool grad_f32, hipStream_t stream);
+
+// Slot selection of bounded depth reads (moda_depth_select.hip): per (token n,
+// query head h) the 64-bit mask of the slots [0, n_depth) that enter the softmax:
+// the last `recent`, and the `topk` largest logits of the others (ties to the
+// lower slot). n_depth <= 64.
+struct SelectParams {
+  const void* q;
+  const void* kd;
+  uint64_t* mask;  // [N, Hq]
+  int64_t n_tokens;
+  int32_t Hq, Hkv, G;
+  int32_t S_cap, n_depth, topk, recent;
+  float scale;
+};
+constexpr int kMaxSelectSlots = 64;
+hipError_t launch_depth_select(const SelectParams& p, int head_dim, bool bf16, hipStream_t stream);
 
 // Depth-KV writer (moda_depth_kv.hip): rows of row_vecs 16-byte vectors per token.
 struct DepthWriteParams {

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moda_abi_version() == 5
+    assert L.moda_abi_version() == 6
 
 
 def test_status_codes_match_header():
@@ -211,6 +211,50 @@ def test_packed_call_needs_max_seqlen(monkeypatch):
         _lib.attn_fwd(q, k, k, out=out, lse=lse, cu_seqlens=cu)
 
 
+def callt(topk=2, recent=1, ws=P, ws_bytes=1 << 30, **kw):
+    a = dict(A)
+    a.update(kw)
+    L = _lib.lib()
+    return L.moda_attn_fwd_topk(a["q"], a["k"], a["v"], a["kd"], a["vd"], a["out"], a["lse"], a["dtype"], a["odt"],
+                                a["B"], a["T"], a["Hq"], a["Hkv"], a["d"], a["Scap"], a["S"], topk, recent,
+                                a["causal"], a["scale"], ws, ws_bytes, None)
+
+
+def callvt(topk=2, recent=1, ws=P, ws_bytes=1 << 30, cu=P, n_seqs=2, N=16, max_len=8, **kw):
+    a = dict(A)
+    a.update(kw)
+    L = _lib.lib()
+    return L.moda_attn_fwd_varlen_topk(a["q"], a["k"], a["v"], a["kd"], a["vd"], a["out"], a["lse"], a["dtype"],
+                                       a["odt"], cu, n_seqs, N, max_len, a["Hq"], a["Hkv"], a["d"], a["Scap"], a["S"],
+                                       topk, recent, a["causal"], a["scale"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(topk=-1), 7),
+        (dict(recent=-2), 7),
+        (dict(S=65, Scap=65), 5),
+        (dict(ws=None), 1),
+        (dict(ws=P + 8), 4),
+        (dict(ws_bytes=16 * 4 * 8 - 1), 2),
+        (dict(d=96), 5),
+        (dict(q=None), 1),
+    ],
+)
+def test_topk_validation_rejects(kw, code):
+    assert callt(**kw) == code and err()
+    assert callvt(**kw) == code and err()
+
+
+def test_topk_workspace_size():
+    L = _lib.lib()
+    assert L.moda_attn_fwd_topk_workspace_size(16, 4) == 16 * 4 * 8
+    assert L.moda_attn_fwd_topk_workspace_size(-1, 4) == -1
+    assert L.moda_attn_fwd_topk_workspace_size(16, 0) == -1
+    assert callt(B=0) == 0 and callvt(n_seqs=0) == 0
+
+
 def test_python_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libmoda_attn.so")
@@ -224,6 +268,9 @@ def test_ctypes_signatures():
     assert len(L.moda_attn_fwd_varlen.argtypes) == 21
     assert len(L.moda_attn_fwd_phases.argtypes) == 20
     assert len(L.moda_attn_fwd_varlen_phases.argtypes) == 22
+    assert len(L.moda_attn_fwd_topk.argtypes) == 23
+    assert len(L.moda_attn_fwd_varlen_topk.argtypes) == 25
+    assert len(L.moda_attn_fwd_topk_workspace_size.argtypes) == 2
     assert len(L.moda_attn_decode.argtypes) == 21
     assert len(L.moda_attn_decode_noalloc.argtypes) == 19
     assert len(L.moda_attn_decode_workspace_size.argtypes) == 5
