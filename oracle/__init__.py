@@ -4,6 +4,7 @@ Test infrastructure: only the tests, the smoke check and the benchmark's CPU
 baseline leg may import it. It shares no code with the HIP library."""
 from .moda_oracle import (  # noqa: F401
     decode,
+    depth_kv_projection,
     depth_only,
     depth_utilization,
     depth_visible,

@@ -487,3 +487,27 @@ def joint_attention_backward(
             dkd = dkd.reshape((B, T) + dkd.shape[1:])
             dvd = dvd.reshape((B, T) + dvd.shape[1:])
     return dq, dk, dv, dkd, dvd
+
+
+def depth_kv_projection(x, w_kv, k_depth, v_depth, slot: int, n_heads_kv: int, head_dim: int):
+    """The FFN input's KV projection into one depth slot, in float64 (MoDA deck,
+    slide "Reuse attention KV; add a projection for FFN inputs", paper Sec. 2.2:
+    step 4 projects the FFN input into additional depth KV slots; the default
+    variant reuses the attention KV and adds this extra projection).
+
+    x [N, D_model]: the FFN input of N tokens. w_kv [2 * H_kv * d, D_model]: the
+    projection weight in the [out, in] layout of a linear layer, the key rows
+    first, then the value rows. k_depth, v_depth [N, S_cap, H_kv, d]: the depth
+    cache. Returns new copies of (k_depth, v_depth) whose slot ``slot`` holds
+    k = x w_k^T and v = x w_v^T of every token, reshaped [H_kv, d]; every other
+    slot is unchanged.
+    """
+    x, w = _f64(x), _f64(w_kv)
+    hd = n_heads_kv * head_dim
+    if w.shape != (2 * hd, x.shape[1]):
+        raise ValueError(f"w_kv must be [2 * H_kv * d, D_model] = {(2 * hd, x.shape[1])}, got {w.shape}")
+    kd, vd = np.array(k_depth, dtype=np.float64), np.array(v_depth, dtype=np.float64)
+    kv = x @ w.T  # [N, 2 * H_kv * d]
+    kd[:, slot] = kv[:, :hd].reshape(-1, n_heads_kv, head_dim)
+    vd[:, slot] = kv[:, hd:].reshape(-1, n_heads_kv, head_dim)
+    return kd, vd

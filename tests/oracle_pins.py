@@ -545,6 +545,45 @@ def pin_topk_brute_force(orc):
         assert np.max(np.abs(o - o2)) < 1e-12 and np.max(np.abs(lse - lse2)) < 1e-12, (it, topk, recent)
 
 
+# p27 ----------------------------------------------------------------------------
+def pin_projection_hand_example(orc):
+    """FFN-input KV projection into one slot, worked by hand
+    (tests/golden/projection_example.json)."""
+    with open(os.path.join(GOLDEN, "projection_example.json")) as f:
+        g = json.load(f)
+    x = np.array(g["x"], dtype=np.float64)
+    w = np.array(g["w_kv"], dtype=np.float64)
+    kd = np.full((1, g["S_cap"], 1, 2), -1.0)
+    vd = np.full((1, g["S_cap"], 1, 2), -2.0)
+    kd2, vd2 = orc.depth_kv_projection(x, w, kd, vd, g["slot"], 1, 2)
+    assert np.array_equal(kd2[0, g["slot"], 0], g["k"]) and np.array_equal(vd2[0, g["slot"], 0], g["v"])
+    others = [i for i in range(g["S_cap"]) if i != g["slot"]]
+    assert np.all(kd2[0, others] == -1.0) and np.all(vd2[0, others] == -2.0)
+
+
+# p28 ----------------------------------------------------------------------------
+def pin_projection_is_linear_then_slot(orc):
+    """Equals torch's linear layer (fp64) followed by placing the rows in the slot;
+    other slots are bit-identical; linear in the input."""
+    rng = np.random.default_rng(28)
+    N, D, Hkv, d, S = 7, 12, 2, 4, 3
+    x = rng.standard_normal((N, D))
+    w = rng.standard_normal((2 * Hkv * d, D))
+    kd = rng.standard_normal((N, S, Hkv, d))
+    vd = rng.standard_normal((N, S, Hkv, d))
+    kd2, vd2 = orc.depth_kv_projection(x, w, kd, vd, 1, Hkv, d)
+    ref = F.linear(torch.from_numpy(x), torch.from_numpy(w)).numpy()
+    assert np.max(np.abs(kd2[:, 1].reshape(N, -1) - ref[:, : Hkv * d])) < 1e-12
+    assert np.max(np.abs(vd2[:, 1].reshape(N, -1) - ref[:, Hkv * d :])) < 1e-12
+    assert np.array_equal(kd2[:, [0, 2]], kd[:, [0, 2]]) and np.array_equal(vd2[:, [0, 2]], vd[:, [0, 2]])
+    x2 = rng.standard_normal((N, D))
+    ka, va = orc.depth_kv_projection(x, w, kd, vd, 2, Hkv, d)
+    kb, vb = orc.depth_kv_projection(x2, w, kd, vd, 2, Hkv, d)
+    kc, vc = orc.depth_kv_projection(2.0 * x - 3.0 * x2, w, kd, vd, 2, Hkv, d)
+    assert np.max(np.abs(kc[:, 2] - (2.0 * ka[:, 2] - 3.0 * kb[:, 2]))) < 1e-11
+    assert np.max(np.abs(vc[:, 2] - (2.0 * va[:, 2] - 3.0 * vb[:, 2]))) < 1e-11
+
+
 ALL_PINS = [
     pin_empty_depth_is_sdpa,
     pin_equal_logits_plain_mean,
@@ -572,4 +611,6 @@ ALL_PINS = [
     pin_topk_hand_examples,
     pin_topk_limits,
     pin_topk_brute_force,
+    pin_projection_hand_example,
+    pin_projection_is_linear_then_slot,
 ]

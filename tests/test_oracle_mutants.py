@@ -59,6 +59,9 @@ MUTANTS = {
                           'order = np.argsort(-np.abs(b[:, :n_old]), axis=1, kind="stable")'),
     "topk_recent_off_by_one": ("keep[:, n_old:] = True", "keep[:, n_old + 1 :] = True"),
     "topk_one_too_many": ("k = max(0, min(topk, n_old))", "k = max(0, min(topk + 1, n_old))"),
+    "projection_key_value_swapped": ("kd[:, slot] = kv[:, :hd]", "kd[:, slot] = kv[:, hd:]"),
+    "projection_weight_read_as_in_out": ("kv = x @ w.T", "kv = x @ w.reshape(w.shape[1], -1)"),
+    "projection_wrong_slot": ("vd[:, slot] = kv[:, hd:]", "vd[:, (slot + 1) % vd.shape[1]] = kv[:, hd:]"),
 }
 
 
