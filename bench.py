@@ -45,6 +45,7 @@ KERNEL_SOURCES = ["moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_attn.hip", "mod
 DECODE_SOURCES = ["moda_decode.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h"]
 BWD_SOURCES = ["moda_bwd.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h"]
 WRITER_SOURCES = ["moda_depth_kv.hip", "moda_attn.hip", "moda_internal.h"]
+PROJECT_SOURCES = ["moda_depth_kv_project.hip", "moda_attn.hip", "moda_internal.h"]
 WRITER_METRIC = "depth-KV writer HBM GB/s (one layer's K/V rows into one slot of the depth cache)"
 BWD_METRIC = "fused seq+depth attention bwd TFLOP/s (dq, dk, dv, dk_depth, dv_depth)"
 DECODE_METRIC = "MoDA decode step (joint seq+depth softmax, one token per sequence) HBM GB/s"
@@ -725,6 +726,55 @@ def bench_writer(args, w, dev) -> int:
     return 0 if ok else 1
 
 
+PROJECT_METRIC = "FFN-input KV projection into a depth slot, bf16 MFMA TFLOP/s"
+
+
+def bench_project(args, w, dev) -> int:
+    """One step = the FFN input's KV projection of every token of the workload
+    into one slot of its depth cache: x [N, D_model = H_q d] times [W_k; W_v]
+    [2 H_kv d, D_model], the rows stored straight into slot s of [N, S_cap, H_kv, d]
+    (slots cycling over S_cap). Bound: bf16 MFMA."""
+    import torch
+
+    from joint_sequence_depth_amd import depth_kv_project
+    from workloads import gen
+
+    dt = torch.bfloat16 if w.bf16 else torch.float32
+    N, D, Hkv, d = w.n_tokens, w.n_heads_q * w.head_dim, w.n_heads_kv, w.head_dim
+    S_cap = max(1, w.s_cap)
+    x = gen.tensor_t(w.seed, 60, (N, D), dt, dev)
+    wkv = gen.tensor_t(w.seed, 61, (2 * Hkv * d, D), dt, dev, 2.0**-5)
+    kd = torch.zeros((N, S_cap, Hkv, d), dtype=dt, device=dev)
+    vd = torch.zeros_like(kd)
+    torch.cuda.synchronize()
+
+    def step(i):
+        depth_kv_project(x, wkv, kd, vd, i % S_cap)
+
+    class _A:  # time_steps' view of the arguments: S_cap steps per graph pass
+        steps, warmup, no_graph = args.steps, args.warmup, args.no_graph
+
+    ms, steps, use_graph = time_steps(step, S_cap, _A, dev, torch.cuda.current_stream(dev))
+    flops = 2.0 * N * D * 2 * Hkv * d
+    tf = flops / (ms / 1e3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.bf16 else PEAK_F32_TFLOPS
+    rec = {
+        "metric": PROJECT_METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.bf16 else "f32",
+        "data": "synthetic (seeded counter-based N(0,1) quantile grid; weights x 2^-5)",
+        "config": {"workload": w.name, "pass": "FFN-input KV projection", "tokens": N, "d_model": D,
+                   "n_heads_kv": Hkv, "head_dim": d, "depth_capacity": S_cap, "graph": use_graph},
+        "kernel": "moda_depth_kv_project_bf16_kernel" if w.bf16 else "moda_depth_kv_project_f32_kernel",
+        "kernel_source_sha": kernel_source_sha(PROJECT_SOURCES),
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def _lead_index(w, s, L):
     import numpy as np
 
@@ -751,6 +801,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="packed_bf16")
     ap.add_argument("--backward", action="store_true", help="time the backward pass of the workload instead")
     ap.add_argument("--writer", action="store_true", help="time the depth-KV writer on the workload's shapes instead")
+    ap.add_argument("--project", action="store_true",
+                    help="time the FFN-input KV projection into a depth slot on the workload's shapes instead")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
@@ -814,6 +866,8 @@ def main(argv=None) -> int:
         return bench_backward(args, w, dev)
     if args.writer:
         return bench_writer(args, w, dev)
+    if args.project:
+        return bench_project(args, w, dev)
     peaks = attained_peaks(dev)
     print(f"# attained peaks: {peaks}", file=sys.stderr, flush=True)
     batch_bytes = w.total_bytes()

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MODA_ABI_VERSION 6
+#define MODA_ABI_VERSION 7
 
 /* status codes */
 #define MODA_OK 0
@@ -293,6 +293,30 @@ int64_t moda_attn_bwd_workspace_size(int64_t total_tokens, int32_t n_heads_q, in
 int moda_depth_kv_write(const void* k_src, const void* v_src, void* k_depth, void* v_depth, int32_t dtype,
                         int64_t n_tokens, int32_t n_heads_kv, int32_t head_dim, int32_t depth_capacity, int32_t slot,
                         void* stream);
+
+/*
+ * The FFN input's KV projection, written straight into one depth slot (MoDA
+ * deck, slide "Reuse attention KV; add a projection for FFN inputs", paper Sec.
+ * 2.2: step 4 projects the FFN input into additional depth KV slots; the default
+ * variant reuses the attention KV, stored by moda_depth_kv_write, and adds this
+ * projection). For every token n:
+ *   k_depth[n, slot] = x_n W_k^T,  v_depth[n, slot] = x_n W_v^T   (each [Hkv, d])
+ *
+ *   x                  [N, d_model]               the FFN input of N tokens
+ *   w_kv               [2 * Hkv * d, d_model]     [W_k; W_v] in the [out, in] layout of
+ *                                                 a linear layer (key rows first); no bias
+ *   k_depth, v_depth   [N, S_cap, Hkv, d]         slot `slot` of every token is overwritten
+ *
+ * All in `dtype`; bf16 is multiplied on the matrix cores with fp32 accumulation
+ * and rounded to nearest-even once per output; fp32 in fp32. d_model a positive
+ * multiple of 64 and head_dim in {64, 128} (MODA_ERR_UNSUPPORTED otherwise);
+ * 0 <= slot < depth_capacity; all pointers 16-byte aligned, device memory owned
+ * by the caller; x and w_kv must not overlap the cache. Nothing else is written.
+ * n_tokens == 0 returns MODA_OK with no launch. Launches on `stream`.
+ */
+int moda_depth_kv_project(const void* x, const void* w_kv, void* k_depth, void* v_depth, int32_t dtype,
+                          int64_t n_tokens, int32_t d_model, int32_t n_heads_kv, int32_t head_dim,
+                          int32_t depth_capacity, int32_t slot, void* stream);
 
 /* Description of the last non-OK status returned on the calling thread ("" if none). */
 const char* moda_last_error(void);

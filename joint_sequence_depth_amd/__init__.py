@@ -13,10 +13,11 @@ from ._lib import (  # noqa: F401
     attn_fwd,
     bwd_workspace_size,
     decode_workspace_size,
+    depth_kv_project,
     depth_kv_write,
     lib,
     topk_workspace_size,
 )
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_decode_noalloc", "depth_kv_write", "bwd_workspace_size", "decode_workspace_size",
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_decode_noalloc", "depth_kv_write", "depth_kv_project", "bwd_workspace_size", "decode_workspace_size",
            "topk_workspace_size", "lib", "ModaError", "EXPORTS"]

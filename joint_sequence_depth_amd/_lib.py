@@ -33,6 +33,7 @@ EXPORTS = ("moda_attn_fwd", "moda_attn_fwd_varlen", "moda_attn_fwd_phases", "mod
            "moda_attn_fwd_topk", "moda_attn_fwd_varlen_topk", "moda_attn_fwd_topk_workspace_size",
            "moda_attn_decode", "moda_attn_decode_noalloc", "moda_attn_decode_workspace_size",
            "moda_attn_bwd", "moda_attn_bwd_varlen", "moda_attn_bwd_workspace_size", "moda_depth_kv_write",
+           "moda_depth_kv_project",
            "moda_last_error", "moda_abi_version")
 
 _lib = None
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.moda_attn_bwd_workspace_size.restype = ctypes.c_int64
         L.moda_depth_kv_write.argtypes = [vp] * 4 + [i32, i64, i32, i32, i32, i32, vp]
         L.moda_depth_kv_write.restype = ctypes.c_int
+        L.moda_depth_kv_project.argtypes = [vp] * 4 + [i32, i64, i32, i32, i32, i32, i32, vp]
+        L.moda_depth_kv_project.restype = ctypes.c_int
         L.moda_last_error.argtypes = []
         L.moda_last_error.restype = ctypes.c_char_p
         L.moda_abi_version.argtypes = []
@@ -532,4 +535,34 @@ def depth_kv_write(k_src, v_src, k_depth, v_depth, slot: int, stream=None):
         stream = torch.cuda.current_stream(k_src.device).cuda_stream
     _check(lib().moda_depth_kv_write(_ptr(k_src), _ptr(v_src), _ptr(k_depth), _ptr(v_depth), _dtype_code(k_src), n,
                                      k_src.shape[-2], k_src.shape[-1], k_depth.shape[lead], int(slot), stream))
+    return k_depth, v_depth
+
+
+def depth_kv_project(x, w_kv, k_depth, v_depth, slot: int, stream=None):
+    """Project the FFN input into one depth slot in place: x [N, D_model] (or
+    [B, T, D_model]), w_kv [2*Hkv*d, D_model] (key rows, then value rows: the
+    [out, in] layout of a linear layer), k_depth/v_depth [N, S_cap, Hkv, d] (or
+    [B, T, S_cap, Hkv, d]); slot ``slot`` of every token receives x W_k^T and x W_v^T."""
+    import torch
+
+    for t in (x, w_kv, k_depth, v_depth):
+        if not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError("all tensors must be contiguous GPU tensors")
+    if k_depth.shape != v_depth.shape:
+        raise ValueError("k_depth and v_depth must match in shape")
+    lead = x.dim() - 1
+    if k_depth.dim() != lead + 3 or k_depth.shape[:lead] != x.shape[:lead]:
+        raise ValueError(f"depth cache must be [..., S_cap, Hkv, d] for x {tuple(x.shape)}")
+    s_cap, hkv, d = k_depth.shape[lead:]
+    if w_kv.dim() != 2 or tuple(w_kv.shape) != (2 * hkv * d, x.shape[-1]):
+        raise ValueError(f"w_kv must be [2*Hkv*d, D_model] = {(2 * hkv * d, x.shape[-1])}")
+    if len({t.dtype for t in (x, w_kv, k_depth, v_depth)}) != 1:
+        raise TypeError("all tensors must share one dtype")
+    n = 1
+    for s in x.shape[:lead]:
+        n *= s
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    _check(lib().moda_depth_kv_project(_ptr(x), _ptr(w_kv), _ptr(k_depth), _ptr(v_depth), _dtype_code(x), n,
+                                       x.shape[-1], hkv, d, s_cap, int(slot), stream))
     return k_depth, v_depth

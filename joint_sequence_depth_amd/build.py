@@ -18,7 +18,7 @@ LIB_NAME = "libmoda_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 PEAKS_PATH = os.path.join(PKG, "libmoda_peaks.so")  # measurement only (include/moda_peaks.h)
 SOURCES = ["moda_attn.hip", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_depth_select.hip", "moda_decode.hip",
-           "moda_decode_noalloc.hip", "moda_bwd.hip", "moda_depth_kv.hip"]
+           "moda_decode_noalloc.hip", "moda_bwd.hip", "moda_depth_kv.hip", "moda_depth_kv_project.hip"]
 # Compilation units: (source, object stem, extra flags). The bf16 forward's
 # template instances are split by head dim and query heads per workgroup, one
 # unit each, so that they compile side by side.

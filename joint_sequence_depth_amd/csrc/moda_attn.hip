@@ -634,6 +634,43 @@ int moda_depth_kv_write(const void* k_src, const void* v_src, void* k_depth, voi
   return MODA_OK;
 }
 
+int moda_depth_kv_project(const void* x, const void* w_kv, void* k_depth, void* v_depth, int32_t dtype,
+                          int64_t n_tokens, int32_t d_model, int32_t n_heads_kv, int32_t head_dim,
+                          int32_t depth_capacity, int32_t slot, void* stream) {
+  if (n_tokens < 0) return fail(MODA_ERR_SHAPE, "n_tokens must be >= 0");
+  if (n_tokens == 0) {
+    g_err[0] = '\0';
+    return MODA_OK;
+  }
+  if (!x || !w_kv || !k_depth || !v_depth) return fail(MODA_ERR_NULL, "x, w_kv, k_depth and v_depth must be non-NULL");
+  if (dtype != MODA_DTYPE_F32 && dtype != MODA_DTYPE_BF16) return fail(MODA_ERR_DTYPE, "unknown dtype code %d", dtype);
+  if (n_heads_kv < 1) return fail(MODA_ERR_SHAPE, "n_heads_kv must be >= 1");
+  if (head_dim != 64 && head_dim != 128) return fail(MODA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (d_model < 64 || d_model % 64 != 0)
+    return fail(MODA_ERR_UNSUPPORTED, "d_model must be a positive multiple of 64 (got %d)", d_model);
+  if (depth_capacity < 1 || slot < 0 || slot >= depth_capacity)
+    return fail(MODA_ERR_SHAPE, "need 0 <= slot (%d) < depth_capacity (%d)", slot, depth_capacity);
+  if (!aligned16(x) || !aligned16(w_kv) || !aligned16(k_depth) || !aligned16(v_depth))
+    return fail(MODA_ERR_ALIGN, "x, w_kv, k_depth and v_depth must be 16-byte aligned");
+  if ((int64_t)n_heads_kv * head_dim > 0x3fffffffLL) return fail(MODA_ERR_SHAPE, "n_heads_kv * head_dim too large");
+  moda::ProjParams p{};
+  p.x = x;
+  p.w = w_kv;
+  p.kd = k_depth;
+  p.vd = v_depth;
+  p.n_tokens = n_tokens;
+  p.d_model = d_model;
+  p.hd = n_heads_kv * head_dim;
+  p.S_cap = depth_capacity;
+  p.slot = slot;
+  const int64_t tiles = (int64_t)(2 * p.hd / 64) * ((n_tokens + 63) / 64);
+  if (tiles > 0x7fffffffLL) return fail(MODA_ERR_SHAPE, "problem too large for one launch");
+  const hipError_t err = moda::launch_depth_kv_project(p, dtype == MODA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(MODA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  g_err[0] = '\0';
+  return MODA_OK;
+}
+
 const char* moda_last_error(void) { return g_err; }
 
 int32_t moda_abi_version(void) { return MODA_ABI_VERSION; }

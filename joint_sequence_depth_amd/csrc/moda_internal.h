@@ -136,6 +136,24 @@ struct DepthWriteParams {
 };
 hipError_t launch_depth_kv_write(const DepthWriteParams& p, hipStream_t stream);
 
+// The FFN input's KV projection into one depth slot (moda_depth_kv_project.hip):
+// x [N, d_model], w [2 hd, d_model] (key rows, then value rows), hd = H_kv d;
+// outputs at element ((n S_cap + slot) hd + c) of k_depth / v_depth.
+struct ProjParams {
+  const void* x;
+  const void* w;
+  void* kd;
+  void* vd;
+  int64_t n_tokens;
+  int32_t d_model;  // a multiple of 64
+  int32_t hd;       // H_kv * d, a multiple of 64
+  int32_t S_cap;
+  int32_t slot;
+  int32_t n_feat_tiles;  // set by the launcher
+  int64_t n_tok_tiles;   // set by the launcher
+};
+hipError_t launch_depth_kv_project(ProjParams p, bool bf16, hipStream_t stream);
+
 // One decode step (one new token per sequence); see moda_decode.hip.
 // Element offsets: q, out: (b * Hq + h) * D + c; caches: ((b * T_max + j) * Hkv + hk) * D + c;
 // depth: ((b * S_cap + i) * Hkv + hk) * D + c; lse: b * Hq + h.

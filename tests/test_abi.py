@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert L.moda_abi_version() == 6
+    assert L.moda_abi_version() == 7
 
 
 def test_status_codes_match_header():
@@ -279,6 +279,7 @@ def test_ctypes_signatures():
     assert len(L.moda_attn_bwd_varlen.argtypes) == 29
     assert len(L.moda_attn_bwd_workspace_size.argtypes) == 4
     assert len(L.moda_depth_kv_write.argtypes) == 11
+    assert len(L.moda_depth_kv_project.argtypes) == 12
     assert L.moda_last_error.restype is ctypes.c_char_p
 
 
@@ -466,3 +467,31 @@ def test_writer_validation_rejects(kw, code):
 def test_writer_empty_is_ok():
     assert callw(N=0, ks=None) == 0
     assert err() == ""
+
+
+def callp_(x=P, w=P, kd=P, vd=P, dtype=1, n=16, dm=128, hkv=2, d=64, scap=3, slot=1):
+    return _lib.lib().moda_depth_kv_project(x, w, kd, vd, dtype, n, dm, hkv, d, scap, slot, None)
+
+
+@pytest.mark.parametrize(
+    "kw,code",
+    [
+        (dict(x=None), 1),
+        (dict(w=None), 1),
+        (dict(dtype=3), 3),
+        (dict(d=96), 5),
+        (dict(dm=100), 5),
+        (dict(dm=0), 5),
+        (dict(slot=3), 2),
+        (dict(slot=-1), 2),
+        (dict(hkv=0), 2),
+        (dict(n=-1), 2),
+        (dict(kd=P + 4), 4),
+    ],
+)
+def test_projection_validation_rejects(kw, code):
+    assert callp_(**kw) == code and err()
+
+
+def test_projection_empty_is_ok():
+    assert callp_(n=0, x=None) == 0
