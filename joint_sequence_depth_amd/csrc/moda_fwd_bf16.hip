@@ -202,6 +202,7 @@ enum Mode : int {
   kNoDepth = 0,    // sequence keys only (n_depth == 0, or the sequence phase alone)
   kSerial = 1,     // every wave runs a depth pass and the sequence loop, one after the other
   kDepthOnly = 2,  // depth slots only (the depth phase alone): the sequence loop is skipped
+  kSerialMasked = 3,  // as kSerial, reading only the slots of each row's selection mask
 };
 
 // LDS. Stages hold one K or V block each: BN rows of D bf16 without padding, the
@@ -299,6 +300,7 @@ moda_fwd_bf16_kernel(const Params p) {
   const int64_t kend = p.causal ? (len < t0 + TOK ? len : t0 + TOK) : len;
   constexpr bool SEQ = MODE != kDepthOnly;   // the sequence keys enter this launch's softmax
   constexpr bool DEPTH = MODE != kNoDepth;   // the depth slots do
+  constexpr bool MASKED = MODE == kSerialMasked;  // bounded depth reads: a slot mask per row
   const int nkb = SEQ ? (int)((kend + BN - 1) / BN) : 0;  // sequence key blocks
 
   float* od = reinterpret_cast<float*>(smem + SM::OD_OFF);  // [ROWS][OS]
@@ -320,13 +322,15 @@ moda_fwd_bf16_kernel(const Params p) {
   // depth load buffers: shared by depth_begin and depth_end (always written
   // before they are read)
   uint4 dkb[NBUF][U], dvb[NBUF][U], dqb[NBUF][QBUF];
+  constexpr int MBUF = MASKED ? GB : 1;
+  uint64_t dmb[NBUF][MBUF];  // selection masks of the step's token (masked instances only)
 
   // Loads for step `it`: U slot rows of K and V (and the token's q rows at its
   // first batch) into one of the register buffers. The loads are unconditional so
   // the compiler keeps them in flight across the arithmetic: a slot past n_depth
   // re-reads the last slot and a token past the segment re-reads its last token
   // (cache hits); such logits are masked and such rows discarded.
-  auto issue = [&](int it, uint4(&kw)[U], uint4(&vw)[U], uint4(&qw)[QBUF]) MODA_INL {
+  auto issue = [&](int it, uint4(&kw)[U], uint4(&vw)[U], uint4(&qw)[QBUF], uint64_t(&mw)[MBUF]) MODA_INL {
     it = it < n_it ? it : n_it - 1;  // the steps past the end re-load the last one (never processed)
     const int tg = it / nch, ch = it - tg * nch;
     const int tl = tg * NGRP + d_grp;
@@ -344,12 +348,17 @@ moda_fwd_bf16_kernel(const Params p) {
 #pragma unroll
       for (int g = 0; g < QBUF; ++g) qw[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * d_cl));
     }
+    if constexpr (MASKED) {  // every step as well, for the same reason
+#pragma unroll
+      for (int g = 0; g < MBUF; ++g) mw[g] = p.depth_mask[n * Hq + hbase + g];
+    }
   };
   // One step of the pass on the loaded batch; the row states (qc: q rows of the
   // current token, dm / da / dacc: max, sum and weighted sum per head) belong to
   // one call of depth_end, so none of them lives across the sequence loop.
-  auto process = [&](int it, const uint4(&kw)[U], const uint4(&vw)[U], const uint4(&qw)[QBUF], uint4(&qc)[GB],
-                     uint64_t(&dsel)[GB], float(&dm)[GB], float(&da)[GB], float(&dacc)[GB][8]) MODA_INL {
+  auto process = [&](int it, const uint4(&kw)[U], const uint4(&vw)[U], const uint4(&qw)[QBUF],
+                     const uint64_t(&mw)[MBUF], uint4(&qc)[GB], uint64_t(&dsel)[GB], float(&dm)[GB], float(&da)[GB],
+                     float(&dacc)[GB][8]) MODA_INL {
     const int tg = it / nch, ch = it - tg * nch;
     const int tl = tg * NGRP + d_grp;
     if (ch == 0) {
@@ -364,7 +373,10 @@ moda_fwd_bf16_kernel(const Params p) {
           qc[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * d_cl));
         }
         // bounded depth reads: the slots this row's selection keeps (all without one)
-        dsel[g] = p.depth_mask ? p.depth_mask[n * Hq + hbase + g] : ~0ull;
+        if constexpr (MASKED)
+          dsel[g] = mw[g < MBUF ? g : 0];
+        else
+          dsel[g] = ~0ull;
         dm[g] = NEG_INF;
         da[g] = 0.f;
 #pragma unroll
@@ -428,7 +440,7 @@ moda_fwd_bf16_kernel(const Params p) {
   // leaves the others in flight.
   auto depth_begin = [&]() MODA_INL {
 #pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) issue(j, dkb[j], dvb[j], dqb[j]);
+    for (int j = 0; j < NBUF - 1; ++j) issue(j, dkb[j], dvb[j], dqb[j], dmb[j]);
   };
   auto depth_end = [&]() MODA_INL {
     uint4 qc[GB];
@@ -437,8 +449,9 @@ moda_fwd_bf16_kernel(const Params p) {
     for (int it = 0; it < n_it; it += NBUF) {
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
-        issue(it + j + NBUF - 1, dkb[(j + NBUF - 1) % NBUF], dvb[(j + NBUF - 1) % NBUF], dqb[(j + NBUF - 1) % NBUF]);
-        if (it + j < n_it) process(it + j, dkb[j], dvb[j], dqb[j], qc, dsel, dm, da, dacc);
+        issue(it + j + NBUF - 1, dkb[(j + NBUF - 1) % NBUF], dvb[(j + NBUF - 1) % NBUF], dqb[(j + NBUF - 1) % NBUF],
+              dmb[(j + NBUF - 1) % NBUF]);
+        if (it + j < n_it) process(it + j, dkb[j], dvb[j], dqb[j], dmb[j], qc, dsel, dm, da, dacc);
       }
     }
   };
@@ -493,7 +506,8 @@ moda_fwd_bf16_kernel(const Params p) {
   // as the sequence loop starts and consumed after it, which hides their latency
   // (at D = 128 the loop needs those registers; the pass follows the loop).
   constexpr bool EARLY_DEPTH = DEPTH && SPLIT && D == 64;
-  constexpr bool depth_first = (MODE == kSerial && GB < 4 && !SPLIT) || (MODE == kDepthOnly && !SPLIT);
+  constexpr bool depth_first =
+      ((MODE == kSerial || MODE == kSerialMasked) && GB < 4 && !SPLIT) || (MODE == kDepthOnly && !SPLIT);
   if constexpr (depth_first) {
     depth_begin();
     depth_end();
@@ -921,6 +935,7 @@ template <int D, int GB, int NW, bool SPLIT>
 hipError_t launch_d(const Params& p, int phase, bool out_f32, hipStream_t stream) {
   if (phase == kPhaseDepth) return launch_t<D, GB, NW, kDepthOnly, SPLIT>(p, out_f32, stream);
   if (p.n_depth == 0 || phase == kPhaseSeq) return launch_t<D, GB, NW, kNoDepth, SPLIT>(p, out_f32, stream);
+  if (p.depth_mask) return launch_t<D, GB, NW, kSerialMasked, SPLIT>(p, out_f32, stream);
   return launch_t<D, GB, NW, kSerial, SPLIT>(p, out_f32, stream);
 }
 
