@@ -152,7 +152,7 @@ def _counter_kib(run_dir, counter, name_part):
 def write_traffic(w, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cmds) -> None:
     """profiles/traffic_<workload>.json and a text summary from four rocprofv3 --pmc
     runs: FETCH_SIZE and WRITE_SIZE on the workload and on the 1 GiB copy."""
-    kname = kernel_name(w).split("<")[0]
+    kname = kernel_name(w)  # the full instance: the bench also launches the one-part instances
     copy_name = "copyBuffer"
     f_k, n_fk = _counter_kib(fetch_dir, "FETCH_SIZE", kname)
     w_k, n_wk = _counter_kib(write_dir, "WRITE_SIZE", kname)
@@ -243,6 +243,16 @@ def write_trace_summary(w, trace_dir, log_path, cmd, backward=False, writer=Fals
               f"value {bench_line['value']} {bench_line['unit']}; roofline {bench_line['roofline']['bound']} "
               f"{bench_line['roofline']['achieved']:.1f} {bench_line['roofline']['unit']} "
               f"(frac {bench_line['roofline']['frac']:.3f}); kernel sources sha {bench_line['kernel_source_sha']}."]
+    parts = bench_line.get("parts") or {}
+    for part in ("sequence_only", "depth_only"):
+        if part in parts:
+            row = next((r for r in stats if parts[part]["kernel"] in r["Name"]), None)
+            trace = f"; trace average {float(row['AverageNs']) / 1e3:.2f} us" if row else ""
+            rate = (f"{parts[part]['tflops']} TFLOP/s = {parts[part]['mfma_frac_of_peak']:.3f} of bf16 MFMA peak"
+                    if part == "sequence_only" else
+                    f"{parts[part]['depth_kv_gbs']} GB/s of depth K/V = {parts[part]['hbm_frac_of_peak']:.3f} of HBM peak")
+            lines.append(f"{part.replace('_', ' ')} ({parts[part]['kernel']}): bench {parts[part]['ms'] * 1e3:.2f} us"
+                         f"{trace}; {rate}.")
     prefix = "moda_bwd" if backward else "moda_depth_kv" if writer else _summary_prefix(w)
     with open(os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_kernel_trace.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -881,6 +891,7 @@ def main(argv=None) -> int:
     outs = [torch.empty(w.shape_q(), dtype=odt, device=dev) for _ in range(n_batches)]
     lses = [torch.empty(w.shape_lse(), dtype=torch.float32, device=dev) for _ in range(n_batches)]
     torch.cuda.synchronize()
+    print("# inputs generated", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream(dev)
 
     sel = {}

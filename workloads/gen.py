@@ -122,7 +122,7 @@ def _qtab_t(device):
     return _QTAB_CACHE[key]
 
 
-def fill_(out, seed: int, tid: int, mult: float = 1.0, chunk: int = 1 << 26):
+def fill_(out, seed: int, tid: int, mult: float = 1.0, chunk: int = 1 << 28):
     """Fill a contiguous torch tensor (float32 or bfloat16, any device) in place."""
     import torch
 
