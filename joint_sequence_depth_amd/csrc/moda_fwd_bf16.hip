@@ -256,11 +256,10 @@ moda_fwd_bf16_kernel(const Params p) {
   constexpr int U = GB == 1 ? 8 : (GB == 2 ? 4 : 2);  // depth slots per load batch
   constexpr bool QPRE = GB <= 2;               // prefetch a token's q rows with its first batch
   constexpr int QBUF = QPRE ? GB : 1;
-  // depth load buffers (batches in flight + 1); when the depth pass follows the
-  // sequence loop the O^T accumulators are live, so the count stays small (more
-  // batches issued before a split tile's loop only add to the HBM burst at its
-  // start)
-  constexpr int NBUF = GB == 1 ? 2 : (GB == 2 ? 3 : 4);
+  // depth load buffers (batches in flight + 1); split tiles run the pass beside
+  // the live O^T accumulators, so the count stays small (more batches issued
+  // before a split tile's loop only add to the HBM burst at its start)
+  constexpr int NBUF = GB == 1 ? 2 : 3;
   using SM = Smem<D, NW, MODE, SPLIT>;
   constexpr int NST = SM::NST;
   constexpr int P = NST - 1;                 // load groups in flight ahead of the current block
@@ -495,19 +494,17 @@ moda_fwd_bf16_kernel(const Params p) {
     m_run = m_new;
   };
 
-  // Shared tiles, GB < 4: the depth pass runs first, so the workgroup's HBM phase
-  // precedes its matrix-core phase and the staggered starts of the workgroups on
-  // a CU overlap the two. Fixed at compile time: the depth buffers are then never
-  // live together with the output accumulators, which avoids the register spills
-  // a depth-last path costs the D = 128 instances. GB = 4 (four heads share each
-  // depth row, so the sequence loop outweighs the depth stream): the pass runs
-  // last, which measured faster despite those spills. Split tiles at
-  // D = 64: the depth loads are issued
-  // as the sequence loop starts and consumed after it, which hides their latency
-  // (at D = 128 the loop needs those registers; the pass follows the loop).
+  // Shared tiles: the depth pass runs first, so the workgroup's HBM phase precedes
+  // its matrix-core phase and the staggered starts of the workgroups on a CU
+  // overlap the two. Fixed at compile time: the depth buffers are then never live
+  // together with the output accumulators, which keeps every D = 128 instance free
+  // of register spills (a depth-last four-head instance spilled 36-44 bytes per
+  // lane, 1.3x the algorithmic HBM writes, for the same time). Split tiles at
+  // D = 64: the depth loads are issued as the sequence loop starts and consumed
+  // after it, which hides their latency (at D = 128 the loop needs those
+  // registers; the pass follows the loop).
   constexpr bool EARLY_DEPTH = DEPTH && SPLIT && D == 64;
-  constexpr bool depth_first =
-      ((MODE == kSerial || MODE == kSerialMasked) && GB < 4 && !SPLIT) || (MODE == kDepthOnly && !SPLIT);
+  constexpr bool depth_first = DEPTH && !SPLIT;
   if constexpr (depth_first) {
     depth_begin();
     depth_end();
@@ -878,13 +875,7 @@ moda_fwd_bf16_kernel(const Params p) {
       m_run = m_new;
     }
     if constexpr (DEPTH) depth_fold();
-  } else if constexpr (DEPTH && !depth_first) {
-    __syncthreads();  // every wave's loads have landed: the K/V area is free
-    depth_begin();
-    depth_end();
-    __syncthreads();
-    depth_fold();
-  }
+  }  // shared tiles folded their depth state before the loop
 
   // ---- normalise once and write ------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
