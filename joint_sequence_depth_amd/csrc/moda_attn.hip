@@ -125,7 +125,7 @@ int dispatch(moda::Params& p, const Common& c, int64_t n_seg, int64_t max_len, h
     const int64_t nqb = (max_len + tok - 1) / tok;
     p.n_qblocks = (int32_t)nqb;
     p.n_tiles = n_pairs * p.n_hgroups * nqb;
-    p.xcd_interleave = (!split && n_pairs % 8 == 0) ? 1 : 0;
+    p.xcd_interleave = split ? 0 : (p.n_hgroups == 1 && p.Hkv % 8 == 0) ? 2 : n_pairs % 8 == 0 ? 1 : 0;
     p.qb_major = split ? 1 : 0;
     if (nqb > kMaxTiles || p.n_tiles > kMaxTiles) return fail(MODA_ERR_SHAPE, "problem too large for one launch");
     err = launch_fwd_bf16(p, c.d, gb, waves, split, c.out_dtype == MODA_DTYPE_F32, stream);

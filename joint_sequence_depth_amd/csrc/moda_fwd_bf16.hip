@@ -167,12 +167,17 @@ struct Tile {
 // A pair = (segment, KV head); its tiles are (query block, head group), head group
 // fastest, so the workgroups of a KV head's head groups run side by side and share
 // that token block's depth rows in L2. Workgroups go to the 8 XCDs round-robin
-// (id % 8). With a multiple of 8 pairs, pair p runs all of its tiles on XCD p % 8:
-// its K/V blocks, read by every query block, stay in that XCD's L2, and every XCD
-// gets an equal share of every segment, whatever the segment lengths. Within a
-// pair, late (heavy causal) query blocks go first. With qb_major (used when the
-// grid runs in few rounds) the order is by query block across all pairs instead,
-// heaviest first, so the first round holds the longest causal tiles.
+// (id % 8). Late (heavy causal) query blocks go first. Orders:
+//  - xcd_interleave 2 (one head group per KV head, KV heads a multiple of 8):
+//    segment-major, then query block, KV head fastest. The KV heads of a token
+//    block run at the same time, so the slot rows of a token ([S, H_kv, d], one
+//    contiguous run per slot) are read whole rather than head by head at
+//    different times, and KV head hk always lands on XCD hk % 8: its K/V blocks,
+//    read by every query block, stay in that XCD's L2.
+//  - xcd_interleave 1 (a multiple of 8 pairs): pair p runs all of its tiles on XCD
+//    p % 8, and every XCD gets an equal share of every segment.
+//  - qb_major (used when the grid runs in few rounds): by query block across all
+//    pairs, heaviest first, so the first round holds the longest causal tiles.
 __device__ __forceinline__ Tile decode_tile(const Params& p) {
   const int64_t id = blockIdx.x;
   const int64_t per_pair = (int64_t)p.n_qblocks * p.n_hgroups;
@@ -182,7 +187,12 @@ __device__ __forceinline__ Tile decode_tile(const Params& p) {
     const int64_t qrank = id / units, u = id % units;
     pair = u / p.n_hgroups;
     r = qrank * p.n_hgroups + u % p.n_hgroups;
-  } else if (p.xcd_interleave) {
+  } else if (p.xcd_interleave == 2) {
+    const int64_t per_seg = (int64_t)p.n_qblocks * p.Hkv;
+    const int64_t seg = id / per_seg, rr = id % per_seg;
+    pair = seg * p.Hkv + rr % p.Hkv;
+    r = rr / p.Hkv;
+  } else if (p.xcd_interleave == 1) {
     const int64_t x = id & 7, j = id >> 3;
     pair = (j / per_pair) * 8 + x;
     r = j % per_pair;

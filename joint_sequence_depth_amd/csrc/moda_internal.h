@@ -36,7 +36,8 @@ struct Params {
 
   int64_t lse_head_stride;    // T (batch layout) or N (packed layout)
   int32_t lse_batch_layout;   // 1: base = s * Hq * T; 0: base = seg_start
-  int32_t xcd_interleave;     // 1: (segment, KV head) pairs go round-robin to the 8 XCDs
+  int32_t xcd_interleave;     // 1: (segment, KV head) pairs go round-robin to the 8 XCDs;
+                              // 2: KV head fastest, KV head hk on XCD hk % 8
   int32_t qb_major;           // 1: tiles ordered by query block across all pairs (heaviest first)
   int32_t phase;              // kPhaseBoth, or one part alone (kPhaseSeq / kPhaseDepth)
   int64_t n_tiles;
