@@ -710,6 +710,22 @@ moda_fwd_bf16_kernel(const Params p) {
     ph[se][j] = h;
     pl[se][j] = pack_bf16(p0 - lo_bf16(h), p1 - hi_bf16(h));
   };
+  // fast steps: p of pair q written over its scores and packed as bf16 (the high
+  // part); the low part is formed from them later, beside the P.V products
+  auto exp_hi = [&](f32x16(&s)[2], float m_use, int q, uint32_t(&ph)[2][8], float& lsum) MODA_INL {
+    const int se = q >> 3, j = q & 7;
+    const float p0 = fast_exp2(fmaf(s[se][2 * j], c2, -m_use));
+    const float p1 = fast_exp2(fmaf(s[se][2 * j + 1], c2, -m_use));
+    lsum += p0 + p1;
+    s[se][2 * j] = p0;
+    s[se][2 * j + 1] = p1;
+    ph[se][j] = pack_bf16(p0, p1);
+  };
+  auto lo_of = [&](const f32x16(&s)[2], int q, const uint32_t(&ph)[2][8], uint32_t(&pl)[2][8]) MODA_INL {
+    const int se = q >> 3, j = q & 7;
+    const uint32_t h = ph[se][j];
+    pl[se][j] = pack_bf16(s[se][2 * j] - lo_bf16(h), s[se][2 * j + 1] - hi_bf16(h));
+  };
   // B operand of PV MFMA i: the packed probabilities of key tile st, half part.
   auto pfrag = [](const uint32_t(&pp)[2][8], int i) MODA_INL {
     const int st = i / (2 * DT), part = (i / DT) % 2;
@@ -743,9 +759,11 @@ moda_fwd_bf16_kernel(const Params p) {
 
   // Step for a fully visible block, written in issue order: each score MFMA of
   // the next block is followed by the exponentials of pairs of this block's
-  // scores; operands are read two MFMAs ahead. sched_barrier keeps that order, so
-  // the vector work runs while the matrix core is busy. When kb + 1 == nkb the
-  // next scores read a stage that holds no keys and are never used.
+  // scores (p over the scores, and its bf16 high part); the low parts of P.V
+  // fragment f + 1 are formed between the products of fragment f, so the wave's
+  // vector work also fills its P.V phase. Operands are read two MFMAs ahead.
+  // sched_barrier keeps that order. When kb + 1 == nkb the next scores read a
+  // stage that holds no keys and are never used.
   auto fast_step = [&](int i, f32x16(&scur)[2], f32x16(&snext)[2]) MODA_INL {
     issue_group(i + P);
     const float m_use = max_and_rescale(scur);
@@ -769,7 +787,8 @@ moda_fwd_bf16_kernel(const Params p) {
         snext[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kc], snext[st], 0, 0, 0);
       }
 #pragma unroll
-      for (int q = i * 16 / NQK; q < (i + 1) * 16 / NQK; ++q) exp_pair(scur, m_use, q, ph, pl, lsum);
+      for (int q = i * 16 / NQK; q < (i + 1) * 16 / NQK; ++q) exp_hi(scur, m_use, q, ph, lsum);
+      if (i >= NQK - 4) lo_of(scur, i - (NQK - 4), ph, pl);  // low parts of the first P.V fragment
       __builtin_amdgcn_sched_barrier(0);
       a0 = a1;
       a1 = a2;
@@ -782,6 +801,11 @@ moda_fwd_bf16_kernel(const Params p) {
       bf16x8 b2 = b1;
       if (i + 2 < NPV) b2 = vread(vs, i + 2);
       acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, pfrag(ph, i), acc[i % DT], 0, 0, 0);
+      // fragment f = i / DT (pairs 4 f .. 4 f + 3) is in use: form the next one's low parts
+      if (i / DT + 1 < 4) {
+#pragma unroll
+        for (int k = 0; k < 4 / DT; ++k) lo_of(scur, 4 * (i / DT + 1) + (i % DT) * (4 / DT) + k, ph, pl);
+      }
       acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, pfrag(pl, i), acc[i % DT], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       b0 = b1;
