@@ -977,8 +977,8 @@ def main(argv=None) -> int:
             "depth_topk": args.depth_topk, "depth_recent": args.depth_recent, "kept_slots": kept,
             "algorithmic_bytes": alg, "gbs": round(alg / sec / 1e9, 1),
             "hbm_frac_of_peak": round(alg / sec / 1e9 / PEAK_HBM_GBS, 4),
-            "note": "keys of every slot are read to score them; values only of the kept slots count as algorithmic "
-                    "bytes (the kernel reads all of them)",
+            "note": "keys of every slot are read to rank them, values of the kept slots only (bf16: selected "
+                    "inside the depth pass; grouped heads read the union of their kept slots)",
         }
     rec = {
         "metric": METRIC,

@@ -137,12 +137,16 @@ int moda_attn_fwd_varlen_phases(const void* q, const void* k, const void* v, con
  * depth_topk = 0 a sliding window of the depth_recent most recent slots, both > 0
  * the hybrid. When depth_topk covers every older slot the call is the operator.
  *
- * A selection kernel scores every slot and writes a 64-bit slot mask per row to
- * `workspace` (DEVICE memory of at least moda_attn_fwd_topk_workspace_size(N, Hq)
- * bytes, 16-byte aligned, caller-owned, contents on entry irrelevant; calls that
- * share one workspace must not overlap); the forward then reads the kept slots.
- * Both kernels run on `stream`. The logits that decide the selection are fp32:
- * slots whose logits tie within fp32 rounding may be chosen either way.
+ * bf16 inputs: the forward's depth pass makes the selection itself (it reads
+ * every slot's key, ranks each row's logits, then reads the values of the kept
+ * slots only) and leaves `workspace` untouched. fp32 inputs: a selection kernel
+ * scores every slot and writes a 64-bit slot mask per row to `workspace`, which
+ * the forward then reads. `workspace`: DEVICE memory of at least
+ * moda_attn_fwd_topk_workspace_size(N, Hq) bytes, 16-byte aligned, caller-owned,
+ * contents on entry irrelevant; calls that share one workspace must not overlap
+ * (required for both dtypes). Every kernel runs on `stream`. The logits that
+ * decide the selection are fp32: slots whose logits tie within fp32 rounding may
+ * be chosen either way.
  * n_depth <= 64 (MODA_ERR_UNSUPPORTED otherwise); depth_topk, depth_recent >= 0
  * (MODA_ERR_VALUE). Other arguments, checks and errors as for moda_attn_fwd /
  * moda_attn_fwd_varlen; MODA_ERR_SHAPE also for a too small workspace.

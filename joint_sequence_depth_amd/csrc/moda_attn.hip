@@ -310,7 +310,13 @@ int prepare_select(const Select& sel, const Common& c, moda::Params& p, int64_t 
     p.kd = p.vd = nullptr;
     return MODA_OK;
   }
-  moda::SelectParams s{};
+  if (c.dtype == MODA_DTYPE_BF16) {  // selected inside the forward's depth pass
+    p.sel_fused = 1;
+    p.sel_topk = sel.topk;
+    p.sel_recent = recent;
+    return MODA_OK;
+  }
+  moda::SelectParams s{};  // fp32: a selection kernel writes one slot mask per row
   s.q = c.q;
   s.kd = c.kd;
   s.mask = static_cast<uint64_t*>(sel.workspace);

@@ -13,9 +13,10 @@
 // head are scored against them (fp32 FMA, DPP group sums). Per head,
 // lane i then ranks slot i among the older slots by (logit descending, index
 // ascending) and a ballot gives the 64-bit mask of the slots that enter, written
-// to mask[token * Hq + head]. The forward's depth pass reads the mask and leaves
-// the other slots out of the softmax. The selection only decides membership: the
-// forward recomputes the kept logits itself.
+// to mask[token * Hq + head]. The fp32 forward reads the mask and leaves the
+// other slots out of the softmax (the bf16 forward selects inside its own depth
+// pass). The selection only decides membership: the forward recomputes the kept
+// logits itself.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

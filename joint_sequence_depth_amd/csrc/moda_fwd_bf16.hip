@@ -159,6 +159,14 @@ __device__ __forceinline__ float group_sum(float s) {
   if constexpr (LPR == 16) s += dpp_f<0x140>(s);  // row_mirror: the other half of the row
   return s;
 }
+template <int LPR>
+__device__ __forceinline__ float group_max(float s) {
+  s = fmaxf(s, dpp_f<0xB1>(s));
+  s = fmaxf(s, dpp_f<0x4E>(s));
+  s = fmaxf(s, dpp_f<0x141>(s));
+  if constexpr (LPR == 16) s = fmaxf(s, dpp_f<0x140>(s));
+  return s;
+}
 
 struct Tile {
   int seg, hk, hg, qb;
@@ -212,7 +220,7 @@ enum Mode : int {
   kNoDepth = 0,    // sequence keys only (n_depth == 0, or the sequence phase alone)
   kSerial = 1,     // every wave runs a depth pass and the sequence loop, one after the other
   kDepthOnly = 2,  // depth slots only (the depth phase alone): the sequence loop is skipped
-  kSerialMasked = 3,  // as kSerial, reading only the slots of each row's selection mask
+  kSelect = 3,     // as kSerial, with bounded depth reads: each row keeps some of its slots
 };
 
 // LDS. Stages hold one K or V block each: BN rows of D bf16 without padding, the
@@ -309,7 +317,7 @@ moda_fwd_bf16_kernel(const Params p) {
   const int64_t kend = p.causal ? (len < t0 + TOK ? len : t0 + TOK) : len;
   constexpr bool SEQ = MODE != kDepthOnly;   // the sequence keys enter this launch's softmax
   constexpr bool DEPTH = MODE != kNoDepth;   // the depth slots do
-  constexpr bool MASKED = MODE == kSerialMasked;  // bounded depth reads: a slot mask per row
+  constexpr bool SELECT = MODE == kSelect;   // bounded depth reads, selected inside the depth pass
   const int nkb = SEQ ? (int)((kend + BN - 1) / BN) : 0;  // sequence key blocks
 
   float* od = reinterpret_cast<float*>(smem + SM::OD_OFF);  // [ROWS][OS]
@@ -331,15 +339,13 @@ moda_fwd_bf16_kernel(const Params p) {
   // depth load buffers: shared by depth_begin and depth_end (always written
   // before they are read)
   uint4 dkb[NBUF][U], dvb[NBUF][U], dqb[NBUF][QBUF];
-  constexpr int MBUF = MASKED ? GB : 1;
-  uint64_t dmb[NBUF][MBUF];  // selection masks of the step's token (masked instances only)
 
   // Loads for step `it`: U slot rows of K and V (and the token's q rows at its
   // first batch) into one of the register buffers. The loads are unconditional so
   // the compiler keeps them in flight across the arithmetic: a slot past n_depth
   // re-reads the last slot and a token past the segment re-reads its last token
   // (cache hits); such logits are masked and such rows discarded.
-  auto issue = [&](int it, uint4(&kw)[U], uint4(&vw)[U], uint4(&qw)[QBUF], uint64_t(&mw)[MBUF]) MODA_INL {
+  auto issue = [&](int it, uint4(&kw)[U], uint4(&vw)[U], uint4(&qw)[QBUF]) MODA_INL {
     it = it < n_it ? it : n_it - 1;  // the steps past the end re-load the last one (never processed)
     const int tg = it / nch, ch = it - tg * nch;
     const int tl = tg * NGRP + d_grp;
@@ -357,17 +363,12 @@ moda_fwd_bf16_kernel(const Params p) {
 #pragma unroll
       for (int g = 0; g < QBUF; ++g) qw[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * d_cl));
     }
-    if constexpr (MASKED) {  // every step as well, for the same reason
-#pragma unroll
-      for (int g = 0; g < MBUF; ++g) mw[g] = p.depth_mask[n * Hq + hbase + g];
-    }
   };
   // One step of the pass on the loaded batch; the row states (qc: q rows of the
   // current token, dm / da / dacc: max, sum and weighted sum per head) belong to
   // one call of depth_end, so none of them lives across the sequence loop.
-  auto process = [&](int it, const uint4(&kw)[U], const uint4(&vw)[U], const uint4(&qw)[QBUF],
-                     const uint64_t(&mw)[MBUF], uint4(&qc)[GB], uint64_t(&dsel)[GB], float(&dm)[GB], float(&da)[GB],
-                     float(&dacc)[GB][8]) MODA_INL {
+  auto process = [&](int it, const uint4(&kw)[U], const uint4(&vw)[U], const uint4(&qw)[QBUF], uint4(&qc)[GB],
+                     float(&dm)[GB], float(&da)[GB], float(&dacc)[GB][8]) MODA_INL {
     const int tg = it / nch, ch = it - tg * nch;
     const int tl = tg * NGRP + d_grp;
     if (ch == 0) {
@@ -381,11 +382,6 @@ moda_fwd_bf16_kernel(const Params p) {
         } else {
           qc[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * d_cl));
         }
-        // bounded depth reads: the slots this row's selection keeps (all without one)
-        if constexpr (MASKED)
-          dsel[g] = mw[g < MBUF ? g : 0];
-        else
-          dsel[g] = ~0ull;
         dm[g] = NEG_INF;
         da[g] = 0.f;
 #pragma unroll
@@ -403,8 +399,7 @@ moda_fwd_bf16_kernel(const Params p) {
         sc = dot2(qc[g].w, kw[u].w, sc);
         sc = group_sum<LPR>(sc);
         const int slot = ch * U + u;
-        // (a mask exists only for n_depth <= 64; without one every bit is set)
-        b[u] = (slot < n_depth && ((dsel[g] >> (slot & 63)) & 1ull)) ? sc * c2 : NEG_INF;
+        b[u] = slot < n_depth ? sc * c2 : NEG_INF;
       }
       float mx = b[0];
 #pragma unroll
@@ -449,18 +444,250 @@ moda_fwd_bf16_kernel(const Params p) {
   // leaves the others in flight.
   auto depth_begin = [&]() MODA_INL {
 #pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) issue(j, dkb[j], dvb[j], dqb[j], dmb[j]);
+    for (int j = 0; j < NBUF - 1; ++j) issue(j, dkb[j], dvb[j], dqb[j]);
   };
   auto depth_end = [&]() MODA_INL {
     uint4 qc[GB];
-    uint64_t dsel[GB];
     float dm[GB], da[GB], dacc[GB][8];
     for (int it = 0; it < n_it; it += NBUF) {
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
-        issue(it + j + NBUF - 1, dkb[(j + NBUF - 1) % NBUF], dvb[(j + NBUF - 1) % NBUF], dqb[(j + NBUF - 1) % NBUF],
-              dmb[(j + NBUF - 1) % NBUF]);
-        if (it + j < n_it) process(it + j, dkb[j], dvb[j], dqb[j], dmb[j], qc, dsel, dm, da, dacc);
+        issue(it + j + NBUF - 1, dkb[(j + NBUF - 1) % NBUF], dvb[(j + NBUF - 1) % NBUF], dqb[(j + NBUF - 1) % NBUF]);
+        if (it + j < n_it) process(it + j, dkb[j], dvb[j], dqb[j], qc, dm, da, dacc);
+      }
+    }
+  };
+
+  // ---------------------------------------------------- bounded depth reads (kSelect)
+  // Of a row's slots [0, n_depth), the last sel_recent always enter its softmax and
+  // of the older ones the sel_topk with the largest logits, ties to the lower slot
+  // (the future-work buffer of the MoDA deck's slide "The main open cost is
+  // retaining and reading depth history", read as a per-row selection). The
+  // selection runs inside the pass. Per token group, K steps read every slot's
+  // key row, score it against the GB heads and keep the raw dot products in the
+  // rows' LDS hand-off records; after the last K step each row ranks its older
+  // slots and adds its 64-bit keep mask and the max of its kept logits to the
+  // record. V steps then read the value rows of the kept slots only (for GB > 1,
+  // of the union over the heads, at most n_cand rows per token) and accumulate
+  // against the known max: no rescale. Steps run as [K(0)], [K(1), V(0)], ...,
+  // [V(last)], so a V step's slots, which follow from its group's masks, are
+  // loaded (one step ahead) only after that group's ranking has run; with a
+  // single token group the first V step is issued after it instead.
+  constexpr int US = 2 * U;         // slot rows per select step (keys or values, not both)
+  constexpr int SPL = 64 / LPR;     // slots each lane ranks
+  constexpr int REC_MASK = 64;      // record words: [0, 64) dot products, mask (2 words), max
+  constexpr int REC_MAX = 66;
+  static_assert(SM::OS > REC_MAX, "selection record");
+  const uintptr_t vd_minus_kd = reinterpret_cast<uintptr_t>(p.vd) - reinterpret_cast<uintptr_t>(p.kd);
+  const int sel_recent = SELECT ? p.sel_recent : 0;
+  const int n_old = n_depth - sel_recent;
+  const int n_keep = (p.sel_topk < n_old ? p.sel_topk : n_old) + sel_recent;
+  const int n_cand = GB * n_keep < n_depth ? GB * n_keep : n_depth;  // value rows per token (bound)
+  const int nck = (n_depth + US - 1) / US;  // K steps per token group
+  const int ncv = (n_cand + US - 1) / US;   // V steps per token group
+  const int seg_steps = nck + ncv;
+  const int n_sel = NTG * seg_steps;
+  struct SelStep {
+    bool is_k;
+    int tg, b;
+  };
+  auto sel_step = [&](int it) MODA_INL {
+    SelStep st;
+    if (it < nck) {
+      st.is_k = true;
+      st.tg = 0;
+      st.b = it;
+    } else {
+      const int j = it - nck, sg = 1 + j / seg_steps, r = j - (sg - 1) * seg_steps;
+      st.is_k = sg < NTG && r < nck;
+      st.tg = st.is_k ? sg : sg - 1;
+      st.b = st.is_k ? r : (sg < NTG ? r - nck : r);
+    }
+    return st;
+  };
+  // the record of row (token tl of this wave, head g); tokens past the wave's use
+  // its last token's (they compute, but never write)
+  auto rec_of = [&](int tl, int g) MODA_INL {
+    const int tlc = tl < TPW ? tl : TPW - 1;
+    return od + ((dt0 + tlc) * GB + g) * SM::OS;
+  };
+  auto rec_mask = [&](const float* rec) MODA_INL {
+    return (uint64_t)__float_as_uint(rec[REC_MASK]) | ((uint64_t)__float_as_uint(rec[REC_MASK + 1]) << 32);
+  };
+  // slots of V step b of token tl: set bits b US .. b US + US - 1 of the union of its
+  // heads' masks (-1 past the last), every index below n_depth
+  auto v_slots = [&](int tl, int b, int(&slot)[US]) MODA_INL {
+    uint64_t m = 0;
+#pragma unroll
+    for (int g = 0; g < GB; ++g) m |= rec_mask(rec_of(tl, g));
+    for (int k = 0; k < b * US; ++k) m &= m - 1;
+#pragma unroll
+    for (int u = 0; u < US; ++u) {
+      const int i = m ? (int)__builtin_ctzll(m) : -1;
+      slot[u] = i < n_depth ? i : n_depth - 1;
+      m &= m - 1;
+    }
+  };
+  auto sel_issue = [&](int it, uint4(&w)[US], uint4(&qw)[QBUF]) MODA_INL {
+    it = it < n_sel ? it : n_sel - 1;  // the steps past the end re-load the last one (never processed)
+    const SelStep st = sel_step(it);
+    const int tl = st.tg * NGRP + d_grp;
+    int64_t t = t0 + dt0 + (tl < TPW ? tl : TPW - 1);
+    t = t < len ? t : len - 1;
+    const int64_t n = seg_start + t;
+    const int64_t base = (n * p.S_cap * Hkv + hk) * (int64_t)D + 8 * d_cl;
+    int slot[US];
+    if (st.is_k) {
+#pragma unroll
+      for (int u = 0; u < US; ++u) slot[u] = st.b * US + u < n_depth ? st.b * US + u : n_depth - 1;
+    } else {
+      v_slots(tl, st.b, slot);
+#pragma unroll
+      for (int u = 0; u < US; ++u) slot[u] = slot[u] < 0 ? 0 : slot[u];
+    }
+    // key or value rows: KD plus a selected byte offset (a select between the two
+    // captured pointers becomes a select of their addresses, which keeps them in
+    // scratch memory)
+    const uintptr_t src_addr = reinterpret_cast<uintptr_t>(KD) + (st.is_k ? 0 : vd_minus_kd);
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(src_addr);
+#pragma unroll
+    for (int u = 0; u < US; ++u) w[u] = rowops::stream_load16(src + base + slot[u] * slot_stride);
+    if constexpr (QPRE) {
+#pragma unroll
+      for (int g = 0; g < QBUF; ++g) qw[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * d_cl));
+    }
+  };
+  auto sel_process = [&](int it, const uint4(&w)[US], const uint4(&qw)[QBUF], uint4(&qc)[GB], float(&da)[GB],
+                         float(&dacc)[GB][8]) MODA_INL {
+    const SelStep st = sel_step(it);
+    const int tl = st.tg * NGRP + d_grp;
+    const bool own = tl < TPW;
+    if (st.is_k) {
+      if (st.b == 0) {
+        int64_t t = t0 + dt0 + (tl < TPW ? tl : TPW - 1);
+        t = t < len ? t : len - 1;
+        const int64_t n = seg_start + t;
+#pragma unroll
+        for (int g = 0; g < GB; ++g) {
+          if constexpr (QPRE) {
+            qc[g] = qw[g < QBUF ? g : 0];
+          } else {
+            qc[g] = ldg16(Q + ((n * Hq + hbase + g) * (int64_t)D + 8 * d_cl));
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < GB; ++g) {
+        float* rec = rec_of(tl, g);
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+          float sc = dot2(qc[g].x, w[u].x, 0.f);
+          sc = dot2(qc[g].y, w[u].y, sc);
+          sc = dot2(qc[g].z, w[u].z, sc);
+          sc = dot2(qc[g].w, w[u].w, sc);
+          sc = group_sum<LPR>(sc);
+          const int slot = st.b * US + u;
+          if (own && slot < n_depth && d_cl == u % LPR) rec[slot] = sc;
+        }
+      }
+      if (st.b == nck - 1) {  // every key scored: rank the older slots of each head's row
+#pragma unroll
+        for (int g = 0; g < GB; ++g) {
+          float* rec = rec_of(tl, g);
+          float bj[SPL];
+          int rank[SPL];
+#pragma unroll
+          for (int k = 0; k < SPL; ++k) {
+            const int j = d_cl + LPR * k;
+            bj[k] = j < n_depth ? rec[j] : NEG_INF;
+            rank[k] = 0;
+          }
+          for (int i = 0; i < n_old; ++i) {
+            const float bi = rec[i];
+#pragma unroll
+            for (int k = 0; k < SPL; ++k) {
+              const int j = d_cl + LPR * k;
+              rank[k] += (bi > bj[k] || (bi == bj[k] && i < j)) ? 1 : 0;
+            }
+          }
+          uint64_t keep_mask = 0;
+          float mx = NEG_INF;
+#pragma unroll
+          for (int k = 0; k < SPL; ++k) {
+            const int j = d_cl + LPR * k;
+            const bool keep = j < n_depth && (j >= n_old || rank[k] < p.sel_topk);
+            if (keep) mx = fmaxf(mx, bj[k]);
+            const uint64_t bal = __ballot(keep);  // bits of this lane group: slots LPR k .. LPR k + LPR - 1
+            keep_mask |= ((bal >> (LPR * d_grp)) & ((1ull << LPR) - 1)) << (LPR * k);
+          }
+          mx = group_max<LPR>(mx);
+          if (own && d_cl == 0) {
+            rec[REC_MASK] = __uint_as_float((uint32_t)keep_mask);
+            rec[REC_MASK + 1] = __uint_as_float((uint32_t)(keep_mask >> 32));
+            rec[REC_MAX] = mx * c2;
+          }
+        }
+      }
+    } else {
+      if (st.b == 0) {
+#pragma unroll
+        for (int g = 0; g < GB; ++g) {
+          da[g] = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dacc[g][j] = 0.f;
+        }
+      }
+      int slot[US];
+      v_slots(tl, st.b, slot);
+      float mg[GB];
+#pragma unroll
+      for (int g = 0; g < GB; ++g) {
+        const float* rec = rec_of(tl, g);
+        const uint64_t km = rec_mask(rec);
+        mg[g] = rec[REC_MAX];
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+          const bool kept = slot[u] >= 0 && ((km >> (slot[u] & 63)) & 1ull);
+          const float pu = kept ? fast_exp2(rec[slot[u] < 0 ? 0 : slot[u]] * c2 - mg[g]) : 0.f;
+          da[g] += pu;
+          dacc[g][0] = fmaf(pu, lo_bf16(w[u].x), dacc[g][0]);
+          dacc[g][1] = fmaf(pu, hi_bf16(w[u].x), dacc[g][1]);
+          dacc[g][2] = fmaf(pu, lo_bf16(w[u].y), dacc[g][2]);
+          dacc[g][3] = fmaf(pu, hi_bf16(w[u].y), dacc[g][3]);
+          dacc[g][4] = fmaf(pu, lo_bf16(w[u].z), dacc[g][4]);
+          dacc[g][5] = fmaf(pu, hi_bf16(w[u].z), dacc[g][5]);
+          dacc[g][6] = fmaf(pu, lo_bf16(w[u].w), dacc[g][6]);
+          dacc[g][7] = fmaf(pu, hi_bf16(w[u].w), dacc[g][7]);
+        }
+      }
+      if (st.b == ncv - 1 && own) {  // the record's words are read: the row state replaces them
+#pragma unroll
+        for (int g = 0; g < GB; ++g) {
+          const int row = (dt0 + tl) * GB + g;
+          float4* dst = reinterpret_cast<float4*>(od + row * SM::OS + 8 * d_cl);
+          dst[0] = make_float4(dacc[g][0], dacc[g][1], dacc[g][2], dacc[g][3]);
+          dst[1] = make_float4(dacc[g][4], dacc[g][5], dacc[g][6], dacc[g][7]);
+          if (d_cl == 0) {
+            md[row] = mg[g];
+            ad[row] = da[g];
+          }
+        }
+      }
+    }
+  };
+  auto sel_pass = [&]() MODA_INL {
+    uint4 sw[2][US], sq[2][QBUF];
+    uint4 qc[GB];
+    float da[GB], dacc[GB][8];
+    sel_issue(0, sw[0], sq[0]);
+    for (int it = 0; it < n_sel; it += 2) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        // one token group: its first V step's slots come from this step's ranking
+        const bool late = NTG == 1 && it + j + 1 == nck;
+        if (!late) sel_issue(it + j + 1, sw[j ^ 1], sq[j ^ 1]);
+        if (it + j < n_sel) sel_process(it + j, sw[j], sq[j], qc, da, dacc);
+        if (late) sel_issue(it + j + 1, sw[j ^ 1], sq[j ^ 1]);
       }
     }
   };
@@ -513,11 +740,15 @@ moda_fwd_bf16_kernel(const Params p) {
   // D = 64: the depth loads are issued as the sequence loop starts and consumed
   // after it, which hides their latency (at D = 128 the loop needs those
   // registers; the pass follows the loop).
-  constexpr bool EARLY_DEPTH = DEPTH && SPLIT && D == 64;
+  constexpr bool EARLY_DEPTH = DEPTH && SPLIT && D == 64 && !SELECT;
   constexpr bool depth_first = DEPTH && !SPLIT;
   if constexpr (depth_first) {
-    depth_begin();
-    depth_end();
+    if constexpr (SELECT) {
+      sel_pass();
+    } else {
+      depth_begin();
+      depth_end();
+    }
     __syncthreads();
     depth_fold();
     __syncthreads();  // the hand-off area is the K/V area
@@ -870,7 +1101,9 @@ moda_fwd_bf16_kernel(const Params p) {
   if constexpr (SPLIT) {
     // finish the depth pass (its own LDS area), then merge the partial states of
     // waves 1 .. NW - 1 into wave 0's through the (now free) stage bytes
-    if constexpr (DEPTH) {
+    if constexpr (SELECT) {
+      sel_pass();
+    } else if constexpr (DEPTH) {
       if constexpr (!EARLY_DEPTH) depth_begin();
       depth_end();
     }
@@ -960,7 +1193,7 @@ template <int D, int GB, int NW, bool SPLIT>
 hipError_t launch_d(const Params& p, int phase, bool out_f32, hipStream_t stream) {
   if (phase == kPhaseDepth) return launch_t<D, GB, NW, kDepthOnly, SPLIT>(p, out_f32, stream);
   if (p.n_depth == 0 || phase == kPhaseSeq) return launch_t<D, GB, NW, kNoDepth, SPLIT>(p, out_f32, stream);
-  if (p.depth_mask) return launch_t<D, GB, NW, kSerialMasked, SPLIT>(p, out_f32, stream);
+  if (p.sel_fused) return launch_t<D, GB, NW, kSelect, SPLIT>(p, out_f32, stream);
   return launch_t<D, GB, NW, kSerial, SPLIT>(p, out_f32, stream);
 }
 

@@ -41,9 +41,12 @@ struct Params {
   int32_t qb_major;           // 1: tiles ordered by query block across all pairs (heaviest first)
   int32_t phase;              // kPhaseBoth, or one part alone (kPhaseSeq / kPhaseDepth)
   int64_t n_tiles;
-  // bounded depth reads: bit i of depth_mask[n * Hq + h] says whether slot i enters
-  // row (n, h)'s softmax (null = every slot below n_depth)
+  // bounded depth reads, fp32 path: bit i of depth_mask[n * Hq + h] says whether
+  // slot i enters row (n, h)'s softmax (null = every slot below n_depth)
   const uint64_t* depth_mask;
+  // bounded depth reads, bf16 path (sel_fused = 1): selected inside the depth pass;
+  // 0 < sel_topk < n_depth - sel_recent, 0 <= sel_recent <= n_depth
+  int32_t sel_fused, sel_topk, sel_recent;
 };
 
 // Which key sets enter the softmax of a forward launch: both (the operator), or
