@@ -41,11 +41,12 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector
 CACHE_DEFEAT_BYTES = 768 << 20  # > 256 MB Infinity Cache + 8 x 4 MB L2
-KERNEL_SOURCES = ["moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h"]  # the forward path
+KERNEL_SOURCES = ["moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h",
+                  "moda_lds_load.h"]  # the forward path
 DECODE_SOURCES = ["moda_decode.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h"]
 BWD_SOURCES = ["moda_bwd.hip", "moda_attn.hip", "moda_internal.h", "moda_rowops.h"]
 WRITER_SOURCES = ["moda_depth_kv.hip", "moda_attn.hip", "moda_internal.h"]
-PROJECT_SOURCES = ["moda_depth_kv_project.hip", "moda_attn.hip", "moda_internal.h"]
+PROJECT_SOURCES = ["moda_depth_kv_project.hip", "moda_attn.hip", "moda_internal.h", "moda_lds_load.h"]
 WRITER_METRIC = "depth-KV writer HBM GB/s (one layer's K/V rows into one slot of the depth cache)"
 BWD_METRIC = "fused seq+depth attention bwd TFLOP/s (dq, dk, dv, dk_depth, dv_depth)"
 DECODE_METRIC = "MoDA decode step (joint seq+depth softmax, one token per sequence) HBM GB/s"
@@ -201,7 +202,7 @@ def write_traffic(w, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cmds)
         f.write("\n".join(lines) + "\n")
 
 
-def write_trace_summary(w, trace_dir, log_path, cmd, backward=False, writer=False) -> None:
+def write_trace_summary(w, trace_dir, log_path, cmd, backward=False, writer=False, project=False) -> None:
     """Text summary of a rocprofv3 --kernel-trace --stats run of bench.py."""
     stats = _read_csv(os.path.join(trace_dir, "run_kernel_stats.csv"))
     bench_line = None
@@ -214,6 +215,9 @@ def write_trace_summary(w, trace_dir, log_path, cmd, backward=False, writer=Fals
         kname = "backward (prep + dq + dk/dv kernels)"
     elif writer:
         parts = ["moda_depth_kv_write_kernel"]
+        kname = parts[0]
+    elif project:
+        parts = ["moda_depth_kv_project_bf16_kernel" if w.bf16 else "moda_depth_kv_project_f32_kernel"]
         kname = parts[0]
     elif _is_decode(w):  # a decode step is the partial kernel and the merge kernel
         parts = [kernel_name(w), "moda_decode_merge_kernel"]
@@ -253,7 +257,8 @@ def write_trace_summary(w, trace_dir, log_path, cmd, backward=False, writer=Fals
                     f"{parts[part]['depth_kv_gbs']} GB/s of depth K/V = {parts[part]['hbm_frac_of_peak']:.3f} of HBM peak")
             lines.append(f"{part.replace('_', ' ')} ({parts[part]['kernel']}): bench {parts[part]['ms'] * 1e3:.2f} us"
                          f"{trace}; {rate}.")
-    prefix = "moda_bwd" if backward else "moda_depth_kv" if writer else _summary_prefix(w)
+    prefix = ("moda_bwd" if backward else "moda_depth_kv" if writer else "moda_depth_kv_project" if project
+              else _summary_prefix(w))
     with open(os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_kernel_trace.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -835,7 +840,7 @@ def main(argv=None) -> int:
         w = configs.WORKLOADS.get(args.workload) or configs.DECODE_WORKLOADS[args.workload]
         if args.summarize_trace:
             write_trace_summary(w, args.summarize_trace[0], args.summarize_trace[1], " ".join(args.profile_cmd),
-                                backward=args.backward, writer=args.writer)
+                                backward=args.backward, writer=args.writer, project=args.project)
         if args.write_traffic:
             write_traffic(w, *args.write_traffic, args.profile_cmd)
         return 0

@@ -8,21 +8,27 @@
 // linear layer). No intermediate tensor: the product's epilogue stores the rows
 // at their place in the [N, S_cap, H_kv, d] cache.
 //
-// bf16: a dense contraction on the matrix cores. A workgroup computes the
-// transposed tile C^T[f, n] = sum_k W[f, k] x[n, k] for 128 output features x 128
-// tokens with v_mfma_f32_32x32x16_bf16 (four waves, each 64 x 64 = 2 x 2 MFMA
-// tiles): both operands are read along k, so both are MFMA operands as stored. K
-// steps of 64 go through two LDS stages (16-byte chunks XOR-swizzled by row, the
-// next step's global loads in registers while the current one is multiplied).
-// The output lane layout puts 4 consecutive features of one token in a lane, so
-// the epilogue writes 8-byte runs of a slot row. Workgroups are renumbered so that
-// each XCD takes a contiguous range of tiles: the 32 feature tiles of a token
+// bf16: a dense contraction on the matrix cores. A workgroup of eight waves
+// computes the transposed tile C^T[f, n] = sum_k W[f, k] x[n, k] for 256 output
+// features x 256 tokens with v_mfma_f32_32x32x16_bf16, each wave 128 x 64 (4 x 2
+// MFMA tiles); both operands are read along k, so both are MFMA operands as
+// stored. K steps of 64 go from memory straight into two LDS stages (buffer
+// loads with the LDS flag: no register staging), the next step's loads in flight
+// while the current one is multiplied; rows past the last token or feature read
+// zeros. In LDS each 128-byte row holds its eight 16-byte chunks XOR-swizzled by
+// (row / 2) % 8, so the 16 rows that one operand read serves per LDS cycle cover
+// every bank once. Operands are read one k sub-step ahead of the products. The
+// output lane layout puts 4 consecutive features of one token in a lane, so the
+// epilogue writes 8-byte runs of a slot row (a workgroup writes 512 contiguous
+// bytes of each of its tokens' rows, merged in L2). Workgroups are renumbered so
+// that each XCD takes a contiguous range of tiles: the feature tiles of a token
 // tile then share its x rows in one L2.
 // fp32: a tiled vector kernel (the full-precision path, not a performance target).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "moda_internal.h"
+#include "moda_lds_load.h"
 
 namespace moda {
 namespace {
@@ -32,15 +38,30 @@ typedef __bf16 pbf16x2 __attribute__((ext_vector_type(2)));
 typedef float pf32x16 __attribute__((ext_vector_type(16)));
 typedef float pf32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kPF = 128;        // output features per workgroup tile
-constexpr int kPT = 128;        // tokens per workgroup tile
-constexpr int kPK = 64;         // k per step
-constexpr int kCH = kPK / 8;    // 16-byte chunks per tile row
-constexpr int kLoads = kPF * kCH / 256;  // 16-byte loads per thread per operand and step
+#ifndef MODA_PROJ_PK
+#define MODA_PROJ_PK 64
+#define MODA_PROJ_NST 2
+#endif
+constexpr int kPF = 256;             // output features per workgroup tile
+constexpr int kPT = 256;             // tokens per workgroup tile
+constexpr int kPK = MODA_PROJ_PK;    // k per step
+constexpr int kNST = MODA_PROJ_NST;  // LDS stages (loads run kNST - 1 steps ahead)
+constexpr int kPW = 8;               // waves per workgroup
+constexpr int kRow = kPK * 2;        // bytes of one tile row per stage
+constexpr int kCPR = kPK / 8;        // 16-byte chunks per row
+constexpr int kRPR = 1024 / kRow;    // rows per 1 KB run
+constexpr int kRuns = kPF / kRPR;    // runs per operand tile and step
+constexpr int kRunsW = kRuns / kPW;  // runs of each operand loaded by each wave per step
+constexpr int kLoadsW = 2 * kRunsW;  // loads issued by a wave per step
+constexpr int kStage = (kPF + kPT) * kRow;  // bytes of one stage (W rows, then x rows)
+constexpr int kBankRows = 256 / kRow;       // rows sharing one 256-byte bank line
+static_assert(kPF == kPT && kRunsW * kPW == kRuns && kNST >= 2, "tile shape");
 
-// LDS index (16-byte units) of chunk `c` of tile row `row`: XOR-swizzled so that
-// the 32 rows an MFMA operand read touches spread over the banks
-__device__ __forceinline__ int pswz(int row, int c) { return row * kCH + (c ^ (row & 7)); }
+// byte offset in a stage of 16-byte chunk c of tile row `row`: the chunks of the
+// 16 rows one operand read serves per LDS cycle land on distinct bank slots
+__device__ __forceinline__ uint32_t pswz(int row, int c) {
+  return (uint32_t)(row * kRow + 16 * (c ^ ((row / kBankRows) % kCPR)));
+}
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   const pf32x2 v = {a, b};
@@ -55,73 +76,93 @@ __device__ __forceinline__ int64_t tile_id(const ProjParams& p) {
   return id;
 }
 
-__global__ __launch_bounds__(256, 2) void moda_depth_kv_project_bf16_kernel(const ProjParams p) {
-  __shared__ uint4 sw[2][kPF * kCH];
-  __shared__ uint4 sx[2][kPT * kCH];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wf = wave >> 1, wt = wave & 1;  // this wave's 64-feature and 64-token quarter
+__global__ __launch_bounds__(64 * kPW, 1) void moda_depth_kv_project_bf16_kernel(const ProjParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kNST * kStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wf = wave & 1, wt = wave >> 1;  // this wave's 128-feature half and 64-token quarter
   const int r = lane & 31, hh = lane >> 5;
   const int64_t id = tile_id(p);
   const int f0 = (int)(id % p.n_feat_tiles) * kPF;
   const int64_t t0 = (id / p.n_feat_tiles) * kPT;
-  const uint16_t* __restrict__ X = static_cast<const uint16_t*>(p.x);
-  const uint16_t* __restrict__ W = static_cast<const uint16_t*>(p.w);
   const int K = p.d_model;
   const int nk = K / kPK;
+  const int64_t rowb = (int64_t)K * 2;  // bytes from one operand row to the next
 
-  uint4 rx[kLoads], rw[kLoads];
-  // thread tid loads chunks c = tid + 256 j: row c / 8, 16-byte column c % 8 (eight
-  // consecutive threads read one 128-byte row segment); tokens past N read zeros
-  auto gload = [&](int kt) {
+  // the tile's rows of W and x as buffer ranges: rows past the last feature or
+  // token read zeros
+  const int64_t w_left = 2 * (int64_t)p.hd - f0;
+  const int64_t x_left = p.n_tokens - t0;
+  const int64_t w_bytes = (w_left < kPF ? w_left : kPF) * rowb;
+  const int64_t x_bytes = (x_left < kPT ? x_left : kPT) * rowb;
+  const i32x4 w_rs = make_rsrc(static_cast<const char*>(p.w) + (int64_t)f0 * rowb, (uint32_t)w_bytes);
+  const i32x4 x_rs = make_rsrc(static_cast<const char*>(p.x) + t0 * rowb, (uint32_t)x_bytes);
+
+  // lane l of a 1 KB run fills LDS bytes [16 l, 16 l + 16): row l / kCPR of the run
+  // at chunk position l % kCPR, which holds the chunk pswz puts there
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(smem + stage * kStage);
+    const uint32_t kofs = (uint32_t)(kt * kRow);
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int c = tid + 256 * j, row = c >> 3, col = c & 7;
-      rw[j] = *reinterpret_cast<const uint4*>(W + (int64_t)(f0 + row) * K + kt * kPK + col * 8);
-      const int64_t n = t0 + row;
-      rx[j] = n < p.n_tokens ? *reinterpret_cast<const uint4*>(X + n * K + kt * kPK + col * 8)
-                             : make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < kRunsW; ++j) {
+      const int run = wave * kRunsW + j;
+      const int row = run * kRPR + lane / kCPR;
+      const int chunk = (lane % kCPR) ^ ((row / kBankRows) % kCPR);
+      const uint32_t voff = (uint32_t)(row * rowb) + 16u * (uint32_t)chunk + kofs;
+      load_to_lds16(lds + 1024u * run, voff, w_rs);
+      load_to_lds16(lds + kPF * kRow + 1024u * run, voff, x_rs);
     }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int c = tid + 256 * j, row = c >> 3, col = c & 7;
-      sw[buf][pswz(row, col)] = rw[j];
-      sx[buf][pswz(row, col)] = rx[j];
-    }
-  };
 
-  pf32x16 acc[2][2];
+  pf32x16 acc[4][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-  gload(0);
-  sstore(0);
+  // operands of k sub-step kk (16 k) of a stage: W rows 128 wf + 32 i + r and x
+  // rows 64 wt + 32 i + r, chunk 2 kk + hh
+  auto read_ops = [&](const unsigned char* st, int kk, pbf16x8(&a)[4], pbf16x8(&b)[2])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const pbf16x8*>(st + pswz(wf * 128 + i * 32 + r, 2 * kk + hh));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      b[i] = *reinterpret_cast<const pbf16x8*>(st + kPF * kRow + pswz(wt * 64 + i * 32 + r, 2 * kk + hh));
+  };
+
+  // every step issues one load group (past the last k step it reloads that one
+  // into a free stage) so that a fixed wait count leaves exactly the later groups
+  // in flight
+#pragma unroll
+  for (int j = 0; j < kNST - 1; ++j) issue(j < nk ? j : nk - 1, j);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsW * (kNST - 2)));
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);  // in flight during this step's products
+    const int stage = kt % kNST;
+    {  // into the stage step kt - 1 used, released by the last barrier
+      const int kn = kt + kNST - 1;
+      issue(kn < nk ? kn : nk - 1, kn % kNST);
+    }
+    const unsigned char* st = smem + stage * kStage;
+    pbf16x8 a[2][4], b[2][2];
+    read_ops(st, 0, a[0], b[0]);
 #pragma unroll
     for (int kk = 0; kk < kPK / 16; ++kk) {
-      pbf16x8 a[2], b[2];
+      if (kk + 1 < kPK / 16) read_ops(st, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i] = __builtin_bit_cast(pbf16x8, sw[buf][pswz(wf * 64 + i * 32 + r, 2 * kk + hh)]);
-        b[i] = __builtin_bit_cast(pbf16x8, sx[buf][pswz(wt * 64 + i * 32 + r, 2 * kk + hh)]);
-      }
-#pragma unroll
-      for (int fi = 0; fi < 2; ++fi)
+      for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti)
-          acc[fi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fi], b[ti], acc[fi][ti], 0, 0, 0);
+          acc[fi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][fi], b[kk & 1][ti], acc[fi][ti], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);  // the other stage was released by the last barrier
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsW * (kNST - 2)));  // step kt + 1's rows have landed
+    __syncthreads();                                               // and every wave is done with this stage
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load into LDS outlives the loop
 
   // epilogue: lane (r, hh) of tile (fi, ti) holds token t0 + 64 wt + 32 ti + r and
   // features 8 g + 4 hh + {0..3} of its 32-feature block, g = 0..3
@@ -134,10 +175,11 @@ __global__ __launch_bounds__(256, 2) void moda_depth_kv_project_bf16_kernel(cons
     if (n >= p.n_tokens) continue;
     const int64_t row = (n * p.S_cap + p.slot) * (int64_t)HD;
 #pragma unroll
-    for (int fi = 0; fi < 2; ++fi)
+    for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int f = f0 + wf * 64 + fi * 32 + 8 * g + 4 * hh;
+        const int f = f0 + wf * 128 + fi * 32 + 8 * g + 4 * hh;
+        if (f >= 2 * HD) continue;
         const uint2 val = make_uint2(pack2(acc[fi][ti][4 * g], acc[fi][ti][4 * g + 1]),
                                      pack2(acc[fi][ti][4 * g + 2], acc[fi][ti][4 * g + 3]));
         uint16_t* dst = f < HD ? KDo + row + f : VDo + row + (f - HD);
@@ -196,10 +238,10 @@ __global__ __launch_bounds__(256) void moda_depth_kv_project_f32_kernel(const Pr
 hipError_t launch_depth_kv_project(ProjParams p, bool bf16, hipStream_t stream) {
   const int F = 2 * p.hd;
   if (bf16) {
-    p.n_feat_tiles = F / kPF;
+    p.n_feat_tiles = (F + kPF - 1) / kPF;
     p.n_tok_tiles = (p.n_tokens + kPT - 1) / kPT;
     const int64_t n = (int64_t)p.n_feat_tiles * p.n_tok_tiles;
-    hipLaunchKernelGGL(moda_depth_kv_project_bf16_kernel, dim3((unsigned)n), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(moda_depth_kv_project_bf16_kernel, dim3((unsigned)n), dim3(64 * kPW), 0, stream, p);
   } else {
     p.n_feat_tiles = F / 64;
     p.n_tok_tiles = (p.n_tokens + 63) / 64;

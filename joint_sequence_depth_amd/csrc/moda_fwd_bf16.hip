@@ -53,6 +53,7 @@
 #include <type_traits>
 
 #include "moda_internal.h"
+#include "moda_lds_load.h"
 #include "moda_rowops.h"
 
 namespace moda {
@@ -110,39 +111,6 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_
 #define MODA_INL __attribute__((always_inline))
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
-
-// s_waitcnt immediate: wait until at most n vector-memory loads are outstanding
-// (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and
-// lgkmcnt at their maximum, i.e. not waited for).
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource (raw, no stride): byte range [base, base + nrec); reads past it
-// return zeros without touching memory.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t nrec) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = (int)(uint32_t)b;
-  r[1] = (int)((uint32_t)(b >> 32) & 0xffffu);
-  r[2] = (int)nrec;
-  r[3] = 0x00020000;
-  return r;
-}
-
-// One wave-wide 16-byte-per-lane load from memory straight into LDS: lane l reads
-// bytes [voff, voff + 16) of the resource and writes them to LDS bytes
-// [lds + 16 l, lds + 16 l + 16) (lds is uniform; the compiler puts it in M0).
-// Written as inline assembly so that the compiler's wait insertion does not see
-// an LDS write in flight and drain all loads before every later LDS read: the
-// kernel waits for these loads itself (vector-memory loads complete in issue
-// order, so the compiler's own waits for other loads only become more
-// conservative).
-__device__ __forceinline__ void load_to_lds16(uint32_t lds, uint32_t voff, i32x4 rsrc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);  // uniform: no-op when scalar
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
-}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
