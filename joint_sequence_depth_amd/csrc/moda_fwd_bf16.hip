@@ -239,13 +239,15 @@ moda_fwd_bf16_kernel(const Params p) {
   constexpr int KPT = SPLIT ? BN / RPI : BN / (NW * RPI);  // such loads per wave per K (or V) block
   constexpr int KC = D / 16;                   // k-chunks of Q K^T
   constexpr int DT = D / 32;                   // 32-wide d tiles of O^T
-  constexpr int U = GB == 1 ? 8 : (GB == 2 ? 4 : 2);  // depth slots per load batch
+  constexpr int U = GB == 1 ? 8 : 4;  // depth slots per load batch
   constexpr bool QPRE = GB <= 2;               // prefetch a token's q rows with its first batch
   constexpr int QBUF = QPRE ? GB : 1;
   // depth load buffers (batches in flight + 1); split tiles run the pass beside
   // the live O^T accumulators, so the count stays small (more batches issued
-  // before a split tile's loop only add to the HBM burst at its start)
-  constexpr int NBUF = GB == 1 ? 2 : 3;
+  // before a split tile's loop only add to the HBM burst at its start). Four
+  // heads: four slots with two buffers beat two slots with three (gqa depth-only
+  // 345 -> 320 us) and eight slots.
+  constexpr int NBUF = GB == 2 ? 3 : 2;
   using SM = Smem<D, NW, MODE, SPLIT>;
   constexpr int NST = SM::NST;
   constexpr int P = NST - 1;                 // load groups in flight ahead of the current block
@@ -441,7 +443,7 @@ moda_fwd_bf16_kernel(const Params p) {
   // [V(last)], so a V step's slots, which follow from its group's masks, are
   // loaded (one step ahead) only after that group's ranking has run; with a
   // single token group the first V step is issued after it instead.
-  constexpr int US = 2 * U;         // slot rows per select step (keys or values, not both)
+  constexpr int US = GB == 1 ? 16 : (GB == 2 ? 8 : 4);  // slot rows per select step (keys or values)
   constexpr int SPL = 64 / LPR;     // slots each lane ranks
   constexpr int REC_MASK = 64;      // record words: [0, 64) dot products, mask (2 words), max
   constexpr int REC_MAX = 66;
