@@ -13,7 +13,7 @@
 // one more application of the same update before the single normalisation: the
 // same operator up to the order of rounding.
 //
-// Work unit: one workgroup owns 32 NW expanded query rows (NW in {1, 2, 4}):
+// Work unit: one workgroup owns 32 NW expanded query rows (NW in {2, 4}):
 // TOK = 32 NW / GB tokens x GB query heads of one KV head (rows ordered
 // token-major, row r -> token r / GB, head r % GB, as in the expanded-row map of
 // the deck's backup slide on grouped indexing). Wave w owns rows [32 w, 32 w + 32)
@@ -27,6 +27,8 @@
 //    arithmetic in register buffers and carry the non-temporal hint (the slots are
 //    read once; the sequence K/V blocks are read again by later query blocks and
 //    should keep their L2 lines). Finished row states (m, acc, o) go to LDS.
+//    With bounded depth reads (mode kSelect) the pass reads and ranks every
+//    slot's key first and then reads the values of the kept slots only.
 //
 //  * the sequence loop (MFMA-bound): a flash-style loop over 64-key blocks.
 //    S^T = K Q^T on v_mfma_f32_32x32x16_bf16 puts one query row per lane (lanes l
