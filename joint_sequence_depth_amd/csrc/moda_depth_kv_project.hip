@@ -42,11 +42,16 @@ typedef float pf32x2 __attribute__((ext_vector_type(2)));
 #define MODA_PROJ_PK 64
 #define MODA_PROJ_NST 2
 #endif
+#ifndef MODA_PROJ_PW  // 4 (128 x 128 per wave, one wave per SIMD) measured 27 % slower
+#define MODA_PROJ_PW 8
+#endif
 constexpr int kPF = 256;             // output features per workgroup tile
 constexpr int kPT = 256;             // tokens per workgroup tile
 constexpr int kPK = MODA_PROJ_PK;    // k per step
 constexpr int kNST = MODA_PROJ_NST;  // LDS stages (loads run kNST - 1 steps ahead)
-constexpr int kPW = 8;               // waves per workgroup
+constexpr int kPW = MODA_PROJ_PW;    // waves per workgroup: 2 along features x kPW / 2 along tokens
+constexpr int kWT = kPT / (kPW / 2); // tokens per wave
+constexpr int kNTI = kWT / 32;       // 32-token MFMA tiles per wave
 constexpr int kRow = kPK * 2;        // bytes of one tile row per stage
 constexpr int kCPR = kPK / 8;        // 16-byte chunks per row
 constexpr int kRPR = 1024 / kRow;    // rows per 1 KB run
@@ -80,7 +85,7 @@ __global__ __launch_bounds__(64 * kPW, 1) void moda_depth_kv_project_bf16_kernel
   __shared__ __attribute__((aligned(16))) unsigned char smem[kNST * kStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wf = wave & 1, wt = wave >> 1;  // this wave's 128-feature half and 64-token quarter
+  const int wf = wave & 1, wt = wave >> 1;  // this wave's 128-feature half and kWT-token slice
   const int r = lane & 31, hh = lane >> 5;
   const int64_t id = tile_id(p);
   const int f0 = (int)(id % p.n_feat_tiles) * kPF;
@@ -114,24 +119,24 @@ __global__ __launch_bounds__(64 * kPW, 1) void moda_depth_kv_project_bf16_kernel
     }
   };
 
-  pf32x16 acc[4][2];
+  pf32x16 acc[4][kNTI];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kNTI; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
   // operands of k sub-step kk (16 k) of a stage: W rows 128 wf + 32 i + r and x
-  // rows 64 wt + 32 i + r, chunk 2 kk + hh
-  auto read_ops = [&](const unsigned char* st, int kk, pbf16x8(&a)[4], pbf16x8(&b)[2])
+  // rows kWT wt + 32 i + r, chunk 2 kk + hh
+  auto read_ops = [&](const unsigned char* st, int kk, pbf16x8(&a)[4], pbf16x8(&b)[kNTI])
       __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       a[i] = *reinterpret_cast<const pbf16x8*>(st + pswz(wf * 128 + i * 32 + r, 2 * kk + hh));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      b[i] = *reinterpret_cast<const pbf16x8*>(st + kPF * kRow + pswz(wt * 64 + i * 32 + r, 2 * kk + hh));
+    for (int i = 0; i < kNTI; ++i)
+      b[i] = *reinterpret_cast<const pbf16x8*>(st + kPF * kRow + pswz(wt * kWT + i * 32 + r, 2 * kk + hh));
   };
 
   // every step issues one load group (past the last k step it reloads that one
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(64 * kPW, 1) void moda_depth_kv_project_bf16_kernel
       issue(kn < nk ? kn : nk - 1, kn % kNST);
     }
     const unsigned char* st = smem + stage * kStage;
-    pbf16x8 a[2][4], b[2][2];
+    pbf16x8 a[2][4], b[2][kNTI];
     read_ops(st, 0, a[0], b[0]);
 #pragma unroll
     for (int kk = 0; kk < kPK / 16; ++kk) {
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(64 * kPW, 1) void moda_depth_kv_project_bf16_kernel
 #pragma unroll
       for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
-        for (int ti = 0; ti < 2; ++ti)
+        for (int ti = 0; ti < kNTI; ++ti)
           acc[fi][ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][fi], b[kk & 1][ti], acc[fi][ti], 0, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsW * (kNST - 2)));  // step kt + 1's rows have landed
@@ -164,14 +169,14 @@ __global__ __launch_bounds__(64 * kPW, 1) void moda_depth_kv_project_bf16_kernel
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load into LDS outlives the loop
 
-  // epilogue: lane (r, hh) of tile (fi, ti) holds token t0 + 64 wt + 32 ti + r and
+  // epilogue: lane (r, hh) of tile (fi, ti) holds token t0 + kWT wt + 32 ti + r and
   // features 8 g + 4 hh + {0..3} of its 32-feature block, g = 0..3
   const int HD = p.hd;
   uint16_t* KDo = static_cast<uint16_t*>(p.kd);
   uint16_t* VDo = static_cast<uint16_t*>(p.vd);
 #pragma unroll
-  for (int ti = 0; ti < 2; ++ti) {
-    const int64_t n = t0 + wt * 64 + ti * 32 + r;
+  for (int ti = 0; ti < kNTI; ++ti) {
+    const int64_t n = t0 + wt * kWT + ti * 32 + r;
     if (n >= p.n_tokens) continue;
     const int64_t row = (n * p.S_cap + p.slot) * (int64_t)HD;
 #pragma unroll
