@@ -105,6 +105,11 @@ CASES = {
                         n_depth=8),
     "fp32_d64": dict(dtype="f32", head_dim=64, seqlen=129, batch=2, n_heads_q=4, n_heads_kv=2, n_depth=7),
     "slots_64": dict(dtype="bf16", head_dim=128, seqlen=200, batch=1, n_heads_q=4, n_heads_kv=2, n_depth=64),
+    # split tiles of four heads: one token group per wave, so the first value step
+    # is issued after the ranking; at d = 64 half of its lane groups lie past the
+    # wave's tokens
+    "split_d64_g4": dict(dtype="bf16", head_dim=64, seqlen=200, batch=1, n_heads_q=8, n_heads_kv=2, n_depth=11),
+    "split_d128_g4": dict(dtype="bf16", head_dim=128, seqlen=150, batch=1, n_heads_q=8, n_heads_kv=2, n_depth=9),
 }
 SELECTIONS = [(1, 0), (4, 0), (3, 2), (0, 3)]
 
