@@ -705,16 +705,24 @@ moda_fwd_bf16_kernel(const Params p) {
 
   // Shared tiles: the depth pass runs first, so the workgroup's HBM phase precedes
   // its matrix-core phase and the staggered starts of the workgroups on a CU
-  // overlap the two. Fixed at compile time: the depth buffers are then never live
-  // together with the output accumulators, which keeps every D = 128 instance free
-  // of register spills (a depth-last four-head instance spilled 36-44 bytes per
-  // lane, 1.3x the algorithmic HBM writes, for the same time). Split tiles at
-  // D = 64: the depth loads are issued as the sequence loop starts and consumed
-  // after it, which hides their latency (at D = 128 the loop needs those
+  // overlap the two. With one or two heads per workgroup this is fixed at compile
+  // time: the depth buffers are then never live together with the output
+  // accumulators, which keeps those D = 128 instances free of register spills.
+  // Four-head tiles alternate the order (below); their depth-last path holds both
+  // and spills 36 bytes per lane, which the better overlap outweighs. Split tiles
+  // at D = 64: the depth loads are issued as the sequence loop starts and
+  // consumed after it, which hides their latency (at D = 128 the loop needs those
   // registers; the pass follows the loop).
   constexpr bool EARLY_DEPTH = DEPTH && SPLIT && D == 64 && !SELECT;
   constexpr bool depth_first = DEPTH && !SPLIT;
-  if constexpr (depth_first) {
+  // Four-head tiles (few launch rounds: every workgroup of a round would stream
+  // its depth rows at the same time) alternate the order: the second 256
+  // workgroups of each 512 - one per CU once the first 256 have taken theirs - run
+  // the pass after the sequence loop (gqa 1.026 -> 0.986 ms; for one head per
+  // workgroup, many rounds desynchronise on their own and the alternation cost
+  // 1-2 %).
+  const bool pass_first = !(GB == 4 && MODE == kSerial) || ((blockIdx.x >> 8) & 1) == 0;
+  if (depth_first && pass_first) {
     if constexpr (SELECT) {
       sel_pass();
     } else {
@@ -1114,7 +1122,13 @@ moda_fwd_bf16_kernel(const Params p) {
       m_run = m_new;
     }
     if constexpr (DEPTH) depth_fold();
-  }  // shared tiles folded their depth state before the loop
+  } else if (depth_first && !pass_first) {
+    __syncthreads();  // every wave is past its loop: the K/V area is free for the hand-off
+    depth_begin();
+    depth_end();
+    __syncthreads();
+    depth_fold();
+  }  // the other shared tiles folded their depth state before the loop
 
   // ---- normalise once and write ------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
