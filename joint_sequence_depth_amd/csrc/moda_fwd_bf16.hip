@@ -98,6 +98,7 @@ __device__ __forceinline__ float other_half(float x, int lane) {
 }
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // The low 32 bits of a generic pointer into __shared__ memory are its LDS byte
 // address.
@@ -1131,34 +1132,48 @@ moda_fwd_bf16_kernel(const Params p) {
   }  // the other shared tiles folded their depth state before the loop
 
   // ---- normalise once and write ------------------------------------------------
+  // A lane holds 4 output values of one row, so a direct store would spread each
+  // instruction over 32 rows. The wave's 32 rows go through LDS instead (the stage
+  // bytes, free once every wave is past its loop) and leave as whole rows: lane l
+  // stores 16-byte chunk l % CH of row l / CH. Marking the stores non-temporal
+  // takes about a third off what the writes cost the depth stream.
+  constexpr int EB = OUT_F32 ? 4 : 2;   // output element bytes
+  constexpr int RB = D * EB;            // bytes of one output row
+  constexpr int CH = RB / 16;           // 16-byte chunks per row (8 .. 32)
+  constexpr int ORI = 64 / CH;          // rows per store instruction
+  static_assert(SM::SEQ_BYTES >= (SPLIT ? 1 : NW) * WROWS * RB, "output staging");
+  if constexpr (!SPLIT) __syncthreads();  // other waves may still read the stages or the hand-off
+  unsigned char* ob = smem + (SPLIT ? 0 : wave * WROWS * RB);
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (row_valid) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int64_t obase = ((seg_start + tq) * Hq + hq) * (int64_t)D + 4 * hh;
-    if constexpr (OUT_F32) {
-      float* orow = static_cast<float*>(p.out) + obase;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<float4*>(orow + 32 * dt + 8 * q4) =
-              make_float4(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv, acc[dt][4 * q4 + 2] * inv,
-                          acc[dt][4 * q4 + 3] * inv);
-    } else {
-      uint16_t* orow = static_cast<uint16_t*>(p.out) + obase;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const uint32_t w0 = pack_bf16(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv);
-          const uint32_t w1 = pack_bf16(acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
-          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4) = make_uint2(w0, w1);
-        }
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int off = (32 * dt + 8 * q4 + 4 * hh) * EB;  // byte offset in the row
+      unsigned char* dst = ob + r * RB + 16 * ((off / 16) ^ (r % CH)) + off % 16;
+      if constexpr (OUT_F32) {
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv,
+                                                      acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
+      } else {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv),
+                                                    pack_bf16(acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv));
+      }
     }
-    if (hh == 0 && p.lse) {
-      const int64_t lbase = p.lse_batch_layout ? (int64_t)seg * Hq * p.lse_head_stride : seg_start;
-      p.lse[lbase + (int64_t)hq * p.lse_head_stride + tq] = (m_run + __log2f(l_tot)) * LN2;
-    }
+  if (row_valid && hh == 0 && p.lse) {
+    const int64_t lbase = p.lse_batch_layout ? (int64_t)seg * Hq * p.lse_head_stride : seg_start;
+    p.lse[lbase + (int64_t)hq * p.lse_head_stride + tq] = (m_run + __log2f(l_tot)) * LN2;
+  }
+  const int c = lane % CH;
+#pragma unroll
+  for (int j = 0; j < WROWS / ORI; ++j) {
+    const int rr = j * ORI + lane / CH;  // row within the wave
+    const int64_t t = t0 + (wrow0 + rr) / GB;
+    const int h = hbase + (wrow0 + rr) % GB;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ob + rr * RB + 16 * (c ^ (rr % CH)));
+    if (t < len)  // streaming store: nothing reads the output back here
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<unsigned char*>(p.out) +
+                                                              ((seg_start + t) * Hq + h) * (int64_t)RB + 16 * c));
   }
 }
 
