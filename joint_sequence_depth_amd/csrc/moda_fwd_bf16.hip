@@ -1144,14 +1144,18 @@ moda_fwd_bf16_kernel(const Params p) {
   static_assert(SM::SEQ_BYTES >= (SPLIT ? 1 : NW) * WROWS * RB, "output staging");
   if constexpr (!SPLIT) __syncthreads();  // other waves may still read the stages or the hand-off
   unsigned char* ob = smem + (SPLIT ? 0 : wave * WROWS * RB);
+  // The empty asm makes the lane terms opaque here, so the compiler cannot form
+  // the staging addresses before the loops and hold (spill) them across them.
+  int er = r, ehh = hh;
+  asm volatile("" : "+v"(er), "+v"(ehh));
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int off = (32 * dt + 8 * q4 + 4 * hh) * EB;  // byte offset in the row
-      unsigned char* dst = ob + r * RB + 16 * ((off / 16) ^ (r % CH)) + off % 16;
+      const int off = (32 * dt + 8 * q4 + 4 * ehh) * EB;  // byte offset in the row
+      unsigned char* dst = ob + er * RB + 16 * ((off / 16) ^ (er % CH)) + off % 16;
       if constexpr (OUT_F32) {
         *reinterpret_cast<float4*>(dst) = make_float4(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv,
                                                       acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
