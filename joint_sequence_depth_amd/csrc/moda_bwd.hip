@@ -100,16 +100,23 @@ __device__ __forceinline__ int64_t lse_index(const BwdParams& p, int64_t n, int 
 
 // ---------------------------------------------------------------- prep + depth
 // 8 consecutive elements of a row as stored (bf16: one 16-byte word, fp32: two);
-// kept raw while the load is in flight and widened where it is used.
+// kept raw while the load is in flight and widened where it is used. NT: with the
+// non-temporal hint (the depth slots, read once by the whole backward).
 template <bool BF16>
 struct Raw8 {
   uint4 w[BF16 ? 1 : 2];
 };
-template <bool BF16>
+template <bool BF16, bool NT = false>
 __device__ __forceinline__ Raw8<BF16> load_raw8(const void* base, int64_t elem) {
   Raw8<BF16> r;
-  if constexpr (BF16) {
+  if constexpr (BF16 && NT) {
+    r.w[0] = rowops::stream_load16(static_cast<const uint16_t*>(base) + elem);
+  } else if constexpr (BF16) {
     r.w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+  } else if constexpr (NT) {
+    const float* p = static_cast<const float*>(base) + elem;
+    r.w[0] = rowops::stream_load16(p);
+    r.w[1] = rowops::stream_load16(p + 4);
   } else {
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem);
     r.w[0] = p[0];
@@ -183,8 +190,8 @@ __global__ __launch_bounds__(256) void moda_bwd_prep_kernel(const BwdParams p) {
   if (S > 0) {  // the first slots are in flight while delta is computed
 #pragma unroll
     for (int j = 0; j < kPrepRing - 1; ++j) {
-      kr[j] = load_raw8<BF16>(p.kd, slot_elem(j));
-      vr[j] = load_raw8<BF16>(p.vd, slot_elem(j));
+      kr[j] = load_raw8<BF16, true>(p.kd, slot_elem(j));
+      vr[j] = load_raw8<BF16, true>(p.vd, slot_elem(j));
     }
   }
 
@@ -286,16 +293,16 @@ __global__ __launch_bounds__(256) void moda_bwd_prep_kernel(const BwdParams p) {
       }
     }
     const int64_t de = slot_elem(i);
-    store_n<GF32, 8>(p.dkd, de, dk8);
-    store_n<GF32, 8>(p.dvd, de, dv8);
+    store_n<GF32, 8, true>(p.dkd, de, dk8);  // the depth gradients: written once, streamed
+    store_n<GF32, 8, true>(p.dvd, de, dv8);
   };
   int i0 = 0;
   for (; i0 + kPrepRing <= S; i0 += kPrepRing) {  // whole rounds: straight-line body
 #pragma unroll
     for (int u = 0; u < kPrepRing; ++u) {
       const int r = (u + kPrepRing - 1) % kPrepRing;
-      kr[r] = load_raw8<BF16>(p.kd, slot_elem(i0 + u + kPrepRing - 1));
-      vr[r] = load_raw8<BF16>(p.vd, slot_elem(i0 + u + kPrepRing - 1));
+      kr[r] = load_raw8<BF16, true>(p.kd, slot_elem(i0 + u + kPrepRing - 1));
+      vr[r] = load_raw8<BF16, true>(p.vd, slot_elem(i0 + u + kPrepRing - 1));
       process(i0 + u, kr[u], vr[u]);
     }
   }

@@ -286,60 +286,79 @@ __global__ __launch_bounds__(64 * kDecWaves) void moda_decode_partial_kernel(con
   }
 }
 
-// One workgroup of 64 lanes per (sequence, query head): lane c < D / 8 handles an
-// 8-element slice (64 lanes cover D <= 512).
+// One wave per (sequence, query head). The chunk states are read side by side,
+// not one after another: the maximum first (lanes over chunks), then the weighted
+// sums, NG chunks at a time with C4 lanes per chunk (one float4 of o each) and
+// four rounds of loads in flight, the groups' partial sums added at the end.
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(64) void moda_decode_merge_kernel(const DecodeParams p) {
-  constexpr int LPR = D / 8;
+  constexpr int C4 = D / 4;     // float4 words of a state's o (16 or 32)
+  constexpr int NG = 64 / C4;   // chunk states read side by side (4 or 2)
+  constexpr int UR = 4;         // rounds of loads issued before they are used
   const int lane = threadIdx.x;
   const int64_t bh = blockIdx.x;  // b * Hq + h
   const int b = (int)(bh / p.Hq);
   int64_t L = p.cache_seqlens[b];
   L = L < 1 ? 1 : (L > p.T_max ? p.T_max : L);
   const int n_used = (int)((L + p.chunk - 1) / p.chunk);
+  // the states written for this row: sequence chunks [0, n_used), then the depth chunk
+  const int n_rec = n_used + (p.n_depth > 0 ? 1 : 0);
   const float* recs = p.workspace + bh * p.n_chunks * (D + 4);
+  auto rec_of = [&](int i) { return recs + (int64_t)(i < n_used ? i : p.n_seq_chunks) * (D + 4); };
+
   float M = kNegInf;
-  for (int s = 0; s < n_used; ++s) M = fmaxf(M, recs[s * (D + 4) + D]);
-  if (p.n_depth > 0) M = fmaxf(M, recs[p.n_seq_chunks * (D + 4) + D]);
+  for (int i = lane; i < n_rec; i += 64) M = fmaxf(M, rec_of(i)[D]);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
   const float mu = M == kNegInf ? 0.f : M;
-  float Z = 0.f, R = 0.f, acc[8];  // Z: sum of the weights (for lse); R: as applied to the values
+
+  const int grp = lane / C4, c4 = lane % C4;
+  float Z = 0.f, R = 0.f;  // Z: sum of the weights (for lse); R: as applied to the values
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = 0; i0 < n_rec; i0 += UR * NG) {
+    float mi[UR], li[UR], ri[UR];
+    float4 oi[UR];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  const int c = lane < LPR ? lane : 0;
-  auto add = [&](int s) {
-    const float* rec = recs + s * (D + 4);
-    const float f = __builtin_amdgcn_exp2f(rec[D] - mu);
-    Z = fmaf(rec[D + 1], f, Z);
-    R = fmaf(rec[D + 2], f, R);
-    const float4 a = *reinterpret_cast<const float4*>(rec + 8 * c);
-    const float4 bb = *reinterpret_cast<const float4*>(rec + 8 * c + 4);
-    acc[0] = fmaf(a.x, f, acc[0]);
-    acc[1] = fmaf(a.y, f, acc[1]);
-    acc[2] = fmaf(a.z, f, acc[2]);
-    acc[3] = fmaf(a.w, f, acc[3]);
-    acc[4] = fmaf(bb.x, f, acc[4]);
-    acc[5] = fmaf(bb.y, f, acc[5]);
-    acc[6] = fmaf(bb.z, f, acc[6]);
-    acc[7] = fmaf(bb.w, f, acc[7]);
-  };
-  for (int s = 0; s < n_used; ++s) add(s);
-  if (p.n_depth > 0) add(p.n_seq_chunks);
+    for (int u = 0; u < UR; ++u) {  // loads of all rounds first
+      const int i = i0 + u * NG + grp;
+      const float* rec = rec_of(i < n_rec ? i : 0);
+      mi[u] = i < n_rec ? rec[D] : kNegInf;
+      li[u] = rec[D + 1];
+      ri[u] = rec[D + 2];
+      oi[u] = *reinterpret_cast<const float4*>(rec + 4 * c4);
+    }
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const float f = mi[u] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mi[u] - mu);
+      Z = fmaf(li[u], f, Z);
+      R = fmaf(ri[u], f, R);
+      acc.x = fmaf(oi[u].x, f, acc.x);
+      acc.y = fmaf(oi[u].y, f, acc.y);
+      acc.z = fmaf(oi[u].z, f, acc.z);
+      acc.w = fmaf(oi[u].w, f, acc.w);
+    }
+  }
+#pragma unroll
+  for (int off = C4; off < 64; off <<= 1) {  // add the groups' sums
+    Z += __shfl_xor(Z, off);
+    R += __shfl_xor(R, off);
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
   const float inv = R > 0.f ? 1.f / R : 0.f;
-  if (lane < LPR) {
-    const int64_t e = bh * D + 8 * lane;
+  if (grp == 0) {
+    const int64_t e = bh * D + 4 * c4;
     if constexpr (OUT_F32) {
-      float* out = static_cast<float*>(p.out) + e;
-      *reinterpret_cast<float4*>(out) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-      *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+      *reinterpret_cast<float4*>(static_cast<float*>(p.out) + e) =
+          make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     } else {
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        typedef float f2 __attribute__((ext_vector_type(2)));
-        const f2 v = {acc[2 * j] * inv, acc[2 * j + 1] * inv};
-        w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, dbf16x2));
-      }
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + e) = make_uint4(w[0], w[1], w[2], w[3]);
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      const f2 v0 = {acc.x * inv, acc.y * inv}, v1 = {acc.z * inv, acc.w * inv};
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + e) =
+          make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(v0, dbf16x2)),
+                     __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, dbf16x2)));
     }
     if (lane == 0 && p.lse) p.lse[bh] = (M + __log2f(Z)) * kLn2;
   }

@@ -62,14 +62,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// Stores n (4 or 8) consecutive fp32 values at element offset `elem`, as bf16 or fp32.
-template <bool F32, int N>
+// One 16-byte store with the non-temporal hint (for streams written once).
+__device__ __forceinline__ void stream_store16(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = {a, b, c, d};
+  __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
+}
+
+// Stores n (4 or 8) consecutive fp32 values at element offset `elem`, as bf16 or
+// fp32; NT: with the non-temporal hint (N = 8).
+template <bool F32, int N, bool NT = false>
 __device__ __forceinline__ void store_n(void* base, int64_t elem, const float* x) {
   static_assert(N == 4 || N == 8, "4 or 8 elements");
-  if constexpr (F32) {
+  static_assert(!NT || N == 8, "streaming stores of whole 16-byte words");
+  if constexpr (F32 && NT) {
+    float* p = static_cast<float*>(base) + elem;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      stream_store16(p + 4 * j, __float_as_uint(x[4 * j]), __float_as_uint(x[4 * j + 1]), __float_as_uint(x[4 * j + 2]),
+                     __float_as_uint(x[4 * j + 3]));
+  } else if constexpr (F32) {
     float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + elem);
 #pragma unroll
     for (int j = 0; j < N / 4; ++j) p[j] = make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
+  } else if constexpr (NT) {
+    stream_store16(static_cast<uint16_t*>(base) + elem, pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                   pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
   } else if constexpr (N == 8) {
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + elem) =
         make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
