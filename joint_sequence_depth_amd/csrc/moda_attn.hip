@@ -6,6 +6,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <initializer_list>
+
 #include "moda_internal.h"
 
 namespace {
@@ -21,6 +23,19 @@ int fail(int code, const char* fmt, ...) {
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Every size the host derives from the arguments (element and byte counts,
+// offsets, workspace sizes) is a product of a few of them with small constants.
+// A call is refused unless each tensor it names holds fewer than 2^56 elements,
+// so that none of those products can overflow int64 (checked without overflowing).
+constexpr int64_t kMaxElems = int64_t(1) << 56;
+bool fits(std::initializer_list<int64_t> factors) {
+  int64_t x = 1;
+  for (const int64_t f : factors) {
+    if (f < 0 || __builtin_mul_overflow(x, f, &x) || x >= kMaxElems) return false;
+  }
+  return true;
+}
 
 // Query heads handled together by one bf16 workgroup: the largest power of two
 // (at most 4) dividing the group size. A workgroup's heads share one KV head, so
@@ -171,9 +186,12 @@ int64_t decode_chunk(int64_t batch, int Hq, int Hkv, int d, int64_t T_max) {
   return chunk < unit ? unit : chunk;
 }
 
+// -1 when the workspace would not fit the size limit.
 int64_t decode_workspace_bytes(int64_t batch, int Hq, int Hkv, int d, int64_t T_max) {
+  if (!fits({batch, Hq, T_max, d + 4})) return -1;
   const int64_t chunk = decode_chunk(batch, Hq, Hkv, d, T_max);
   const int64_t n_chunks = (T_max + chunk - 1) / chunk + 1;
+  if (!fits({batch, Hq, n_chunks, d + 4})) return -1;
   return batch * Hq * n_chunks * (int64_t)(d + 4) * 4;
 }
 
@@ -215,6 +233,8 @@ int check_bwd(const BwdArgs& a, int64_t N, moda::BwdParams& p) {
   if (a.n_depth > 0 && (!aligned16(a.dkd) || !aligned16(a.dvd)))
     return fail(MODA_ERR_ALIGN, "dk_depth and dv_depth must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(a.lse) & 3u) return fail(MODA_ERR_ALIGN, "lse must be 4-byte aligned");
+  if (!fits({N, a.Hq, a.d}) || !fits({N, a.S_cap, a.Hkv, a.d}))
+    return fail(MODA_ERR_SHAPE, "problem too large (a tensor of 2^56 elements or more)");
   if (!a.workspace) return fail(MODA_ERR_NULL, "workspace must be non-NULL");
   if (reinterpret_cast<uintptr_t>(a.workspace) & 255u) return fail(MODA_ERR_ALIGN, "workspace must be 256-byte aligned");
   const int64_t need = bwd_workspace_bytes(N, a.Hq, a.d, a.n_depth);
@@ -351,6 +371,8 @@ int fwd_batch(const void* q, const void* k, const void* v, const void* k_depth, 
   rc = check_phase(phase, n_depth);
   if (rc != MODA_OK) return rc;
   if (batch > 0x7fffffffLL) return fail(MODA_ERR_SHAPE, "batch too large");
+  if (!fits({batch, seqlen, n_heads_q, head_dim}) || !fits({batch, seqlen, depth_capacity, n_heads_kv, head_dim}))
+    return fail(MODA_ERR_SHAPE, "problem too large (a tensor of 2^56 elements or more)");
   moda::Params p = base_params(c);
   p.phase = phase;
   p.cu_seqlens = nullptr;
@@ -384,6 +406,9 @@ int fwd_varlen(const void* q, const void* k, const void* v, const void* k_depth,
   rc = check_phase(phase, n_depth);
   if (rc != MODA_OK) return rc;
   if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return fail(MODA_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+  if (!fits({total_tokens, n_heads_q, head_dim}) || !fits({total_tokens, depth_capacity, n_heads_kv, head_dim}) ||
+      !fits({n_seqs, n_heads_q, max_seqlen}))  // the tile grid: segments x heads x query blocks
+    return fail(MODA_ERR_SHAPE, "problem too large (a tensor of 2^56 elements or more)");
   moda::Params p = base_params(c);
   p.phase = phase;
   p.cu_seqlens = cu_seqlens;
@@ -419,6 +444,10 @@ int decode_prepare(const DecodeArgs& a, DecodePlan& plan) {
   if (reinterpret_cast<uintptr_t>(a.cache_seqlens) & 3u)
     return fail(MODA_ERR_ALIGN, "cache_seqlens must be 4-byte aligned");
   if (a.batch > 0x7fffffffLL) return fail(MODA_ERR_SHAPE, "batch too large");
+  if (!fits({a.batch, a.max_cache_len, a.n_heads_kv, a.head_dim}) ||
+      !fits({a.batch, a.depth_capacity, a.n_heads_kv, a.head_dim}) ||
+      decode_workspace_bytes(a.batch, a.n_heads_q, a.n_heads_kv, a.head_dim, a.max_cache_len) < 0)
+    return fail(MODA_ERR_SHAPE, "problem too large (a tensor of 2^56 elements or more)");
   DecodeParams& p = plan.p;
   p = DecodeParams{};
   p.q = a.q;
@@ -524,7 +553,7 @@ int moda_attn_fwd_varlen_topk(const void* q, const void* k, const void* v, const
 }
 
 int64_t moda_attn_fwd_topk_workspace_size(int64_t total_tokens, int32_t n_heads_q) {
-  if (total_tokens < 0 || n_heads_q < 1) return -1;
+  if (total_tokens < 0 || n_heads_q < 1 || !fits({total_tokens, n_heads_q})) return -1;
   return select_workspace_bytes(total_tokens, n_heads_q);
 }
 
@@ -558,6 +587,7 @@ int moda_attn_decode(const void* q, const void* k_cache, const void* v_cache, co
 
 int64_t moda_attn_bwd_workspace_size(int64_t total_tokens, int32_t n_heads_q, int32_t head_dim, int32_t n_depth) {
   if (total_tokens < 0 || n_heads_q < 1 || n_depth < 0 || (head_dim != 64 && head_dim != 128)) return -1;
+  if (!fits({total_tokens, n_heads_q, head_dim})) return -1;
   return bwd_workspace_bytes(total_tokens, n_heads_q, head_dim, n_depth);
 }
 
@@ -572,6 +602,7 @@ int moda_attn_bwd(const void* q, const void* k, const void* v, const void* k_dep
     return MODA_OK;
   }
   if (batch > 0x7fffffffLL) return fail(MODA_ERR_SHAPE, "batch too large");
+  if (!fits({batch, seqlen})) return fail(MODA_ERR_SHAPE, "problem too large (a tensor of 2^56 elements or more)");
   const BwdArgs a{q,  k,  v,  k_depth, v_depth,    out,       dout,       lse,          dq,
                   dk, dv, dk_depth, dv_depth, dtype, grad_dtype, n_heads_q, n_heads_kv, head_dim,
                   depth_capacity, n_depth, causal, scale, workspace, workspace_bytes};
@@ -604,6 +635,8 @@ int moda_attn_bwd_varlen(const void* q, const void* k, const void* v, const void
   const BwdArgs a{q,  k,  v,  k_depth, v_depth,    out,       dout,       lse,          dq,
                   dk, dv, dk_depth, dv_depth, dtype, grad_dtype, n_heads_q, n_heads_kv, head_dim,
                   depth_capacity, n_depth, causal, scale, workspace, workspace_bytes};
+  if (!fits({n_seqs, n_heads_q, max_seqlen}))  // the grids: segments x heads x blocks
+    return fail(MODA_ERR_SHAPE, "problem too large (a tensor of 2^56 elements or more)");
   moda::BwdParams p;
   const int rc = check_bwd(a, total_tokens, p);
   if (rc != MODA_OK) return rc;
@@ -629,6 +662,8 @@ int moda_depth_kv_write(const void* k_src, const void* v_src, void* k_depth, voi
   if (n_heads_kv < 1 || head_dim < 1) return fail(MODA_ERR_SHAPE, "n_heads_kv and head_dim must be >= 1");
   if (depth_capacity < 1 || slot < 0 || slot >= depth_capacity)
     return fail(MODA_ERR_SHAPE, "need 0 <= slot (%d) < depth_capacity (%d)", slot, depth_capacity);
+  if (!fits({n_tokens, depth_capacity, n_heads_kv, head_dim}))
+    return fail(MODA_ERR_SHAPE, "problem too large (a tensor of 2^56 elements or more)");
   const int64_t row_bytes = (int64_t)n_heads_kv * head_dim * (dtype == MODA_DTYPE_BF16 ? 2 : 4);
   if (row_bytes % 16) return fail(MODA_ERR_SHAPE, "n_heads_kv * head_dim * element bytes must be a multiple of 16");
   if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_depth) || !aligned16(v_depth))
@@ -659,6 +694,9 @@ int moda_depth_kv_project(const void* x, const void* w_kv, void* k_depth, void* 
   if (!aligned16(x) || !aligned16(w_kv) || !aligned16(k_depth) || !aligned16(v_depth))
     return fail(MODA_ERR_ALIGN, "x, w_kv, k_depth and v_depth must be 16-byte aligned");
   if ((int64_t)n_heads_kv * head_dim > 0x3fffffffLL) return fail(MODA_ERR_SHAPE, "n_heads_kv * head_dim too large");
+  if (!fits({n_tokens, d_model}) || !fits({n_tokens, depth_capacity, n_heads_kv, head_dim}) ||
+      !fits({2, n_heads_kv, head_dim, d_model}))
+    return fail(MODA_ERR_SHAPE, "problem too large (a tensor of 2^56 elements or more)");
   moda::ProjParams p{};
   p.x = x;
   p.w = w_kv;

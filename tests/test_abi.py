@@ -495,3 +495,33 @@ def test_projection_validation_rejects(kw, code):
 
 def test_projection_empty_is_ok():
     assert callp_(n=0, x=None) == 0
+
+
+# Sizes whose products would overflow int64 (or reach 2^56 elements) are refused
+# before any size is computed from them; the size queries answer -1. Every call
+# stays host-only (rejected by validation).
+HUGE = 1 << 62
+
+
+def test_oversized_problems_are_refused():
+    assert call(B=(1 << 31) - 1, T=1 << 40) == 2 and "too large" in err()
+    assert call(B=1, T=HUGE, S=0, kd=None, vd=None) == 2 and "too large" in err()
+    assert call(B=1 << 20, T=1 << 20, Scap=1 << 30, S=1) == 2 and "too large" in err()
+    assert callv(n_seqs=(1 << 31) - 1, N=1 << 40, max_len=(1 << 31) - 1) == 2 and "too large" in err()
+    assert callv(n_seqs=(1 << 31) - 1, N=(1 << 31) - 1, max_len=(1 << 31) - 1, Hq=1 << 20, Hkv=1) == 2
+    assert calld(B=(1 << 31) - 1, Tmax=(1 << 31) - 1, Hq=1 << 20, Hkv=1 << 20) == 2 and "too large" in err()
+    assert callb(B=1, T=HUGE) == 2 and "too large" in err()
+    assert callbv(n_seqs=(1 << 31) - 1, N=1 << 40, max_len=(1 << 31) - 1) == 2 and "too large" in err()
+    assert callw(N=HUGE) == 2 and "too large" in err()
+    assert callp_(n=HUGE) == 2 and "too large" in err()
+
+
+def test_size_queries_refuse_overflowing_sizes():
+    L = _lib.lib()
+    assert L.moda_attn_bwd_workspace_size(HUGE, 64, 128, 64) == -1
+    assert L.moda_attn_bwd_workspace_size(1 << 40, 1 << 30, 128, 0) == -1
+    assert L.moda_attn_fwd_topk_workspace_size(HUGE, 1 << 30) == -1
+    assert L.moda_attn_decode_workspace_size(HUGE, 64, 8, 128, 1 << 30) == -1
+    assert L.moda_attn_decode_workspace_size((1 << 31) - 1, 1 << 30, 1 << 30, 128, (1 << 31) - 1) == -1
+    # large but representable sizes still answer
+    assert L.moda_attn_bwd_workspace_size(1 << 30, 64, 128, 8) > 0
