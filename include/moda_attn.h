@@ -35,7 +35,10 @@
  * which reports a failed launch. moda_last_error() then describes the failure
  * (per calling thread). The device contents of cu_seqlens are not checked on the
  * host: offsets are clamped to [0, N] on the device, so malformed offsets give
- * unspecified values but never an out-of-bounds access.
+ * unspecified values but never an out-of-bounds access. Every entry point refuses
+ * (MODA_ERR_SHAPE) sizes under which a tensor it names would hold 2^56 elements
+ * or more, and the workspace-size queries return -1 for them, so no size the
+ * library computes can overflow.
  */
 #ifndef MODA_ATTN_H
 #define MODA_ATTN_H

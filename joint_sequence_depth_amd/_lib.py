@@ -6,6 +6,7 @@ memory and the current stream. There is no fallback: without the built library
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -49,52 +50,69 @@ def lib() -> ctypes.CDLL:
     """Load the shared library (once). Raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is missing: build it with `python -m joint_sequence_depth_amd.build` "
-                "(there is no non-HIP fallback)"
-            )
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
-        L.moda_attn_fwd.argtypes = [vp] * 7 + [i32, i32, i64, i64, i32, i32, i32, i32, i32, i32, f32, vp]
-        L.moda_attn_fwd.restype = ctypes.c_int
-        L.moda_attn_fwd_varlen.argtypes = [vp] * 7 + [i32, i32, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32, f32, vp]
-        L.moda_attn_fwd_varlen.restype = ctypes.c_int
-        L.moda_attn_fwd_phases.argtypes = L.moda_attn_fwd.argtypes[:-1] + [i32, vp]
-        L.moda_attn_fwd_phases.restype = ctypes.c_int
-        L.moda_attn_fwd_varlen_phases.argtypes = L.moda_attn_fwd_varlen.argtypes[:-1] + [i32, vp]
-        L.moda_attn_fwd_varlen_phases.restype = ctypes.c_int
-        L.moda_attn_fwd_topk.argtypes = L.moda_attn_fwd.argtypes[:16] + [i32, i32] + L.moda_attn_fwd.argtypes[16:18] + [
-            vp, i64, vp]
-        L.moda_attn_fwd_topk.restype = ctypes.c_int
-        L.moda_attn_fwd_varlen_topk.argtypes = L.moda_attn_fwd_varlen.argtypes[:18] + [i32, i32] + \
-            L.moda_attn_fwd_varlen.argtypes[18:20] + [vp, i64, vp]
-        L.moda_attn_fwd_varlen_topk.restype = ctypes.c_int
-        L.moda_attn_fwd_topk_workspace_size.argtypes = [i64, i32]
-        L.moda_attn_fwd_topk_workspace_size.restype = ctypes.c_int64
-        L.moda_attn_decode.argtypes = [vp] * 7 + [i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp, i64, vp]
-        L.moda_attn_decode.restype = ctypes.c_int
-        L.moda_attn_decode_noalloc.argtypes = [vp] * 7 + [i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp]
-        L.moda_attn_decode_noalloc.restype = ctypes.c_int
-        L.moda_attn_decode_workspace_size.argtypes = [i64, i32, i32, i32, i32]
-        L.moda_attn_decode_workspace_size.restype = ctypes.c_int64
-        L.moda_attn_bwd.argtypes = [vp] * 13 + [i32, i32, i64, i64, i32, i32, i32, i32, i32, i32, f32, vp, i64, vp]
-        L.moda_attn_bwd.restype = ctypes.c_int
-        L.moda_attn_bwd_varlen.argtypes = [vp] * 13 + [i32, i32, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32, f32,
-                                                        vp, i64, vp]
-        L.moda_attn_bwd_varlen.restype = ctypes.c_int
-        L.moda_attn_bwd_workspace_size.argtypes = [i64, i32, i32, i32]
-        L.moda_attn_bwd_workspace_size.restype = ctypes.c_int64
-        L.moda_depth_kv_write.argtypes = [vp] * 4 + [i32, i64, i32, i32, i32, i32, vp]
-        L.moda_depth_kv_write.restype = ctypes.c_int
-        L.moda_depth_kv_project.argtypes = [vp] * 4 + [i32, i64, i32, i32, i32, i32, i32, vp]
-        L.moda_depth_kv_project.restype = ctypes.c_int
-        L.moda_last_error.argtypes = []
-        L.moda_last_error.restype = ctypes.c_char_p
-        L.moda_abi_version.argtypes = []
-        L.moda_abi_version.restype = ctypes.c_int32
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Route this module's calls to another build of the library (the
+    poisoned-LDS debug build) inside the block."""
+    global _lib
+    saved = _lib
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m joint_sequence_depth_amd.build` "
+            "(there is no non-HIP fallback)"
+        )
+    L = ctypes.CDLL(path)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    L.moda_attn_fwd.argtypes = [vp] * 7 + [i32, i32, i64, i64, i32, i32, i32, i32, i32, i32, f32, vp]
+    L.moda_attn_fwd.restype = ctypes.c_int
+    L.moda_attn_fwd_varlen.argtypes = [vp] * 7 + [i32, i32, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32, f32, vp]
+    L.moda_attn_fwd_varlen.restype = ctypes.c_int
+    L.moda_attn_fwd_phases.argtypes = L.moda_attn_fwd.argtypes[:-1] + [i32, vp]
+    L.moda_attn_fwd_phases.restype = ctypes.c_int
+    L.moda_attn_fwd_varlen_phases.argtypes = L.moda_attn_fwd_varlen.argtypes[:-1] + [i32, vp]
+    L.moda_attn_fwd_varlen_phases.restype = ctypes.c_int
+    L.moda_attn_fwd_topk.argtypes = L.moda_attn_fwd.argtypes[:16] + [i32, i32] + L.moda_attn_fwd.argtypes[16:18] + [
+        vp, i64, vp]
+    L.moda_attn_fwd_topk.restype = ctypes.c_int
+    L.moda_attn_fwd_varlen_topk.argtypes = L.moda_attn_fwd_varlen.argtypes[:18] + [i32, i32] + \
+        L.moda_attn_fwd_varlen.argtypes[18:20] + [vp, i64, vp]
+    L.moda_attn_fwd_varlen_topk.restype = ctypes.c_int
+    L.moda_attn_fwd_topk_workspace_size.argtypes = [i64, i32]
+    L.moda_attn_fwd_topk_workspace_size.restype = ctypes.c_int64
+    L.moda_attn_decode.argtypes = [vp] * 7 + [i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp, i64, vp]
+    L.moda_attn_decode.restype = ctypes.c_int
+    L.moda_attn_decode_noalloc.argtypes = [vp] * 7 + [i32, i32, vp, i64, i32, i32, i32, i32, i32, i32, f32, vp]
+    L.moda_attn_decode_noalloc.restype = ctypes.c_int
+    L.moda_attn_decode_workspace_size.argtypes = [i64, i32, i32, i32, i32]
+    L.moda_attn_decode_workspace_size.restype = ctypes.c_int64
+    L.moda_attn_bwd.argtypes = [vp] * 13 + [i32, i32, i64, i64, i32, i32, i32, i32, i32, i32, f32, vp, i64, vp]
+    L.moda_attn_bwd.restype = ctypes.c_int
+    L.moda_attn_bwd_varlen.argtypes = [vp] * 13 + [i32, i32, vp, i32, i64, i32, i32, i32, i32, i32, i32, i32, f32,
+                                                    vp, i64, vp]
+    L.moda_attn_bwd_varlen.restype = ctypes.c_int
+    L.moda_attn_bwd_workspace_size.argtypes = [i64, i32, i32, i32]
+    L.moda_attn_bwd_workspace_size.restype = ctypes.c_int64
+    L.moda_depth_kv_write.argtypes = [vp] * 4 + [i32, i64, i32, i32, i32, i32, vp]
+    L.moda_depth_kv_write.restype = ctypes.c_int
+    L.moda_depth_kv_project.argtypes = [vp] * 4 + [i32, i64, i32, i32, i32, i32, i32, vp]
+    L.moda_depth_kv_project.restype = ctypes.c_int
+    L.moda_last_error.argtypes = []
+    L.moda_last_error.restype = ctypes.c_char_p
+    L.moda_abi_version.argtypes = []
+    L.moda_abi_version.restype = ctypes.c_int32
+    return L
 
 
 def _check(status: int):

@@ -17,6 +17,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmoda_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 PEAKS_PATH = os.path.join(PKG, "libmoda_peaks.so")  # measurement only (include/moda_peaks.h)
+# Debug build: the same sources with -DMODA_POISON_LDS=1 (csrc/moda_debug.h), every
+# kernel's LDS filled with NaNs at its start; loaded only by its GPU test.
+POISON_LIB_PATH = os.path.join(PKG, "libmoda_attn_poison.so")
 SOURCES = ["moda_attn.hip", "moda_fwd_bf16.hip", "moda_fwd_f32.hip", "moda_depth_select.hip", "moda_decode.hip",
            "moda_decode_noalloc.hip", "moda_bwd.hip", "moda_depth_kv.hip", "moda_depth_kv_project.hip"]
 # Compilation units: (source, object stem, extra flags). The bf16 forward's
@@ -63,8 +66,9 @@ def compile_flags(source: str = ""):
     return flags
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
+def build(verbose: bool = False, poison: bool = True) -> str:
+    """Compile every source and link the shared library (and, with `poison`, the
+    poisoned-LDS debug build beside it); returns the library's path."""
     cc = hipcc()
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -75,11 +79,21 @@ def build(verbose: bool = False) -> str:
     # attained-peak microbenchmarks go into a library of their own
     peaks_obj = os.path.join(objdir, "moda_peaks.o")
     cmds.append([cc, *compile_flags("moda_peaks.hip"), "-c", os.path.join(CSRC, "moda_peaks.hip"), "-o", peaks_obj])
+    links = [(LIB_PATH, objs), (PEAKS_PATH, [peaks_obj])]
+    if poison:
+        pdir = os.path.join(PKG, "_build_poison")
+        os.makedirs(pdir, exist_ok=True)
+        pobjs = [os.path.join(pdir, stem + ".o") for _, stem, _ in UNITS]
+        cmds += [[cc, *compile_flags(src), *extra, "-DMODA_POISON_LDS=1", "-c", os.path.join(CSRC, src), "-o", obj]
+                 for (src, _, extra), obj in zip(UNITS, pobjs)]
+        links.append((POISON_LIB_PATH, pobjs))
+    # the slowest units (the bf16 forward's) first
+    cmds.sort(key=lambda c: "moda_fwd_bf16" not in c[-1])
     workers = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(max_workers=workers) as ex:
         for f in [ex.submit(_run, cmd, verbose) for cmd in cmds]:
             f.result()
-    for path, ob in ((LIB_PATH, objs), (PEAKS_PATH, [peaks_obj])):
+    for path, ob in links:
         tmp = path + ".tmp"
         _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *ob, "-o", tmp], verbose)
         os.replace(tmp, path)

@@ -169,6 +169,7 @@ __global__ __launch_bounds__(256) void moda_bwd_prep_kernel(const BwdParams p) {
   constexpr bool REG = GC > 0;    // the G heads' state in registers
   constexpr int GR = REG ? GC : 1;  // register copies
   extern __shared__ float dyn[];
+  if constexpr (GC == 0) poison_lds(dyn, (int)(blockDim.x >> 6) * prep_wave_floats(p.G, D) * 4);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
   const int grp = lane / LPR, cl = lane % LPR;
   const int n_hb = (p.Hkv + NGRP - 1) / NGRP;
@@ -368,6 +369,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) MODA_BWD_DQ_ATTR void moda_bwd_dq_k
   // two buffers: the tile after next is stored while the current one is read
   __shared__ __align__(16) unsigned char kbuf[2][kTile * PITCH];
   __shared__ __align__(16) unsigned char vbuf[2][kTile * PITCH];
+  poison_lds(kbuf, sizeof(kbuf));
+  poison_lds(vbuf, sizeof(vbuf));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 31, hh = lane >> 5;
 
   // Workgroup order: with xcd_group, consecutive workgroups (which the hardware
@@ -570,6 +573,7 @@ void moda_bwd_dkv8_kernel(const BwdParams p) {
   constexpr int LDS_BYTES = OFF_D + 2 * kTile * 4;
   static_assert(4 * 64 * 2 * DT * 16 * 4 <= LDS_BYTES, "partials of four waves fit in the LDS block");
   __shared__ __align__(16) unsigned char sm[LDS_BYTES];
+  poison_lds(sm, LDS_BYTES);
   unsigned char* const kt = sm;
   unsigned char* const vt = sm + KV_BYTES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 31, hh = lane >> 5;

@@ -107,6 +107,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void moda_decode_partial_kernel(con
   constexpr int ROWS_PER_BATCH = NGRP * U;  // key rows one wave consumes per batch
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane / LPR, cl = lane % LPR;
+  __shared__ float red[kDecWaves][GD][D + 4];  // per wave: o slices, then m, l and r
+  poison_lds(red, sizeof(red));
 
   // workgroup -> (sequence b, KV head hk, head group hg, chunk s)
   int64_t id = blockIdx.x;
@@ -247,7 +249,6 @@ __global__ __launch_bounds__(64 * kDecWaves) void moda_decode_partial_kernel(con
       merge_state(m[g], l[g], rr[g], o[g], mb, lb, rb, ob);
     }
   }
-  __shared__ float red[kDecWaves][GD][D + 4];  // per wave: o slices, then m, l and r
   if (grp == 0) {
 #pragma unroll
     for (int g = 0; g < GD; ++g) {

@@ -83,6 +83,7 @@ __device__ __forceinline__ int64_t tile_id(const ProjParams& p) {
 
 __global__ __launch_bounds__(64 * kPW, 1) void moda_depth_kv_project_bf16_kernel(const ProjParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kNST * kStage];
+  poison_lds(smem, kNST * kStage);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wf = wave & 1, wt = wave >> 1;  // this wave's 128-feature half and kWT-token slice
@@ -198,6 +199,8 @@ __global__ __launch_bounds__(64 * kPW, 1) void moda_depth_kv_project_bf16_kernel
 __global__ __launch_bounds__(256) void moda_depth_kv_project_f32_kernel(const ProjParams p) {
   __shared__ float sw[16][64 + 1];
   __shared__ float sx[16][64 + 1];
+  poison_lds(sw, sizeof(sw));
+  poison_lds(sx, sizeof(sx));
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int64_t id = blockIdx.x;
   const int f0 = (int)(id % p.n_feat_tiles) * 64;

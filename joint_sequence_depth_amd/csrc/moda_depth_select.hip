@@ -46,6 +46,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void moda_depth_select_kernel(const
   const int hk = (int)(unit % p.Hkv);
   const int S = p.n_depth;
   __shared__ float logit[kSelWaves][64];
+  poison_lds(logit, sizeof(logit));
 
   // the token's slot keys: slice cl of slot b * NGRP + grp in kx[b]
   float kx[NB][8];

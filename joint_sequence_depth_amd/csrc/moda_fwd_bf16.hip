@@ -259,6 +259,7 @@ moda_fwd_bf16_kernel(const Params p) {
   static_assert(!SPLIT || (TW % NW == 0 && NW >= 2), "split tile shape");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[SM::BYTES];
+  poison_lds(smem, SM::BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

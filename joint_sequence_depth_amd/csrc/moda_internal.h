@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moda_debug.h"
+
 namespace moda {
 
 // One launch of the fused joint sequence/depth attention forward.

@@ -525,3 +525,17 @@ def test_size_queries_refuse_overflowing_sizes():
     assert L.moda_attn_decode_workspace_size((1 << 31) - 1, 1 << 30, 1 << 30, 128, (1 << 31) - 1) == -1
     # large but representable sizes still answer
     assert L.moda_attn_bwd_workspace_size(1 << 30, 64, 128, 8) > 0
+
+
+def test_poisoned_lds_build_is_instrumented():
+    # the debug build's kernels carry the NaN fill pattern (0x7fc07fc0) as an
+    # immediate and the normal build's do not: the GPU comparison of the two
+    # builds compares instrumented kernels against plain ones
+    from joint_sequence_depth_amd import build
+
+    pattern = (0x7FC07FC0).to_bytes(4, "little")
+    for path in (build.LIB_PATH, build.POISON_LIB_PATH):
+        if not os.path.exists(path):
+            pytest.skip("the library is not built")
+    assert open(build.LIB_PATH, "rb").read().count(pattern) == 0
+    assert open(build.POISON_LIB_PATH, "rb").read().count(pattern) >= 20
