@@ -108,6 +108,14 @@ def test_bwd_depth_counts(dtype, S, S_cap):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("S,S_cap,Hq,Hkv,d", [(65, 70, 8, 2, 128), (130, 131, 4, 4, 64)])
+def test_bwd_many_depth_slots(dtype, S, S_cap, Hq, Hkv, d):
+    # the prep kernel's ring of slot loads wraps many times and ends ragged
+    _full_compare(workload(dtype=dtype, head_dim=d, seqlen=90, batch=1, n_heads_q=Hq, n_heads_kv=Hkv, n_depth=S,
+                           depth_capacity=S_cap, seed=1150 + S))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 1), (8, 2), (6, 2), (16, 1), (12, 4)])
 def test_bwd_grouped_heads(dtype, Hq, Hkv):
     _full_compare(workload(dtype=dtype, head_dim=64, seqlen=150, batch=1, n_heads_q=Hq, n_heads_kv=Hkv, n_depth=4,

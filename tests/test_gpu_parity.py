@@ -76,6 +76,16 @@ def test_depth_counts(dtype, S, S_cap):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("S,S_cap,Hq,Hkv,d", [(65, 70, 2, 2, 128), (130, 130, 8, 2, 128), (97, 100, 8, 4, 64),
+                                              (200, 201, 4, 1, 64)])
+def test_many_depth_slots(dtype, S, S_cap, Hq, Hkv, d):
+    # more slots than any load batch, round or selection width covers (64):
+    # the depth pass's batches over slots wrap many times and end ragged
+    _full_compare(workload(dtype=dtype, head_dim=d, seqlen=100, batch=1, n_heads_q=Hq, n_heads_kv=Hkv, n_depth=S,
+                           depth_capacity=S_cap, seed=S + Hq))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 1), (8, 2), (16, 2), (6, 2), (3, 1), (12, 4)])
 def test_grouped_heads(dtype, Hq, Hkv):
     _full_compare(workload(dtype=dtype, head_dim=64, seqlen=150, batch=2, n_heads_q=Hq, n_heads_kv=Hkv, n_depth=4,
