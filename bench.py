@@ -60,11 +60,12 @@ def kernel_source_sha(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_name(w, phase: int = 3) -> str:
+def kernel_name(w, phase: int = 3, select: bool = False) -> str:
     """The kernel instance the library launches for this workload (mirrors the
     host dispatch: heads per workgroup, waves per workgroup, depth schedule,
     shared or split tiles); ``phase`` 1 or 2 names the sequence-only or
-    depth-only launch."""
+    depth-only launch, ``select`` the bounded depth reads (bf16: selection in
+    the depth pass)."""
     if _is_decode(w):
         G = w.group
         gd = next(g for g in (8, 4, 2, 1) if G % g == 0)
@@ -84,7 +85,7 @@ def kernel_name(w, phase: int = 3) -> str:
             break
     if waves == 0:
         waves, split = 2, True
-    mode = 2 if phase == 2 else 0 if (w.n_depth == 0 or phase == 1) else 1
+    mode = 2 if phase == 2 else 0 if (w.n_depth == 0 or phase == 1) else 3 if select else 1
     return f"moda_fwd_bf16_kernel<{w.head_dim}, {gb}, {waves}, {mode}, false, {str(split).lower()}>"
 
 
@@ -202,7 +203,17 @@ def write_traffic(w, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cmds)
         f.write("\n".join(lines) + "\n")
 
 
-def write_trace_summary(w, trace_dir, log_path, cmd, backward=False, writer=False, project=False) -> None:
+def _selects(w, args) -> bool:
+    """Whether a bounded-read run launches the bf16 selecting instance (some slots
+    dropped: 0 < topk < n_depth - recent)."""
+    if args.depth_topk is None or not w.bf16:
+        return False
+    recent = min(args.depth_recent, w.n_depth)
+    return 0 < args.depth_topk < w.n_depth - recent
+
+
+def write_trace_summary(w, trace_dir, log_path, cmd, backward=False, writer=False, project=False,
+                        depth_topk=None) -> None:
     """Text summary of a rocprofv3 --kernel-trace --stats run of bench.py."""
     stats = _read_csv(os.path.join(trace_dir, "run_kernel_stats.csv"))
     bench_line = None
@@ -223,8 +234,8 @@ def write_trace_summary(w, trace_dir, log_path, cmd, backward=False, writer=Fals
         parts = [kernel_name(w), "moda_decode_merge_kernel"]
         kname = kernel_name(w)
     else:
-        parts = [kernel_name(w)]
-        kname = kernel_name(w)
+        parts = [kernel_name(w, select=depth_topk is not None and w.bf16)]
+        kname = parts[0]
     rows = [next((r for r in stats if part in r["Name"]), None) for part in parts]
     if any(r is None for r in rows) or bench_line is None:
         raise SystemExit(f"kernels {parts} or the bench line missing in {trace_dir}")
@@ -259,7 +270,8 @@ def write_trace_summary(w, trace_dir, log_path, cmd, backward=False, writer=Fals
                          f"{trace}; {rate}.")
     prefix = ("moda_bwd" if backward else "moda_depth_kv" if writer else "moda_depth_kv_project" if project
               else _summary_prefix(w))
-    with open(os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_kernel_trace.txt"), "w") as f:
+    tag = f"_top{depth_topk}" if depth_topk is not None else ""
+    with open(os.path.join(ROOT, "profiles", f"{prefix}_{w.name}{tag}_kernel_trace.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
@@ -840,7 +852,8 @@ def main(argv=None) -> int:
         w = configs.WORKLOADS.get(args.workload) or configs.DECODE_WORKLOADS[args.workload]
         if args.summarize_trace:
             write_trace_summary(w, args.summarize_trace[0], args.summarize_trace[1], " ".join(args.profile_cmd),
-                                backward=args.backward, writer=args.writer, project=args.project)
+                                backward=args.backward, writer=args.writer, project=args.project,
+                                depth_topk=args.depth_topk)
         if args.write_traffic:
             write_traffic(w, *args.write_traffic, args.profile_cmd)
         return 0
@@ -1014,7 +1027,7 @@ def main(argv=None) -> int:
             "depth_recent": args.depth_recent if sel else None,
         },
         "parts": parts,
-        "kernel": kernel_name(w),
+        "kernel": kernel_name(w, select=_selects(w, args)),
         "kernel_source_sha": kernel_source_sha(),
         "replay_matches_eager": replay_ok,
         "roofline": roofline(w, sec) if not sel else {
