@@ -19,8 +19,8 @@
 // (row / 2) % 8, so the 16 rows that one operand read serves per LDS cycle cover
 // every bank once. Operands are read one k sub-step ahead of the products. The
 // output lane layout puts 4 consecutive features of one token in a lane, so the
-// epilogue writes 8-byte runs of a slot row (a workgroup writes 512 contiguous
-// bytes of each of its tokens' rows, merged in L2). Workgroups are renumbered so
+// epilogue stages each wave's outputs through LDS token by token and stores whole
+// 256-byte runs of a slot row with the non-temporal hint. Workgroups are renumbered so
 // that each XCD takes a contiguous range of tiles: the feature tiles of a token
 // tile then share its x rows in one L2.
 // fp32: a tiled vector kernel (the full-precision path, not a performance target).
@@ -169,28 +169,44 @@ __global__ __launch_bounds__(64 * kPW, 1) void moda_depth_kv_project_bf16_kernel
     __syncthreads();                                               // and every wave is done with this stage
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load into LDS outlives the loop
+  __syncthreads();                           // nor any other wave's: the stages are free
 
-  // epilogue: lane (r, hh) of tile (fi, ti) holds token t0 + kWT wt + 32 ti + r and
-  // features 8 g + 4 hh + {0..3} of its 32-feature block, g = 0..3
-  const int HD = p.hd;
-  uint16_t* KDo = static_cast<uint16_t*>(p.kd);
-  uint16_t* VDo = static_cast<uint16_t*>(p.vd);
+  // epilogue: lane (r, hh) of tile (fi, ti) holds token kWT wt + 32 ti + r of the
+  // tile and features 8 g + 4 hh + {0..3} of its 32-feature block, g = 0..3. Each
+  // wave stages its 128 features x kWT tokens through LDS, token-major (the
+  // 16-byte chunks of a token's 256-byte row XOR-swizzled by token % 16), and
+  // stores whole runs: 16 lanes write a token's 256 contiguous bytes.
+  constexpr int kOR = 128 * 2;      // bytes of a wave's token row (128 features)
+  constexpr int kOC = kOR / 16;     // 16-byte chunks per row
+  static_assert(kPW * kWT * kOR <= kNST * kStage, "output staging");
+  unsigned char* ob = smem + wave * kWT * kOR;
 #pragma unroll
   for (int ti = 0; ti < kNTI; ++ti) {
-    const int64_t n = t0 + wt * kWT + ti * 32 + r;
-    if (n >= p.n_tokens) continue;
-    const int64_t row = (n * p.S_cap + p.slot) * (int64_t)HD;
+    const int tt = ti * 32 + r;
 #pragma unroll
     for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int f = f0 + wf * 128 + fi * 32 + 8 * g + 4 * hh;
-        if (f >= 2 * HD) continue;
-        const uint2 val = make_uint2(pack2(acc[fi][ti][4 * g], acc[fi][ti][4 * g + 1]),
-                                     pack2(acc[fi][ti][4 * g + 2], acc[fi][ti][4 * g + 3]));
-        uint16_t* dst = f < HD ? KDo + row + f : VDo + row + (f - HD);
-        *reinterpret_cast<uint2*>(dst) = val;
-      }
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<uint2*>(ob + tt * kOR + 16 * ((4 * fi + g) ^ (tt % kOC)) + 8 * hh) =
+            make_uint2(pack2(acc[fi][ti][4 * g], acc[fi][ti][4 * g + 1]),
+                       pack2(acc[fi][ti][4 * g + 2], acc[fi][ti][4 * g + 3]));
+  }
+  const int HD = p.hd;
+  uint16_t* KDo = static_cast<uint16_t*>(p.kd);
+  uint16_t* VDo = static_cast<uint16_t*>(p.vd);
+  const int c = lane % kOC;
+  const int f = f0 + wf * 128 + 8 * c;  // first of the chunk's 8 features (HD % 64 == 0: one side of HD)
+#pragma unroll
+  for (int j = 0; j < kWT * kOC / 64; ++j) {
+    const int tt = j * (64 / kOC) + lane / kOC;
+    typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v v = *reinterpret_cast<const u32x4v*>(ob + tt * kOR + 16 * (c ^ (tt % kOC)));
+    const int64_t n = t0 + wt * kWT + tt;
+    if (n < p.n_tokens && f < 2 * HD) {
+      const int64_t row = (n * p.S_cap + p.slot) * (int64_t)HD;
+      uint16_t* dst = f < HD ? KDo + row + f : VDo + row + (f - HD);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4v*>(dst));
+    }
   }
 }
 
