@@ -9,11 +9,13 @@
 //
 // Per token the source row (H_kv d elements) and the destination slot row are
 // both contiguous, so the copy is a stream of 16-byte vectors: thread i moves
-// vector i of the flattened [N, H_kv d] source into the slot row of its token.
+// vector i of the flattened [N, H_kv d] source into the slot row of its token,
+// stored with the non-temporal hint.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "moda_internal.h"
+#include "moda_rowops.h"
 
 namespace moda {
 namespace {
@@ -28,8 +30,10 @@ __global__ __launch_bounds__(kWriterThreads) void moda_depth_kv_write_kernel(con
     const int64_t dst = (n * p.S_cap + p.slot) * p.row_vecs + c;
     const uint4 kv = reinterpret_cast<const uint4*>(p.k_src)[i];
     const uint4 vv = reinterpret_cast<const uint4*>(p.v_src)[i];
-    reinterpret_cast<uint4*>(p.k_depth)[dst] = kv;
-    reinterpret_cast<uint4*>(p.v_depth)[dst] = vv;
+    // streaming stores: a later layer reads the slot, not this kernel (16384 tokens
+    // x 16 KV heads x 128: 43.1 -> 39.5 us)
+    rowops::stream_store16(reinterpret_cast<uint4*>(p.k_depth) + dst, kv.x, kv.y, kv.z, kv.w);
+    rowops::stream_store16(reinterpret_cast<uint4*>(p.v_depth) + dst, vv.x, vv.y, vv.z, vv.w);
   }
 }
 
@@ -38,7 +42,7 @@ __global__ __launch_bounds__(kWriterThreads) void moda_depth_kv_write_kernel(con
 hipError_t launch_depth_kv_write(const DepthWriteParams& p, hipStream_t stream) {
   const int64_t n_vec = p.n_tokens * p.row_vecs;
   int64_t blocks = (n_vec + kWriterThreads - 1) / kWriterThreads;
-  const int64_t cap = 256 * 32;  // 32 workgroups per CU, then grid-stride
+  const int64_t cap = 256 * 64;  // 64 workgroups per CU, then grid-stride
   blocks = blocks < cap ? blocks : cap;
   hipLaunchKernelGGL(moda_depth_kv_write_kernel, dim3((unsigned)blocks), dim3(kWriterThreads), 0, stream, p);
   return hipGetLastError();
