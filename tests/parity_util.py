@@ -218,6 +218,10 @@ SCHEDULE_CASES = {
                             kernel="<128, 2, 4, 1, false, false>"),
     "split_d128": dict(head_dim=128, batch=1, seqlen=1500, n_heads_q=4, n_heads_kv=4, n_depth=13,
                        kernel="<128, 1, 2, 1, false, true>"),
+    # one 65536-token sequence: 512 query blocks, up to 1024 key blocks per tile
+    # (the headline instance, with the plain tile order: two pairs)
+    "long_d128": dict(head_dim=128, batch=1, seqlen=65536, n_heads_q=2, n_heads_kv=2, n_depth=4,
+                      kernel="<128, 1, 4, 1, false, false>"),
     # whole-output cases
     "whole_shared2_d64_g4": dict(head_dim=64, batch=1, seqlen=1024, n_heads_q=32, n_heads_kv=8, n_depth=5,
                                  kernel="<64, 4, 2, 1, false, false>", whole=True),
